@@ -1,0 +1,20 @@
+"""Block-hybrid attention for MI355X (gfx950).
+
+For each head, the active denoising block gets exact softmax attention over
+itself plus a linear-attention term ReLU(Q_a) S over all previous blocks, where
+S = sum of ReLU(K_p)^T V_p is an fp32 d x d prefix state ("Retrofitting Linear
+Attention into Diffusion Language Models").  The hot path is three calls of
+the C-ABI library libhybrid_attn.so (hand-written HIP kernels), exposed here
+with the same names:
+
+    hybrid_attn_step      one denoising step of a hybrid layer
+    hybrid_state_commit   S += ReLU(K_blk)^T V_blk when a block is finished
+    hybrid_state_prefill  S = sum over a prompt of ReLU(k)^T v
+
+PyTorch only provides device memory and streams.
+"""
+from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_state_commit,
+                      hybrid_state_prefill, hybrid_state_prefill_workspace_bytes, load_library)
+
+__all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_state_commit",
+           "hybrid_state_prefill", "hybrid_state_prefill_workspace_bytes", "load_library"]

@@ -1,0 +1,177 @@
+"""ctypes binding of libhybrid_attn.so: argument marshalling only.
+
+The functions carry the C ABI's names and take torch tensors on the GPU; they
+check shapes and dtypes, pass raw device pointers and the current HIP stream,
+and raise ``HybridAttnError`` on any non-OK status.  All computation happens
+in the library's HIP kernels; there is no fallback of any kind, and a missing
+library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .build import LIB as LIB_PATH
+
+HA_OK, HA_ERR_INVALID_ARG, HA_ERR_UNSUPPORTED, HA_ERR_HIP = 0, 1, 2, 3
+HA_F32, HA_BF16 = 0, 1
+MAX_BLK = 128
+
+_lock = threading.Lock()
+_lib = None
+
+
+class HybridAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the shared library; raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
+                               "python -m block_hybrid_linear_amd.build")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        lib.hybrid_attn_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, ctypes.c_int, vp]
+        lib.hybrid_state_commit.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+        lib.hybrid_state_prefill.argtypes = [vp, vp, vp, i64, i64, vp, vp, i32, i32, i32, i32, i32, vp, sz,
+                                             ctypes.c_int, vp]
+        lib.hybrid_state_prefill_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32]
+        lib.hybrid_state_prefill_workspace_bytes.restype = sz
+        for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill):
+            fn.restype = ctypes.c_int
+        lib.hybrid_last_error.argtypes = []
+        lib.hybrid_last_error.restype = ctypes.c_char_p
+        lib.hybrid_abi_version.argtypes = []
+        lib.hybrid_abi_version.restype = ctypes.c_int32
+        _lib = lib
+        return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != HA_OK:
+        msg = load_library().hybrid_last_error().decode(errors="replace")
+        raise HybridAttnError(fn, status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HA_BF16
+    if t.dtype == torch.float32:
+        return HA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype) -> int | None:
+    return None if t is None else _dev(t, name, dtype)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def abi_version() -> int:
+    return load_library().hybrid_abi_version()
+
+
+def hybrid_attn_step(q, k, v, state, slots, out=None, blk_lens=None, scale=None, stream=None):
+    """out = Softmax(scale Q K^T) V + ReLU(Q) S[slots] for q/k/v [n_req, blk, H, d];
+    state [n_slots, H, d, d] fp32 (each d x d block stores S transposed)."""
+    n_req, blk, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, d, d):
+        raise ValueError(f"state must be [n_slots, {H}, {d}, {d}]")
+    if slots.shape != (n_req,):
+        raise ValueError("slots must be [n_req]")
+    if out is None:
+        out = torch.zeros_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if blk_lens is not None and blk_lens.shape != (n_req,):
+        raise ValueError("blk_lens must be [n_req]")
+    if scale is None:
+        scale = d ** -0.5
+    lib = load_library()
+    st = lib.hybrid_attn_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(state, "state", torch.float32),
+                              _dev(slots, "slots", torch.int32), _dev(out, "out"),
+                              _opt(blk_lens, "blk_lens", torch.int32), n_req, state.shape[0], H, blk, d,
+                              float(scale), _dtype_code(q), _stream(stream))
+    _check("hybrid_attn_step", st)
+    return out
+
+
+def hybrid_state_commit(k, v, state, slots, blk_lens=None, stream=None):
+    """state[slots] += ReLU(K)^T V (stored transposed), in place."""
+    n_req, blk, H, d = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k, v must share shape and dtype")
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, d, d):
+        raise ValueError(f"state must be [n_slots, {H}, {d}, {d}]")
+    if slots.shape != (n_req,):
+        raise ValueError("slots must be [n_req]")
+    if blk_lens is not None and blk_lens.shape != (n_req,):
+        raise ValueError("blk_lens must be [n_req]")
+    lib = load_library()
+    st = lib.hybrid_state_commit(_dev(k, "k"), _dev(v, "v"), _dev(state, "state", torch.float32),
+                                 _dev(slots, "slots", torch.int32), _opt(blk_lens, "blk_lens", torch.int32),
+                                 n_req, state.shape[0], H, blk, d, _dtype_code(k), _stream(stream))
+    _check("hybrid_state_commit", st)
+    return state
+
+
+def hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk=256) -> int:
+    return int(load_library().hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk))
+
+
+def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, workspace=None,
+                         stream=None):
+    """state[slots[r]] = sum over prompt r of ReLU(k_t)^T v_t (overwrite).
+
+    k, v packed [total, H, d]; cu_seqlens int64 [n_req + 1] on the GPU.
+    ``max_len`` (host int) must bound every prompt length; if omitted it is
+    read back from cu_seqlens (a device synchronisation).  ``workspace`` is a
+    GPU uint8 tensor of at least ``hybrid_state_prefill_workspace_bytes``
+    bytes; if omitted one is allocated through torch."""
+    total, H, d = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k, v must share shape and dtype")
+    n_req = cu_seqlens.shape[0] - 1
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, d, d):
+        raise ValueError(f"state must be [n_slots, {H}, {d}, {d}]")
+    if slots.shape != (n_req,):
+        raise ValueError("slots must be [n_req]")
+    if max_len is None:
+        max_len = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if n_req > 0 else 0
+    need = hybrid_state_prefill_workspace_bytes(n_req, H, d, total, max_len, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    lib = load_library()
+    st = lib.hybrid_state_prefill(_dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens, "cu_seqlens", torch.int64),
+                                  total, max_len, _dev(state, "state", torch.float32),
+                                  _dev(slots, "slots", torch.int32), n_req, state.shape[0], H, d, chunk,
+                                  _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                  _dtype_code(k), _stream(stream))
+    _check("hybrid_state_prefill", st)
+    return state

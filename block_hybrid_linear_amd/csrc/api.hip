@@ -1,0 +1,185 @@
+// C ABI of libhybrid_attn: host-side argument validation and kernel dispatch.
+// Every check runs before anything is enqueued, so a rejected call leaves the
+// outputs and the state store untouched.  The library allocates nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/hybrid_attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ha_status fail(ha_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+ha_status hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return HA_OK;
+    return fail(HA_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool known_dtype(ha_dtype t) { return t == HA_F32 || t == HA_BF16; }
+
+// Prompt tokens per prefill workgroup: whole chunks, about 4096 tokens, so a
+// group's fp32 partial state (d*d*4 bytes) stays a few percent of the bf16
+// K/V bytes it summarises.
+constexpr int64_t kGroupTargetTokens = 4096;
+
+int64_t group_tokens(int32_t chunk)
+{
+    const int64_t per = kGroupTargetTokens / chunk;
+    return (int64_t)chunk * (per > 1 ? per : 1);
+}
+
+int64_t prefill_groups(int64_t max_len, int32_t chunk)
+{
+    if (max_len <= 0) return 0;
+    const int64_t g = group_tokens(chunk);
+    return (max_len + g - 1) / g;
+}
+
+// Checks shared by step and commit.  Returns HA_OK or the failure status.
+ha_status check_block_call(const char* fn, int32_t n_req, int32_t n_slots, int32_t heads,
+                           int32_t blk, int32_t d, ha_dtype dtype)
+{
+    if (n_req < 0) return fail(HA_ERR_INVALID_ARG, "%s: n_req must be >= 0 (got %d)", fn, n_req);
+    if (n_slots <= 0) return fail(HA_ERR_INVALID_ARG, "%s: n_slots must be > 0 (got %d)", fn, n_slots);
+    if (heads <= 0) return fail(HA_ERR_INVALID_ARG, "%s: heads must be > 0 (got %d)", fn, heads);
+    if (blk <= 0 || blk > HYBRID_ATTN_MAX_BLK)
+        return fail(HA_ERR_INVALID_ARG, "%s: blk must be in [1, %d] (got %d)", fn, HYBRID_ATTN_MAX_BLK, blk);
+    if (!known_dtype(dtype)) return fail(HA_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!supported_d(d)) return fail(HA_ERR_UNSUPPORTED, "%s: head dim d=%d not in {16, 32, 64, 128}", fn, d);
+    if ((int64_t)n_req * heads > 0x7fffffffLL)
+        return fail(HA_ERR_INVALID_ARG, "%s: n_req * heads too large", fn);
+    return HA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hybrid_last_error(void) { return g_last_error.c_str(); }
+
+int32_t hybrid_abi_version(void) { return HYBRID_ATTN_ABI_VERSION; }
+
+ha_status hybrid_attn_step(const void* q, const void* k, const void* v, const float* state,
+                           const int32_t* slots, void* out, const int32_t* blk_lens,
+                           int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
+                           float scale, ha_dtype dtype, void* stream)
+{
+    static const char* fn = "hybrid_attn_step";
+    ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
+    if (st != HA_OK) return st;
+    if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    if (n_req == 0) return HA_OK;
+    if (!q || !k || !v || !state || !slots || !out)
+        return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state, slots and out must be non-NULL", fn);
+    ha::StepArgs a{q, k, v, state, slots, out, blk_lens, n_req, n_slots, heads, blk, d, scale,
+                   dtype == HA_BF16};
+    return hip_status(ha::launch_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+ha_status hybrid_state_commit(const void* k, const void* v, float* state, const int32_t* slots,
+                              const int32_t* blk_lens, int32_t n_req, int32_t n_slots,
+                              int32_t heads, int32_t blk, int32_t d, ha_dtype dtype, void* stream)
+{
+    static const char* fn = "hybrid_state_commit";
+    ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
+    if (st != HA_OK) return st;
+    if (n_req == 0) return HA_OK;
+    if (!k || !v || !state || !slots)
+        return fail(HA_ERR_INVALID_ARG, "%s: k, v, state and slots must be non-NULL", fn);
+    ha::PhiKVArgs a{};
+    a.k = k;
+    a.v = v;
+    a.state = state;
+    a.slots = slots;
+    a.blk_lens = blk_lens;
+    a.n_req = n_req;
+    a.n_slots = n_slots;
+    a.heads = heads;
+    a.blk = blk;
+    a.d = d;
+    a.dtype_bf16 = dtype == HA_BF16;
+    return hip_status(ha::launch_commit(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads, int32_t d,
+                                            int64_t total_tokens, int64_t max_len, int32_t chunk)
+{
+    (void)total_tokens;
+    if (n_req <= 0 || heads <= 0 || d <= 0 || chunk <= 0 || max_len <= 0) return 0;
+    return (size_t)n_req * (size_t)prefill_groups(max_len, chunk) * (size_t)heads * (size_t)d *
+           (size_t)d * sizeof(float);
+}
+
+ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_seqlens,
+                               int64_t total_tokens, int64_t max_len, float* state,
+                               const int32_t* slots, int32_t n_req, int32_t n_slots,
+                               int32_t heads, int32_t d, int32_t chunk, void* workspace,
+                               size_t workspace_bytes, ha_dtype dtype, void* stream)
+{
+    static const char* fn = "hybrid_state_prefill";
+    if (n_req < 0) return fail(HA_ERR_INVALID_ARG, "%s: n_req must be >= 0 (got %d)", fn, n_req);
+    if (n_slots <= 0) return fail(HA_ERR_INVALID_ARG, "%s: n_slots must be > 0 (got %d)", fn, n_slots);
+    if (heads <= 0) return fail(HA_ERR_INVALID_ARG, "%s: heads must be > 0 (got %d)", fn, heads);
+    if (chunk <= 0) return fail(HA_ERR_INVALID_ARG, "%s: chunk must be > 0 (got %d)", fn, chunk);
+    if (total_tokens < 0 || max_len < 0)
+        return fail(HA_ERR_INVALID_ARG, "%s: total_tokens and max_len must be >= 0", fn);
+    if (!known_dtype(dtype)) return fail(HA_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!supported_d(d)) return fail(HA_ERR_UNSUPPORTED, "%s: head dim d=%d not in {16, 32, 64, 128}", fn, d);
+    if (n_req > 65535 || heads > 65535)
+        return fail(HA_ERR_INVALID_ARG, "%s: n_req and heads must be <= 65535", fn);
+    const int64_t groups = prefill_groups(max_len, chunk);
+    if (groups > 0x7fffffffLL) return fail(HA_ERR_INVALID_ARG, "%s: max_len too large", fn);
+    if (n_req == 0) return HA_OK;
+    if (!cu_seqlens || !state || !slots)
+        return fail(HA_ERR_INVALID_ARG, "%s: cu_seqlens, state and slots must be non-NULL", fn);
+    if (total_tokens > 0 && (!k || !v))
+        return fail(HA_ERR_INVALID_ARG, "%s: k and v must be non-NULL when total_tokens > 0", fn);
+    const size_t need = hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(HA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
+                    workspace_bytes, workspace ? "" : ", NULL");
+    ha::PhiKVArgs a{};
+    a.k = k;
+    a.v = v;
+    a.cu = cu_seqlens;
+    a.partial = static_cast<float*>(workspace);
+    a.total_tokens = total_tokens;
+    a.group_tokens = group_tokens(chunk);
+    a.groups = (int32_t)groups;
+    a.n_req = n_req;
+    a.n_slots = n_slots;
+    a.heads = heads;
+    a.d = d;
+    a.dtype_bf16 = dtype == HA_BF16;
+    ha::ReduceArgs ra{};
+    ra.partial = a.partial;
+    ra.cu = cu_seqlens;
+    ra.state = state;
+    ra.slots = slots;
+    ra.total_tokens = total_tokens;
+    ra.group_tokens = a.group_tokens;
+    ra.groups = a.groups;
+    ra.n_req = n_req;
+    ra.n_slots = n_slots;
+    ra.heads = heads;
+    ra.d = d;
+    return hip_status(ha::launch_prefill(a, ra, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Device-side helpers for the gfx950 kernels of libhybrid_attn.
+//
+// Matrix-core conventions used throughout (CDNA3/CDNA4 MFMA, wave64):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A operand, lane l: row m = l % 32, k = 8 * (l / 32) + e,  e = 0..7
+//     B operand, lane l: col n = l % 32, k = 8 * (l / 32) + e,  e = 0..7
+//     D/C,       lane l: col n = l % 32, row m = 8 * (r / 4) + 4 * (l / 32) + r % 4,
+//                        r = 0..15 the accumulator register.
+// The reduction index k of one MFMA may be any permutation of the 16 values
+// shared by A and B, which the kernels use to keep loads contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ha {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxBlk = 128;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ReLU on 8 packed bf16: a bf16 is <= 0 exactly when its sign bit is set or it
+// is +0, so max as signed 16-bit integers against 0 maps every value with the
+// sign bit set (including -0) to +0 and keeps the rest.
+__device__ __forceinline__ u16x8 relu_bf16x8(u16x8 x) {
+    u16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (static_cast<int16_t>(x[e]) > 0) ? x[e] : uint16_t(0);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Split 8 fp32 values into bf16 hi + lo with hi + lo == x to about 2^-17
+// relative (hi = RNE(x), lo = RNE(x - hi)); bf16 x bf16 products are exact in
+// fp32, so two matrix-core passes reproduce fp32 operands to ~16 bits.
+__device__ __forceinline__ void split_hi_lo(const float* x, bf16x8& hi, bf16x8& lo) {
+    u16x8 h, l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = f32_to_bf16_bits(x[e]);
+        l[e] = f32_to_bf16_bits(x[e] - bf16_bits_to_f32(h[e]));
+    }
+    hi = as_bf16x8(h);
+    lo = as_bf16x8(l);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float* p, int64_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16_bits(x); }
+};
+
+__device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }
+
+}  // namespace ha

@@ -1,0 +1,164 @@
+/*
+ * hybrid_attn.h -- C ABI of the block-hybrid attention library for MI355X
+ * (gfx950), libhybrid_attn.so.
+ *
+ * Block-hybrid attention (paper "Retrofitting Linear Attention into Diffusion
+ * Language Models": abstract; paper-daily summary page, sections "core
+ * formula" and "technical details in action") keeps exact softmax attention
+ * inside the active denoising block and replaces attention over previous
+ * blocks by linear attention with the feature map phi(x) = ReLU(x):
+ *
+ *     O = Softmax(scale * Q_a K_a^T) V_a + phi(Q_a) S,
+ *     S = sum over committed tokens of phi(k)^T v          (d x d, fp32)
+ *
+ * and after a block is finished S += phi(K_blk)^T V_blk (the worked example's
+ * S_1 = phi(K_1)^T V_1, S_{1,2} = phi(K_1)^T V_1 + phi(K_2)^T V_2).  A prompt
+ * folds into S the same way (prefill).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers are DEVICE pointers unless stated otherwise.  `stream` is a
+ * hipStream_t passed as void* (NULL = the default stream).  Every call is
+ * asynchronous: it validates its host arguments, enqueues kernels on `stream`
+ * and returns; device faults surface at the caller's next synchronisation.
+ *
+ * Ownership: the caller owns all memory.  The library allocates nothing and
+ * keeps no state between calls apart from a thread-local error string.
+ *
+ * Element types (ha_dtype): HA_F32 (float) or HA_BF16 (bfloat16 bits in
+ * uint16).  q/k/v/out share one dtype; the state is always fp32.  All
+ * accumulation is fp32; a bf16 output is rounded to nearest even once.
+ *
+ * Layouts (row-major, innermost dimension contiguous, no other strides):
+ *   active block  q, k, v, out  [n_req][blk][heads][d]
+ *   packed prompt k, v          [total_tokens][heads][d], request r owns rows
+ *                               cu_seqlens[r] .. cu_seqlens[r+1]-1
+ *   state store   state         [n_slots][heads][d][d] fp32.  Each d x d block
+ *                               holds S TRANSPOSED: state[s][h][c][f] =
+ *                               S[f][c] = sum phi(k)_f v_c, i.e. row = value
+ *                               dimension c, column = feature f of phi(k).
+ *                               (This orientation lets the step kernel read S
+ *                               straight into matrix-core operands.)
+ *   slots         int32[n_req]  request r uses state slot slots[r].
+ *   blk_lens      int32[n_req]  valid rows B_r of request r's block, or NULL
+ *                               for "all blk rows valid".
+ *
+ * Ragged blocks: only the first B_r rows of q/k/v are read and only the first
+ * B_r rows of out are written; rows B_r..blk-1 of out are left untouched.
+ * Device data is never read for validation on the host.  On the device a
+ * request whose slot lies outside [0, n_slots) or whose B_r <= 0 is skipped
+ * (nothing read or written for it); B_r > blk is treated as blk.
+ *
+ * Errors: a non-OK status other than HA_ERR_HIP is returned BEFORE anything
+ * is enqueued, so outputs and the state are untouched.  hybrid_last_error()
+ * gives a message for the calling thread's last non-OK status.
+ *   HA_ERR_INVALID_ARG  NULL pointer, negative or zero size, blk > 128,
+ *                       non-finite scale, chunk < 1, workspace too small.
+ *   HA_ERR_UNSUPPORTED  d not in {16, 32, 64, 128} or unknown dtype.
+ *   HA_ERR_HIP          the kernel launch failed (hipGetLastError).
+ * A call with n_req == 0 does nothing and returns HA_OK (pointers unused).
+ *
+ * Aliasing: out must not overlap q, k, v or state; the state store must not
+ * overlap any input.  Calls that write the same state slots must be ordered
+ * on one stream.
+ */
+#ifndef HYBRID_ATTN_H
+#define HYBRID_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYBRID_ATTN_ABI_VERSION 1
+#define HYBRID_ATTN_MAX_BLK 128
+
+typedef enum {
+    HA_OK = 0,
+    HA_ERR_INVALID_ARG = 1,
+    HA_ERR_UNSUPPORTED = 2,
+    HA_ERR_HIP = 3
+} ha_status;
+
+typedef enum { HA_F32 = 0, HA_BF16 = 1 } ha_dtype;
+
+/*
+ * One denoising step of a hybrid layer ("core formula"; worked example:
+ * "block 2's output is the sum of the softmax result and phi(Q_2) S_1"):
+ *
+ *   out[r, i, h, :] = sum_{j < B_r} P_ij v_j  +  phi(q_i) S_{slots[r], h}
+ *   P_ij = exp(scale q_i.k_j - m_i) / sum_{j' < B_r} exp(scale q_i.k_j' - m_i)
+ *
+ * for i < B_r, with no mask inside the block (all tokens of the active block
+ * are denoised in parallel).  `scale` multiplies the logits only; pass
+ * 1/sqrtf(d) for the usual scaling.  The state is read-only here.
+ */
+ha_status hybrid_attn_step(const void* q, const void* k, const void* v,
+                           const float* state, const int32_t* slots,
+                           void* out, const int32_t* blk_lens,
+                           int32_t n_req, int32_t n_slots, int32_t heads,
+                           int32_t blk, int32_t d, float scale,
+                           ha_dtype dtype, void* stream);
+
+/*
+ * Commit a finished block into the prefix state (worked example:
+ * S_{1,2} = S_1 + phi(K_2)^T V_2):
+ *
+ *   S_{slots[r], h} += sum_{j < B_r} phi(k_j)^T v_j        (in place, fp32)
+ *
+ * Not idempotent: committing the same block twice adds it twice.
+ */
+ha_status hybrid_state_commit(const void* k, const void* v, float* state,
+                              const int32_t* slots, const int32_t* blk_lens,
+                              int32_t n_req, int32_t n_slots, int32_t heads,
+                              int32_t blk, int32_t d, ha_dtype dtype,
+                              void* stream);
+
+/*
+ * Fold whole prompts into the state, OVERWRITING each request's slot:
+ *
+ *   S_{slots[r], h} = sum_{t in prompt r} phi(k_t)^T v_t
+ *
+ * (the prefix summary of the worked example, taken over prompt tokens).  A
+ * request with an empty prompt gets S = 0, which is also the reset path.
+ *
+ * cu_seqlens: device int64[n_req + 1], non-decreasing, cu_seqlens[0] = 0,
+ *   cu_seqlens[n_req] = total_tokens.  Requests whose rows fall outside
+ *   [0, total_tokens) are treated as empty.
+ * total_tokens, max_len: HOST scalars; max_len must be >= every prompt
+ *   length (tokens of a longer prompt past max_len are not folded).
+ * chunk: the prompt is cut into chunks of `chunk` tokens; workgroups reduce
+ *   whole chunks into fp32 partial states kept in `workspace`, which a second
+ *   kernel sums per (request, head) in a fixed order (deterministic).  The
+ *   result does not depend on chunk beyond fp32 rounding.
+ * workspace: device scratch of at least
+ *   hybrid_state_prefill_workspace_bytes(...) bytes (NULL allowed if that is
+ *   0); its contents on entry do not matter.
+ */
+ha_status hybrid_state_prefill(const void* k, const void* v,
+                               const int64_t* cu_seqlens,
+                               int64_t total_tokens, int64_t max_len,
+                               float* state, const int32_t* slots,
+                               int32_t n_req, int32_t n_slots, int32_t heads,
+                               int32_t d, int32_t chunk,
+                               void* workspace, size_t workspace_bytes,
+                               ha_dtype dtype, void* stream);
+
+/* Workspace size for hybrid_state_prefill with the same arguments (host). */
+size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads,
+                                            int32_t d, int64_t total_tokens,
+                                            int64_t max_len, int32_t chunk);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* hybrid_last_error(void);
+
+/* HYBRID_ATTN_ABI_VERSION of the loaded library. */
+int32_t hybrid_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYBRID_ATTN_H */

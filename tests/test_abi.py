@@ -1,0 +1,156 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+the header declares, and rejects bad arguments before touching the GPU.
+These calls never launch a kernel: validation fails first, or n_req == 0."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_hybrid_linear_amd as bh
+from block_hybrid_linear_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hybrid_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from block_hybrid_linear_amd.build import build_library
+        build_library()
+    return bh.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hybrid_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("hybrid_attn_step", "hybrid_state_commit", "hybrid_state_prefill",
+              "hybrid_state_prefill_workspace_bytes", "hybrid_last_error", "hybrid_abi_version"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert bh.abi_version() == 1
+
+
+N = None
+
+
+def step(lib, q=1, k=1, v=1, state=1, slots=1, out=1, n_req=2, n_slots=2, heads=4, blk=32, d=64,
+         scale=0.125, dtype=binding.HA_BF16):
+    return lib.hybrid_attn_step(q, k, v, state, slots, out, None, n_req, n_slots, heads, blk, d, scale,
+                                dtype, None)
+
+
+def commit(lib, k=1, v=1, state=1, slots=1, n_req=2, n_slots=2, heads=4, blk=32, d=64, dtype=binding.HA_BF16):
+    return lib.hybrid_state_commit(k, v, state, slots, None, n_req, n_slots, heads, blk, d, dtype, None)
+
+
+def prefill(lib, k=1, v=1, cu=1, total=100, max_len=60, state=1, slots=1, n_req=2, n_slots=2, heads=4, d=64,
+            chunk=256, ws=1, ws_bytes=1 << 40, dtype=binding.HA_BF16):
+    return lib.hybrid_state_prefill(k, v, cu, total, max_len, state, slots, n_req, n_slots, heads, d, chunk,
+                                    ws, ws_bytes, dtype, None)
+
+
+def last(lib):
+    return lib.hybrid_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=100), binding.HA_ERR_UNSUPPORTED, "head dim"),
+    (dict(d=48), binding.HA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=7), binding.HA_ERR_UNSUPPORTED, "dtype"),
+    (dict(blk=0), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(blk=129), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(n_req=-1), binding.HA_ERR_INVALID_ARG, "n_req"),
+    (dict(n_slots=0), binding.HA_ERR_INVALID_ARG, "n_slots"),
+    (dict(heads=0), binding.HA_ERR_INVALID_ARG, "heads"),
+    (dict(scale=float("inf")), binding.HA_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), binding.HA_ERR_INVALID_ARG, "scale"),
+    (dict(q=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(state=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(slots=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(out=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+])
+def test_step_rejects(lib, kw, status, msg):
+    assert step(lib, **kw) == status
+    assert msg in last(lib) and "hybrid_attn_step" in last(lib)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=8), binding.HA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=-1), binding.HA_ERR_UNSUPPORTED, "dtype"),
+    (dict(blk=1000), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(heads=-3), binding.HA_ERR_INVALID_ARG, "heads"),
+    (dict(k=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(state=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+])
+def test_commit_rejects(lib, kw, status, msg):
+    assert commit(lib, **kw) == status
+    assert msg in last(lib) and "hybrid_state_commit" in last(lib)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=256), binding.HA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=2), binding.HA_ERR_UNSUPPORTED, "dtype"),
+    (dict(chunk=0), binding.HA_ERR_INVALID_ARG, "chunk"),
+    (dict(total=-1), binding.HA_ERR_INVALID_ARG, "total_tokens"),
+    (dict(max_len=-5), binding.HA_ERR_INVALID_ARG, "max_len"),
+    (dict(cu=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(k=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(ws_bytes=10), binding.HA_ERR_INVALID_ARG, "workspace"),
+    (dict(ws=None), binding.HA_ERR_INVALID_ARG, "workspace"),
+    (dict(n_req=70000), binding.HA_ERR_INVALID_ARG, "65535"),
+])
+def test_prefill_rejects(lib, kw, status, msg):
+    assert prefill(lib, **kw) == status
+    assert msg in last(lib) and "hybrid_state_prefill" in last(lib)
+
+
+def test_empty_batches_are_noops(lib):
+    """n_req == 0 returns OK without touching any pointer (all NULL here)."""
+    assert step(lib, q=None, k=None, v=None, state=None, slots=None, out=None, n_req=0) == binding.HA_OK
+    assert commit(lib, k=None, v=None, state=None, slots=None, n_req=0) == binding.HA_OK
+    assert prefill(lib, k=None, v=None, cu=None, state=None, slots=None, ws=None, ws_bytes=0,
+                   n_req=0) == binding.HA_OK
+
+
+def test_prefill_workspace_size(lib):
+    f = bh.hybrid_state_prefill_workspace_bytes
+    # groups of whole chunks, about 4096 tokens each
+    assert f(2, 4, 64, 100, 0, 256) == 0
+    assert f(2, 4, 64, 100, 1, 256) == 2 * 1 * 4 * 64 * 64 * 4
+    assert f(2, 4, 64, 100, 4096, 256) == 2 * 1 * 4 * 64 * 64 * 4
+    assert f(2, 4, 64, 100, 4097, 256) == 2 * 2 * 4 * 64 * 64 * 4
+    assert f(1, 1, 128, 0, 65536, 256) == 16 * 128 * 128 * 4
+    assert f(1, 1, 16, 0, 10000, 10000) == 1 * 16 * 16 * 4      # one chunk per group
+    assert f(1, 1, 16, 0, 4095, 1) == 1 * 16 * 16 * 4            # 4096 one-token chunks
+    assert f(0, 1, 16, 0, 10, 1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        bh.hybrid_attn_step(q, q, q, torch.zeros(1, 1, 16, 16), torch.zeros(1, dtype=torch.int32))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        binding._lib_saved = binding._lib
+        try:
+            binding._lib = None
+            binding.load_library(str(tmp_path / "nope.so"))
+        finally:
+            binding._lib = binding._lib_saved

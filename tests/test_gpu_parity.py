@@ -1,0 +1,268 @@
+"""GPU path vs the fp64 oracle on identical seeded inputs, through the C ABI.
+
+Sizes span several 32-row tiles with ragged tails, every supported head dim,
+both dtypes, slot indirection, and the degenerate cases (one valid row, empty
+prompts, invalid slots).  Each step is also checked with its two parts
+isolated (S = 0: softmax only; V = 0: linear only), because at long prefixes
+the linear term dominates the output's magnitude and the whole-output rule
+alone would hide softmax errors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_hybrid_linear_amd as bh
+import oracle
+from block_hybrid_linear_amd import synth
+from block_hybrid_linear_amd.workloads import WORKED_EXAMPLE
+from parity import assert_parity, rows_mask, state_from_oracle, state_to_oracle, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SENTINEL = -1024.0  # exact in bf16 and fp32
+
+
+def gen(shape, seed, dtype, std=1.0):
+    return synth.normal(shape, seed, std=std, dtype=dtype).to(DEV)
+
+
+def check_step(q, k, v, state, slots, blk_lens, scale, what):
+    n_req, blk = q.shape[:2]
+    out = torch.full_like(q, SENTINEL)
+    bh.hybrid_attn_step(q, k, v, state, slots, out=out, blk_lens=blk_lens, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.step(q, k, v, state_to_oracle(state), slots=slots, blk_lens=blk_lens, scale=scale)
+    mask = rows_mask(blk_lens, n_req, blk)
+    o = to64(out)
+    assert np.all(o[~mask] == SENTINEL), f"{what}: rows past B_r were written"
+    return assert_parity(o[mask], ref[mask], q.dtype, what)
+
+
+# --------------------------------------------------------------------------
+# The worked example end to end (fp32, L = 10, B = 4, blocks 4/4/2, H = 2, d = 16)
+# --------------------------------------------------------------------------
+
+def test_worked_example_generation():
+    W = WORKED_EXAMPLE
+    state = torch.zeros(1, W.heads, W.d, W.d, device=DEV)
+    slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    S_ref = np.zeros((1, W.heads, W.d, W.d))
+    for b, n in enumerate(W.block_lens):
+        q, k, v = (gen((1, W.blk, W.heads, W.d), synth.seed_of(W.index, b, 0, t), torch.float32) for t in range(3))
+        lens = torch.tensor([n], dtype=torch.int32, device=DEV)
+        out = bh.hybrid_attn_step(q, k, v, state, slots, blk_lens=lens, scale=W.scale)
+        ref = oracle.step(q, k, v, S_ref, blk_lens=[n], scale=W.scale)
+        assert_parity(out[:, :n], ref[:, :n], torch.float32, f"block {b + 1} output", f32_absolute=True)
+        bh.hybrid_state_commit(k, v, state, slots, blk_lens=lens)
+        S_ref = oracle.commit(k, v, S_ref, blk_lens=[n])
+        torch.cuda.synchronize()
+        assert_parity(state_to_oracle(state), S_ref, torch.float32, f"S after block {b + 1}", f32_absolute=True)
+
+
+# --------------------------------------------------------------------------
+# Step
+# --------------------------------------------------------------------------
+
+STEP_CASES = [  # (d, blk)
+    (128, 32), (128, 64), (128, 100), (128, 128), (128, 1), (128, 5),
+    (64, 32), (64, 33), (64, 128), (32, 17), (32, 64), (32, 96),
+    (16, 4), (16, 32), (16, 128),
+]
+
+
+@pytest.mark.parametrize("d,blk", STEP_CASES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_step_parity(d, blk, dtype):
+    n_req, H, n_slots = 3, 5, 4
+    seed = 7000 + 100 * d + blk
+    q, k, v = (gen((n_req, blk, H, d), seed + t, dtype) for t in range(3))
+    # ragged: one full block, one mid, one single row
+    blk_lens = torch.tensor([blk, max(1, (blk * 2) // 3), 1], dtype=torch.int32, device=DEV)
+    slots = torch.tensor([3, 0, 2], dtype=torch.int32, device=DEV)
+    std = 30.0 if dtype == torch.bfloat16 else 1.0
+    state = synth.normal((n_slots, H, d, d), seed + 3, std=std, dtype=torch.float32).to(DEV)
+    scale = d ** -0.5
+    check_step(q, k, v, state, slots, blk_lens, scale, "full")
+    check_step(q, k, v, torch.zeros_like(state), slots, blk_lens, scale, "softmax part (S = 0)")
+    check_step(q, k, torch.zeros_like(v), state, slots, blk_lens, scale, "linear part (V = 0)")
+
+
+def test_step_no_blk_lens_and_scale():
+    """blk_lens = NULL means every row is valid; the scale is honoured."""
+    n_req, blk, H, d = 2, 48, 3, 128
+    q, k, v = (gen((n_req, blk, H, d), 8100 + t, torch.bfloat16, std=2.0) for t in range(3))
+    state = synth.normal((n_req, H, d, d), 8103, std=5.0, dtype=torch.float32).to(DEV)
+    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
+    for scale in (0.0, 0.02, 0.3):
+        check_step(q, k, v, torch.zeros_like(state), slots, None, scale, f"scale {scale}")
+
+
+def test_step_large_logits():
+    """Logits of several hundred: the max-subtracted softmax stays finite."""
+    n_req, blk, H, d = 1, 32, 2, 64
+    q, k = (gen((n_req, blk, H, d), 8200 + t, torch.bfloat16, std=6.0) for t in range(2))
+    v = gen((n_req, blk, H, d), 8202, torch.bfloat16)
+    state = torch.zeros(1, H, d, d, device=DEV)
+    slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    check_step(q, k, v, state, slots, None, 1.0, "large logits")
+
+
+def test_step_invalid_slot_and_empty_rows_skip():
+    """A request with an out-of-range slot or B_r = 0 writes nothing."""
+    n_req, blk, H, d = 4, 32, 2, 128
+    q, k, v = (gen((n_req, blk, H, d), 8300 + t, torch.bfloat16) for t in range(3))
+    state = synth.normal((2, H, d, d), 8303, dtype=torch.float32).to(DEV)
+    slots = torch.tensor([0, -1, 2, 1], dtype=torch.int32, device=DEV)
+    lens = torch.tensor([32, 32, 32, 0], dtype=torch.int32, device=DEV)
+    out = torch.full_like(q, SENTINEL)
+    bh.hybrid_attn_step(q, k, v, state, slots, out=out, blk_lens=lens)
+    torch.cuda.synchronize()
+    o = to64(out)
+    assert np.all(o[1:] == SENTINEL)
+    ref = oracle.step(q[:1], k[:1], v[:1], state_to_oracle(state)[:1], scale=d ** -0.5)
+    assert_parity(o[:1], ref, torch.bfloat16, "valid request")
+
+
+def test_step_deterministic():
+    n_req, blk, H, d = 4, 64, 4, 128
+    q, k, v = (gen((n_req, blk, H, d), 8400 + t, torch.bfloat16) for t in range(3))
+    state = synth.normal((n_req, H, d, d), 8403, std=40.0, dtype=torch.float32).to(DEV)
+    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
+    a = bh.hybrid_attn_step(q, k, v, state, slots)
+    b = bh.hybrid_attn_step(q, k, v, state, slots)
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# Commit
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (128, 100), (128, 128), (128, 1),
+                                   (64, 32), (64, 77), (32, 32), (32, 5), (16, 4), (16, 64)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_commit_parity(d, blk, dtype):
+    n_req, H, n_slots = 3, 4, 5
+    seed = 9000 + 100 * d + blk
+    k, v = (gen((n_req, blk, H, d), seed + t, dtype) for t in range(2))
+    lens = torch.tensor([blk, max(1, blk // 2), 1], dtype=torch.int32, device=DEV)
+    slots = torch.tensor([4, 1, 2], dtype=torch.int32, device=DEV)
+    state = synth.normal((n_slots, H, d, d), seed + 3, dtype=torch.float32).to(DEV)
+    S0 = state_to_oracle(state)
+    bh.hybrid_state_commit(k, v, state, slots, blk_lens=lens)
+    torch.cuda.synchronize()
+    ref = oracle.commit(k, v, S0, slots=slots, blk_lens=lens)
+    got = state_to_oracle(state)
+    assert np.array_equal(got[[0, 3]], S0[[0, 3]]), "slots not named were modified"
+    assert_parity(got, ref, dtype, "state after commit")
+    # not idempotent: a second identical commit adds the block again
+    bh.hybrid_state_commit(k, v, state, slots, blk_lens=lens)
+    torch.cuda.synchronize()
+    ref2 = oracle.commit(k, v, ref, slots=slots, blk_lens=lens)
+    assert_parity(state_to_oracle(state), ref2, dtype, "state after second commit")
+
+
+def test_commit_order_independent():
+    """Commits of several blocks in any order give the same state (fp32
+    reassociation only), equal to the oracle's sum."""
+    H, d, blk = 4, 128, 32
+    blocks = [tuple(gen((2, blk, H, d), 9500 + 10 * i + t, torch.bfloat16) for t in range(2)) for i in range(4)]
+    slots = torch.arange(2, dtype=torch.int32, device=DEV)
+    finals = []
+    for order in ([0, 1, 2, 3], [3, 1, 0, 2], [2, 3, 1, 0]):
+        state = torch.zeros(2, H, d, d, device=DEV)
+        for i in order:
+            bh.hybrid_state_commit(blocks[i][0], blocks[i][1], state, slots)
+        finals.append(state.clone())
+    torch.cuda.synchronize()
+    ref = np.zeros((2, H, d, d))
+    for kk, vv in blocks:
+        ref = oracle.commit(kk, vv, ref)
+    for f in finals:
+        assert_parity(state_to_oracle(f), ref, torch.bfloat16, "commit order")
+
+
+# --------------------------------------------------------------------------
+# Prefill
+# --------------------------------------------------------------------------
+
+def prefill_case(lengths, H, d, dtype, seed, chunk=256, n_slots=None, slots=None):
+    lengths = list(lengths)
+    n_req = len(lengths)
+    cu = synth.cu_from_lengths(lengths)
+    total = int(cu[-1])
+    k, v = (synth.normal((total, H, d), seed + t, dtype=dtype) for t in range(2))
+    n_slots = n_slots or n_req
+    slots = slots if slots is not None else list(range(n_req))
+    state = torch.full((n_slots, H, d, d), 77.0, device=DEV)
+    before = to64(state)
+    bh.hybrid_state_prefill(k.to(DEV), v.to(DEV), cu.to(DEV), state,
+                            torch.tensor(slots, dtype=torch.int32, device=DEV),
+                            max_len=max(lengths) if lengths else 0, chunk=chunk)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(k, v, cu, S=state_to_oracle(torch.from_numpy(before).float()), slots=slots)
+    return state, ref, before, slots
+
+
+@pytest.mark.parametrize("d", [128, 64, 32, 16])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_parity(d, dtype):
+    lengths = [0, 1, 31, 4096, 4097, 9000] if dtype == torch.bfloat16 else [0, 1, 31, 700]
+    state, ref, before, slots = prefill_case(lengths, 2, d, dtype, 10000 + d)
+    assert_parity(state_to_oracle(state), ref, dtype, "prefilled state")
+    assert np.all(state_to_oracle(state)[slots[0]] == 0.0), "empty prompt must reset the slot"
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 256, 9000])
+def test_prefill_chunk_independent(chunk):
+    lengths = [9000, 300, 4100]
+    state, ref, _, _ = prefill_case(lengths, 2, 128, torch.bfloat16, 11000, chunk=chunk)
+    assert_parity(state_to_oracle(state), ref, torch.bfloat16, f"chunk {chunk}")
+
+
+def test_prefill_slot_indirection():
+    lengths = [500, 0, 1200]
+    state, ref, before, slots = prefill_case(lengths, 3, 64, torch.bfloat16, 11500, n_slots=6, slots=[5, 0, 2])
+    got = state_to_oracle(state)
+    assert np.array_equal(got[[1, 3, 4]], state_to_oracle(torch.from_numpy(before))[[1, 3, 4]])
+    assert_parity(got, ref, torch.bfloat16, "prefill with slots")
+
+
+def test_prefill_equals_commits_and_resume_bitwise():
+    """Prefill of a prompt = commits of its blocks (within tolerance); and a
+    state saved after block k, restored, continues bit-identically."""
+    H, d, blk, nb = 4, 128, 32, 6
+    k, v = (synth.normal((nb * blk, H, d), 12000 + t) for t in range(2))
+    slots = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sp = torch.zeros(1, H, d, d, device=DEV)
+    bh.hybrid_state_prefill(k.to(DEV), v.to(DEV), torch.tensor([0, nb * blk], device=DEV), sp, slots,
+                            max_len=nb * blk)
+    sc = torch.zeros(1, H, d, d, device=DEV)
+    saved = None
+    kb, vb = k.view(nb, 1, blk, H, d).to(DEV), v.view(nb, 1, blk, H, d).to(DEV)
+    for b in range(nb):
+        bh.hybrid_state_commit(kb[b], vb[b], sc, slots)
+        if b == 2:
+            saved = sc.clone()
+    torch.cuda.synchronize()
+    ref = oracle.prefill(k, v, [0, nb * blk])
+    assert_parity(state_to_oracle(sp), ref, torch.bfloat16, "prefill")
+    assert_parity(state_to_oracle(sc), ref, torch.bfloat16, "commits")
+    resumed = saved.clone()
+    for b in range(3, nb):
+        bh.hybrid_state_commit(kb[b], vb[b], resumed, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(resumed, sc)
+
+
+def test_state_roundtrip_layout():
+    """The library's transposed state layout: a state built by the oracle and
+    stored transposed gives the oracle's step output."""
+    n_req, blk, H, d = 2, 32, 2, 128
+    q, k, v = (gen((n_req, blk, H, d), 12500 + t, torch.bfloat16) for t in range(3))
+    S = np.random.default_rng(5).standard_normal((n_req, H, d, d)) * 10
+    state = state_from_oracle(S)
+    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
+    out = bh.hybrid_attn_step(q, k, torch.zeros_like(v), state, slots)
+    torch.cuda.synchronize()
+    ref = oracle.step(q, k, np.zeros(v.shape), state_to_oracle(state), scale=d ** -0.5)
+    assert_parity(out, ref, torch.bfloat16, "layout")

@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Throughput of the block-hybrid attention hot path on one MI355X.
+
+One bench step is one pass of the whole hot path over one batch of synthetic
+input -- the long-prompt prefill + decode workload of one hybrid layer, all
+heads: 8 requests x 32 heads x d = 128 with ragged prompts of 16k-64k tokens
+(bf16, N(0,1)) folded into the fp32 state by hybrid_state_prefill (chunk
+256), then 16 blocks of B = 64 tokens, each denoised by 4 hybrid_attn_step
+calls and committed by one hybrid_state_commit.  Inputs are generated and
+resident in HBM before timing; each step's Q/K/V are distinct tensors.
+
+Reported value: tokens/s through the hybrid layer, where a prompt token
+counts once (folded into S) and an active-block token counts once per
+denoising step.  Per-call HIP-event timings inside the timed region give each
+kernel's achieved GB/s and TFLOP/s against the MI355X peaks (8 TB/s HBM,
+2.5 PFLOP/s dense bf16); ``roofline`` reports the call with the largest share
+of the time.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample
+of the same workload's (request, head) units and scales it to tokens/s.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_hybrid_linear_amd as bh  # noqa: E402
+from block_hybrid_linear_amd import synth  # noqa: E402
+from block_hybrid_linear_amd.workloads import BLOCK_LOOP, PREFILL_DECODE, SERVING_STEP  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROMPT_BLOCK = 99          # seed "block" index reserved for prompt tensors
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes / flops per call (what the method must move: Q/K/V once,
+# S once or twice, O once; never the prefix keys/values it replaces)
+# ---------------------------------------------------------------------------
+
+def step_cost(units, B, d, e=2):
+    return units * (4 * B * d * e + d * d * 4), units * (4 * B * B * d + 2 * B * d * d)
+
+
+def commit_cost(units, B, d, e=2):
+    return units * (2 * B * d * e + 2 * d * d * 4), units * (2 * B * d * d)
+
+
+def prefill_cost(token_heads, units, d, e=2):
+    return token_heads * 2 * d * e + units * d * d * 4, token_heads * 2 * d * d
+
+
+# ---------------------------------------------------------------------------
+# Workload builders
+# ---------------------------------------------------------------------------
+
+class Job:
+    """Inputs resident in HBM plus the list of calls of one bench step."""
+
+    def __init__(self, wl, dev="cuda"):
+        self.wl = wl
+        self.dev = dev
+        n, H, d, B = wl.n_req, wl.heads, wl.d, wl.blk
+        self.slots = torch.arange(n, dtype=torch.int32, device=dev)
+        self.state = torch.zeros(n, H, d, d, device=dev)
+        self.calls = []          # (kind, fn)
+        self.tokens = 0
+        self.cost = {}           # kind -> (bytes, flops) per call
+        if wl.prompt_range:
+            lens = synth.uniform_int(n, *wl.prompt_range, synth.seed_of(wl.index, tensor=synth.TENSOR_LEN))
+            self.prompt_lens = lens
+            cu = synth.cu_from_lengths(lens)
+            total = int(cu[-1])
+            self.pk = synth.normal((total, H, d), synth.seed_of(wl.index, PROMPT_BLOCK, 0, synth.TENSOR_K), device=dev)
+            self.pv = synth.normal((total, H, d), synth.seed_of(wl.index, PROMPT_BLOCK, 0, synth.TENSOR_V), device=dev)
+            self.cu = cu.to(dev)
+            self.max_len = int(lens.max())
+            self.ws = torch.empty(max(1, bh.hybrid_state_prefill_workspace_bytes(n, H, d, total, self.max_len,
+                                                                                  wl.chunk)),
+                                  dtype=torch.uint8, device=dev)
+            self.calls.append(("prefill", self._prefill))
+            self.tokens += total
+            self.cost["prefill"] = prefill_cost(total * H, n * H, d)
+        self.q, self.k, self.v = [], [], []
+        for b in range(wl.n_blocks):
+            for t in range(wl.steps_per_block):
+                s = lambda tid: synth.seed_of(wl.index, b, t, tid)  # noqa: E731
+                self.q.append(synth.normal((n, B, H, d), s(0), std=wl.std, device=dev))
+                self.k.append(synth.normal((n, B, H, d), s(1), std=wl.std, device=dev))
+                self.v.append(synth.normal((n, B, H, d), s(2), std=wl.std, device=dev))
+        self.out = torch.empty(n, B, H, d, dtype=torch.bfloat16, device=dev)
+        i = 0
+        for b in range(wl.n_blocks):
+            for t in range(wl.steps_per_block):
+                self.calls.append(("step", self._step_fn(i)))
+                self.tokens += n * B
+                i += 1
+            if wl.n_blocks > 1 or wl.steps_per_block > 1:
+                self.calls.append(("commit", self._commit_fn(i - 1)))   # the block's last step's K, V
+        self.cost["step"] = step_cost(n * H, B, d)
+        self.cost["commit"] = commit_cost(n * H, B, d)
+
+    def _prefill(self):
+        bh.hybrid_state_prefill(self.pk, self.pv, self.cu, self.state, self.slots, max_len=self.max_len,
+                                chunk=self.wl.chunk, workspace=self.ws)
+
+    def _step_fn(self, i):
+        return lambda: bh.hybrid_attn_step(self.q[i], self.k[i], self.v[i], self.state, self.slots, out=self.out,
+                                           scale=self.wl.scale)
+
+    def _commit_fn(self, i):
+        return lambda: bh.hybrid_state_commit(self.k[i], self.v[i], self.state, self.slots)
+
+    def reset(self):
+        self.state.zero_()
+
+    def run(self, events=None):
+        for kind, fn in self.calls:
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                events.append((kind, e0, e1))
+            else:
+                fn()
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload's units
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(job: Job, budget_s: float) -> dict:
+    import oracle
+    wl = job.wl
+    n, H = wl.n_req, wl.heads
+    multi = wl.n_blocks > 1 or wl.steps_per_block > 1
+
+    def run(h_s: int) -> float:
+        """The whole job for all requests x the first h_s heads; host copies of
+        the sample are made first and are not timed."""
+        hs = slice(0, h_s)
+        pk = job.pk[:, hs].cpu() if wl.prompt_range else None
+        pv = job.pv[:, hs].cpu() if wl.prompt_range else None
+        qkv = [(job.q[i][:, :, hs].cpu(), job.k[i][:, :, hs].cpu(), job.v[i][:, :, hs].cpu())
+               for i in range(len(job.q))]
+        import numpy as np
+        t0 = time.perf_counter()
+        S = np.zeros((n, h_s, wl.d, wl.d))
+        if wl.prompt_range:
+            S = oracle.prefill(pk, pv, job.cu.cpu())
+        i = 0
+        for _ in range(wl.n_blocks):
+            for _ in range(wl.steps_per_block):
+                oracle.step(*qkv[i], S, scale=wl.scale)
+                i += 1
+            if multi:
+                S = oracle.commit(qkv[i - 1][1], qkv[i - 1][2], S)
+        return time.perf_counter() - t0
+
+    dt1 = run(1)                                   # calibration on one head
+    h_s = 1
+    while h_s * 2 <= H and dt1 * h_s * 2 <= budget_s:
+        h_s *= 2
+    dt = run(h_s) if h_s > 1 else dt1
+    return {"value": round(job.tokens * (h_s / H) / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"all {n} requests x {h_s} of {H} heads of the same job (prefill + every step and "
+                      f"commit for those units), {dt:.1f} s of fp64 oracle time, scaled by {H}/{h_s}",
+            "seconds": round(dt, 2)}
+
+
+# ---------------------------------------------------------------------------
+# Traffic measured by rocprofv3 counters, valid only for the kernel source it
+# was taken on (profiles/traffic.md holds one line per kernel)
+# ---------------------------------------------------------------------------
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_hybrid_linear_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(call: str, workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    pat = re.compile(r"^\|\s*%s\s*\|\s*%s\s*\|\s*([0-9a-f]+)\s*\|\s*([0-9.eE+]+)\s*\|" % (re.escape(workload),
+                                                                                    re.escape(call)))
+    for line in open(path):
+        m = pat.match(line)
+        if m and m.group(1) == source_digest():
+            return float(m.group(2))
+    return None
+
+
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {w.name: w for w in (PREFILL_DECODE, BLOCK_LOOP, SERVING_STEP)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=PREFILL_DECODE.name, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle time")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU only "
+              "(every (request, head) unit is independent, see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    bh.load_library()
+    wl = WORKLOADS[args.workload]
+    log(f"[bench] building inputs for {wl.name}")
+    job = Job(wl)
+    torch.cuda.synchronize()
+    log(f"[bench] {len(job.calls)} calls per step, {job.tokens} tokens per step; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        job.reset()
+        job.run()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, per-call events recorded on the stream
+    events = []
+    step_ms = []
+    for s in range(args.steps):
+        job.reset()                       # a fresh generation; not inside the timed interval
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        job.run(events)
+        b.record()
+        torch.cuda.synchronize()
+        step_ms.append(a.elapsed_time(b))
+        log(f"[bench] step {s}: {step_ms[-1]:.3f} ms")
+    total_ms = sum(step_ms)
+    ms_per_step = total_ms / args.steps
+
+    kernels = {}
+    for kind in job.cost:
+        ts = [e0.elapsed_time(e1) for k, e0, e1 in events if k == kind]
+        if not ts:
+            continue
+        avg_ms = sum(ts) / len(ts)
+        byts, flops = job.cost[kind]
+        gbs = byts / (avg_ms * 1e-3) / 1e9
+        tfs = flops / (avg_ms * 1e-3) / 1e12
+        kernels[kind] = {"calls_per_step": len(ts) // args.steps, "avg_us": round(avg_ms * 1e3, 2),
+                         "alg_bytes": byts, "alg_flops": flops, "GBps": round(gbs, 1),
+                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOPs": round(tfs, 2),
+                         "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 5),
+                         "share_of_step": round(avg_ms * len(ts) / args.steps / ms_per_step, 4)}
+    dom = max(kernels, key=lambda k: kernels[k]["share_of_step"])
+    kd = kernels[dom]
+    traffic = measured_traffic(dom, wl.name)
+    roofline = {"bound": "hbm", "achieved": kd["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kd["hbm_frac"], "traffic": traffic, "kernel": dom}
+
+    value = job.tokens * args.steps / (total_ms * 1e-3)
+    result = {
+        "metric": "hybrid-attn denoising throughput (tokens/s) + % HBM peak; commit/prefill % MFMA",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "n_req": wl.n_req, "heads": wl.heads, "head_dim": wl.d,
+                   "block": wl.blk, "blocks": wl.n_blocks, "steps_per_block": wl.steps_per_block,
+                   "prompt_range": list(wl.prompt_range) or None, "chunk": wl.chunk if wl.prompt_range else None,
+                   "qkv_std": wl.std, "tokens_per_step": job.tokens, "parallelism": "single_gpu",
+                   "source_digest": source_digest()},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(job, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

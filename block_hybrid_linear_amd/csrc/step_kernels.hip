@@ -8,9 +8,10 @@
 namespace ha {
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core step, head dim D in {32, 64, 128}, blk <= 128.
+// bf16 matrix-core step, head dim D in {32, 64, 128}, blk <= 32 * NQ.
 //
-// One workgroup per (request, head); wave w owns value columns [32w, 32w+32).
+// One workgroup per (request, head) with NQ x D/32 waves; wave (qt, ct) owns
+// query rows [32 qt, 32 qt + 32) and value columns [32 ct, 32 ct + 32).
 // Everything is computed transposed so that each lane ends up holding one
 // query row:
 //   L^T = K Q^T          (keys x queries): lane l holds query i = l % 32 and
@@ -25,17 +26,24 @@ namespace ha {
 // mantissa bits; Q, K, V are bf16 already, so their products are exact.
 // V^T operands are gathered with 2-byte loads: per load instruction lanes
 // 0..31 read 64 contiguous bytes of one row and lanes 32..63 another.
-// No LDS and no barriers: waves of a unit only share L1/L2 lines of Q and K.
 //
-// Value-column permutation: the A-operand row m of wave w maps to column
-//   c(m) = 32w + 16 * ((m / 4) % 2) + 4 * (m / 8) + m % 4,
+// Latency: every load of a wave is unconditional (rows past B_r are clamped
+// to row B_r - 1 and masked out of the softmax) and issued before the first
+// matrix op, in the order Q, K, V, S, so the S stream -- two thirds of the
+// bytes -- is in flight while the softmax part is computed.  No LDS and no
+// barriers: waves only share L1/L2 lines of Q and K.
+//
+// Value-column permutation: the A-operand row m of tile ct maps to column
+//   c(m) = 32 ct + 16 * ((m / 4) % 2) + 4 * (m / 8) + m % 4,
 // chosen so that accumulator register r of lane half hh holds column
-// 32w + 16 hh + r: each lane stores 16 contiguous output columns (32 bytes).
+// 32 ct + 16 hh + r: each lane stores 16 contiguous output columns (32 bytes).
 // ---------------------------------------------------------------------------
-template <int D, int NKT>
-__global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
+template <int D, int NQ>
+__global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;              // k-steps over the head dimension
+    constexpr int NC = D / 32;              // value-column tiles
+    constexpr int NKT = NQ;                 // key tiles (keys = queries = block rows)
     const int unit = blockIdx.x;
     const int r = unit / a.heads, h = unit % a.heads;
     int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
@@ -44,6 +52,8 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
 
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int qt = w / NC, ct = w % NC;
+    if (qt * 32 >= Br) return;                               // no valid query in this tile
     const int l32 = lane % 32, hh = lane / 32;
     const int64_t rs = (int64_t)a.heads * D;                 // token row stride
     const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
@@ -53,125 +63,249 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     uint16_t* out = static_cast<uint16_t*>(a.out) + base;
     const float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
 
-    const int cA = 32 * w + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;  // A row -> column
+    const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;  // A row -> column
     const int nkt = (Br + 31) / 32;                          // <= NKT
+    const int last = Br - 1;
     const float sl2 = a.scale * 1.4426950408889634f;         // logits in log2 units
 
-    bf16x8 shi[KS], slo[KS];                                 // S^T operands, kept across query tiles
-
-    for (int qt = 0; qt < nkt; ++qt) {
-        // ---- Q operand (B of L^T and, ReLU'd, B of S^T phi(Q)^T): row i, k-step s
-        const int i = qt * 32 + l32;
-        u16x8 qv[KS];
+    // ---- issue every load: Q, K, V^T gathers, then S^T
+    const int i = qt * 32 + l32;
+    const uint16_t* qrow = q + (int64_t)(i < Br ? i : last) * rs + 8 * hh;
+    u16x8 qv[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            qv[s] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (i < Br) qv[s] = *reinterpret_cast<const u16x8*>(q + i * rs + 16 * s + 8 * hh);
-        }
-        // ---- L^T tiles and V^T operands for every key tile
-        f32x16 lt[NKT];
-        u16x8 vop[NKT][2];
+    for (int s = 0; s < KS; ++s) qv[s] = *reinterpret_cast<const u16x8*>(qrow + 16 * s);
+    u16x8 kv[NKT][KS];
+    u16x8 vop[NKT][2];
 #pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
-            lt[jt] = f32x16{};
-            if (jt < nkt) {
-                const int j = jt * 32 + l32;
-                f32x16 acc = {};
+    for (int jt = 0; jt < NKT; ++jt) {
+        const int j = jt * 32 + l32;
+        const uint16_t* krow = k + (int64_t)(j < Br ? j : last) * rs + 8 * hh;
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    u16x8 kv = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                    if (j < Br) kv = *reinterpret_cast<const u16x8*>(k + j * rs + 16 * s + 8 * hh);
-                    acc = mfma32(as_bf16x8(kv), as_bf16x8(qv[s]), acc);
-                }
-                lt[jt] = acc;
-                // V^T operand for k-step (jt, gp): key j = jt*32 + 16gp + 8(e/4) + 4hh + e%4,
-                // matching accumulator registers 8gp .. 8gp+7 of L^T.
+        for (int s = 0; s < KS; ++s) kv[jt][s] = *reinterpret_cast<const u16x8*>(krow + 16 * s);
+    }
 #pragma unroll
-                for (int gp = 0; gp < 2; ++gp) {
+    for (int jt = 0; jt < NKT; ++jt) {
+        // key j = jt*32 + 16gp + 8(e/4) + 4hh + e%4 matches L^T accumulator register 8gp + e
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int jj = jt * 32 + 16 * gp + 8 * (e / 4) + 4 * hh + e % 4;
-                        vop[jt][gp][e] = jj < Br ? v[jj * rs + cA] : uint16_t(0);
-                    }
-                }
-            }
-        }
-        // ---- S^T row cA: 8 contiguous fp32 per k-step, streamed once per unit
-        if (qt == 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const f32x4* sp = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 16 * s + 8 * hh);
-                const f32x4 s0 = sp[0], s1 = sp[1];
-                const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-                split_hi_lo(sv, shi[s], slo[s]);
-            }
-        }
-        // ---- row softmax over the Br valid keys (one query per lane pair)
-        float m = -INFINITY;
-#pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
-            if (jt < nkt) {
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-                    const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
-                    lt[jt][rr] = x;
-                    m = fmaxf(m, x);
-                }
-            }
-        }
-        m = fmaxf(m, __shfl_xor(m, 32));
-        float sum = 0.f;
-#pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
-            if (jt < nkt) {
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const float p = exp2f(lt[jt][rr] - m);
-                    lt[jt][rr] = p;
-                    sum += p;
-                }
-            }
-        }
-        sum += __shfl_xor(sum, 32);
-        const float inv = 1.0f / sum;
-
-        // ---- O^T = V^T P^T (P as hi + lo bf16)
-        f32x16 o = {};
-#pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
-            if (jt < nkt) {
-#pragma unroll
-                for (int gp = 0; gp < 2; ++gp) {
-                    float p[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) p[e] = lt[jt][8 * gp + e] * inv;
-                    bf16x8 phi, plo;
-                    split_hi_lo(p, phi, plo);
-                    o = mfma32(as_bf16x8(vop[jt][gp]), phi, o);
-                    o = mfma32(as_bf16x8(vop[jt][gp]), plo, o);
-                }
-            }
-        }
-        // ---- O^T += S^T phi(Q)^T (S as hi + lo bf16)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 pq = as_bf16x8(relu_bf16x8(qv[s]));
-            o = mfma32(shi[s], pq, o);
-            o = mfma32(slo[s], pq, o);
-        }
-        // ---- store: lane holds query i, columns 32w + 16hh + 0..15
-        if (i < Br) {
-            u16x8 o0, o1;
+        for (int gp = 0; gp < 2; ++gp) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                o0[e] = f32_to_bf16_bits(o[e]);
-                o1[e] = f32_to_bf16_bits(o[8 + e]);
+                const int jj = jt * 32 + 16 * gp + 8 * (e / 4) + 4 * hh + e % 4;
+                vop[jt][gp][e] = v[(int64_t)(jj < Br ? jj : last) * rs + cA];
             }
-            u16x8* op = reinterpret_cast<u16x8*>(out + i * rs + 32 * w + 16 * hh);
-            op[0] = o0;
-            op[1] = o1;
         }
+    }
+    f32x4 sraw[KS][2];
+    const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        sraw[s][0] = srow[4 * s];
+        sraw[s][1] = srow[4 * s + 1];
+    }
+    // keep the scheduler from sinking these loads next to their uses: the
+    // whole wave's bytes must be in flight before the first wait
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- L^T = K Q^T per key tile
+    f32x16 lt[NKT];
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+        f32x16 acc = {};
+        if (jt < nkt) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) acc = mfma32(as_bf16x8(kv[jt][s]), as_bf16x8(qv[s]), acc);
+        }
+        lt[jt] = acc;
+    }
+    // ---- row softmax over the Br valid keys (one query per lane pair)
+    float m = -INFINITY;
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+            const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
+            lt[jt][rr] = x;
+            m = fmaxf(m, x);
+        }
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float sum = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(lt[jt][rr] - m);   // exp2(-inf) = 0 for masked keys
+            lt[jt][rr] = p;
+            sum += p;
+        }
+    }
+    sum += __shfl_xor(sum, 32);
+    const float inv = __builtin_amdgcn_rcpf(sum);
+
+    // ---- O^T = V^T P^T (P as hi + lo bf16)
+    f32x16 o = {};
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+        if (jt < nkt) {
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = lt[jt][8 * gp + e] * inv;
+                bf16x8 phi, plo;
+                split_hi_lo(p, phi, plo);
+                o = mfma32(as_bf16x8(vop[jt][gp]), phi, o);
+                o = mfma32(as_bf16x8(vop[jt][gp]), plo, o);
+            }
+        }
+    }
+    // ---- O^T += S^T phi(Q)^T (S as hi + lo bf16)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const float sv[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
+                             sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
+        bf16x8 shi, slo;
+        split_hi_lo(sv, shi, slo);
+        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv[s]));
+        o = mfma32(shi, pq, o);
+        o = mfma32(slo, pq, o);
+    }
+    // ---- store: lane holds query i, columns 32 ct + 16 hh + 0..15
+    if (i < Br) {
+        u16x8 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o0[e] = f32_to_bf16_bits(o[e]);
+            o1[e] = f32_to_bf16_bits(o[8 + e]);
+        }
+        u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
+        op[0] = o0;
+        op[1] = o1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 matrix-core step for long blocks (64 < blk <= 128): same layout as
+// above, but the keys are visited one 32-key tile at a time with an online
+// softmax (running max and sum, accumulator rescaled when the max grows), so
+// the register footprint does not grow with the block; the S^T stream is
+// issued after the key loop and added to the normalised softmax output.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(4 * D / 32 * kWave) void step_bf16_mfma_long(StepArgs a)
+{
+    constexpr int KS = D / 16;
+    constexpr int NC = D / 32;
+    const int unit = blockIdx.x;
+    const int r = unit / a.heads, h = unit % a.heads;
+    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    Br = Br > a.blk ? a.blk : Br;
+    const int slot = a.slots[r];
+    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;
+
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int qt = w / NC, ct = w % NC;
+    if (qt * 32 >= Br) return;
+    const int l32 = lane % 32, hh = lane / 32;
+    const int64_t rs = (int64_t)a.heads * D;
+    const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + base;
+    const uint16_t* k = static_cast<const uint16_t*>(a.k) + base;
+    const uint16_t* v = static_cast<const uint16_t*>(a.v) + base;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + base;
+    const float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
+    const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
+    const int nkt = (Br + 31) / 32;
+    const int last = Br - 1;
+    const float sl2 = a.scale * 1.4426950408889634f;
+
+    const int i = qt * 32 + l32;
+    const uint16_t* qrow = q + (int64_t)(i < Br ? i : last) * rs + 8 * hh;
+    u16x8 qv[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qv[s] = *reinterpret_cast<const u16x8*>(qrow + 16 * s);
+
+    float m = -INFINITY, l = 0.f;
+    f32x16 o = {};
+#pragma unroll 1
+    for (int jt = 0; jt < nkt; ++jt) {
+        const int j = jt * 32 + l32;
+        const uint16_t* krow = k + (int64_t)(j < Br ? j : last) * rs + 8 * hh;
+        u16x8 kv[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kv[s] = *reinterpret_cast<const u16x8*>(krow + 16 * s);
+        u16x8 vop[2];
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jj = jt * 32 + 16 * gp + 8 * (e / 4) + 4 * hh + e % 4;
+                vop[gp][e] = v[(int64_t)(jj < Br ? jj : last) * rs + cA];
+            }
+        }
+        f32x16 lt = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) lt = mfma32(as_bf16x8(kv[s]), as_bf16x8(qv[s]), lt);
+        float mt = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int jr = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+            const float x = jr < Br ? lt[rr] * sl2 : -INFINITY;
+            lt[rr] = x;
+            mt = fmaxf(mt, x);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float corr = __builtin_amdgcn_exp2f(m - mn);     // 0 on the first tile
+        float ls = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(lt[rr] - mn);
+            lt[rr] = p;
+            ls += p;
+        }
+        ls += __shfl_xor(ls, 32);
+        l = l * corr + ls;
+        m = mn;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) o[rr] *= corr;
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = lt[8 * gp + e];
+            bf16x8 phi, plo;
+            split_hi_lo(p, phi, plo);
+            o = mfma32(as_bf16x8(vop[gp]), phi, o);
+            o = mfma32(as_bf16x8(vop[gp]), plo, o);
+        }
+    }
+    const float inv = __builtin_amdgcn_rcpf(l);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) o[rr] *= inv;
+
+    const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const f32x4 s0 = srow[4 * s], s1 = srow[4 * s + 1];
+        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        bf16x8 shi, slo;
+        split_hi_lo(sv, shi, slo);
+        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv[s]));
+        o = mfma32(shi, pq, o);
+        o = mfma32(slo, pq, o);
+    }
+    if (i < Br) {
+        u16x8 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o0[e] = f32_to_bf16_bits(o[e]);
+            o1[e] = f32_to_bf16_bits(o[8 + e]);
+        }
+        u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
+        op[0] = o0;
+        op[1] = o1;
     }
 }
 
@@ -232,9 +366,9 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
 template <int D>
 static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
 {
-    if (a.blk <= 32) step_bf16_mfma<D, 1><<<units, D / 32 * kWave, 0, stream>>>(a);
-    else if (a.blk <= 64) step_bf16_mfma<D, 2><<<units, D / 32 * kWave, 0, stream>>>(a);
-    else step_bf16_mfma<D, 4><<<units, D / 32 * kWave, 0, stream>>>(a);
+    if (a.blk <= 32) step_bf16_mfma<D, 1><<<units, 1 * D / 32 * kWave, 0, stream>>>(a);
+    else if (a.blk <= 64) step_bf16_mfma<D, 2><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
+    else step_bf16_mfma_long<D><<<units, 4 * D / 32 * kWave, 0, stream>>>(a);
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream)

@@ -24,26 +24,48 @@ namespace ha {
 // loads 8 contiguous fp32 of row c per k-step.  fp32 S and fp32 P enter the
 // bf16 matrix cores as hi + lo bf16 pairs (two passes), which keeps ~16
 // mantissa bits; Q, K, V are bf16 already, so their products are exact.
-// V^T operands are gathered with 2-byte loads: per load instruction lanes
-// 0..31 read 64 contiguous bytes of one row and lanes 32..63 another.
 //
-// Latency: every load of a wave is unconditional (rows past B_r are clamped
-// to row B_r - 1 and masked out of the softmax) and issued before the first
-// matrix op, in the order Q, K, V, S, so the S stream -- two thirds of the
-// bytes -- is in flight while the softmax part is computed.  No LDS and no
-// barriers: waves only share L1/L2 lines of Q and K.
+// Q, K and V are staged once per workgroup in LDS (row-major, 16-byte pad):
+// every wave loads an equal slice with 16-byte coalesced loads, so each byte
+// is fetched once.  Matrix-core operands of Q and K are then one 16-byte LDS
+// read each; V^T operands use the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16), which hands each lane four consecutive rows of one
+// column.  Rows past B_r are clamped to row B_r - 1 (masked out of the
+// softmax), so every global load is unconditional; they are issued in the
+// order Q/K/V slices, then the wave's S tile, and the scheduler is fenced so
+// the S stream -- two thirds of the bytes -- is in flight while the softmax
+// part is computed.
 //
 // Value-column permutation: the A-operand row m of tile ct maps to column
 //   c(m) = 32 ct + 16 * ((m / 4) % 2) + 4 * (m / 8) + m % 4,
 // chosen so that accumulator register r of lane half hh holds column
 // 32 ct + 16 hh + r: each lane stores 16 contiguous output columns (32 bytes).
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+
+// Four consecutive rows of one column per lane: within each 16-lane group,
+// lane j' supplies the address of 4 bf16 at (row0 + j'/4, col(j'%4)) and lane
+// i receives element i%4 of the rows supplied by lanes 4k + i/4, k = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
 template <int D, int NQ>
 __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;              // k-steps over the head dimension
     constexpr int NC = D / 32;              // value-column tiles
     constexpr int NKT = NQ;                 // key tiles (keys = queries = block rows)
+    constexpr int NT = NQ * NC * kWave;     // threads
+    constexpr int R = NQ * 32;              // staged rows
+    constexpr int P = D + 8;                // LDS row pitch (bf16)
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int CPT = R * CPR / NT;       // chunks per thread per tensor
+    static_assert(CPT * NT == R * CPR, "even staging split");
+    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
+
     const int unit = blockIdx.x;
     const int r = unit / a.heads, h = unit % a.heads;
     int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
@@ -51,9 +73,9 @@ __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a
     const int slot = a.slots[r];
     if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
 
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, w = tid / kWave;
     const int qt = w / NC, ct = w % NC;
-    if (qt * 32 >= Br) return;                               // no valid query in this tile
     const int l32 = lane % 32, hh = lane / 32;
     const int64_t rs = (int64_t)a.heads * D;                 // token row stride
     const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
@@ -68,32 +90,15 @@ __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a
     const int last = Br - 1;
     const float sl2 = a.scale * 1.4426950408889634f;         // logits in log2 units
 
-    // ---- issue every load: Q, K, V^T gathers, then S^T
-    const int i = qt * 32 + l32;
-    const uint16_t* qrow = q + (int64_t)(i < Br ? i : last) * rs + 8 * hh;
-    u16x8 qv[KS];
+    // ---- global loads: this thread's Q/K/V chunks, then the wave's S^T tile
+    u32x4 cq[CPT], ck[CPT], cv[CPT];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qv[s] = *reinterpret_cast<const u16x8*>(qrow + 16 * s);
-    u16x8 kv[NKT][KS];
-    u16x8 vop[NKT][2];
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-        const int j = jt * 32 + l32;
-        const uint16_t* krow = k + (int64_t)(j < Br ? j : last) * rs + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kv[jt][s] = *reinterpret_cast<const u16x8*>(krow + 16 * s);
-    }
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-        // key j = jt*32 + 16gp + 8(e/4) + 4hh + e%4 matches L^T accumulator register 8gp + e
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int jj = jt * 32 + 16 * gp + 8 * (e / 4) + 4 * hh + e % 4;
-                vop[jt][gp][e] = v[(int64_t)(jj < Br ? jj : last) * rs + cA];
-            }
-        }
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        const int64_t off = (int64_t)(row < Br ? row : last) * rs + c8;
+        cq[u] = *reinterpret_cast<const u32x4*>(q + off);
+        ck[u] = *reinterpret_cast<const u32x4*>(k + off);
+        cv[u] = *reinterpret_cast<const u32x4*>(v + off);
     }
     f32x4 sraw[KS][2];
     const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
@@ -105,6 +110,21 @@ __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a
     // keep the scheduler from sinking these loads next to their uses: the
     // whole wave's bytes must be in flight before the first wait
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
+        *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
+        *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
+    }
+    __syncthreads();
+    if (qt * 32 >= Br) return;                               // no valid query in this tile
+
+    // ---- Q operand (B of L^T and, ReLU'd, B of S^T phi(Q)^T)
+    const int i = qt * 32 + l32;
+    u16x8 qv[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qv[s] = *reinterpret_cast<const u16x8*>(sq + i * P + 16 * s + 8 * hh);
 
     // ---- L^T = K Q^T per key tile
     f32x16 lt[NKT];
@@ -112,8 +132,10 @@ __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a
     for (int jt = 0; jt < NKT; ++jt) {
         f32x16 acc = {};
         if (jt < nkt) {
+            const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) acc = mfma32(as_bf16x8(kv[jt][s]), as_bf16x8(qv[s]), acc);
+            for (int s = 0; s < KS; ++s)
+                acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)), as_bf16x8(qv[s]), acc);
         }
         lt[jt] = acc;
     }
@@ -143,30 +165,44 @@ __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a
     sum += __shfl_xor(sum, 32);
     const float inv = __builtin_amdgcn_rcpf(sum);
 
-    // ---- O^T = V^T P^T (P as hi + lo bf16)
+    // ---- O^T = V^T P^T (P as hi + lo bf16).  V^T operand of k-step (jt, gp):
+    // keys jt*32 + 16gp + 4hh + {0..3} and the same + 8, matching registers
+    // 8gp .. 8gp+7 of L^T; column of lane i in 16-lane group g is
+    // 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4 with q = i/4 (= cA above).
+    const int g = lane / 16, jl = lane % 16;
+    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
     f32x16 o = {};
 #pragma unroll
     for (int jt = 0; jt < NKT; ++jt) {
         if (jt < nkt) {
 #pragma unroll
             for (int gp = 0; gp < 2; ++gp) {
-                float p[8];
+                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+                u16x8 vop;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = lt[jt][8 * gp + e] * inv;
+                for (int e = 0; e < 4; ++e) {
+                    vop[e] = static_cast<uint16_t>(v0[e]);
+                    vop[4 + e] = static_cast<uint16_t>(v1[e]);
+                }
+                float pp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
                 bf16x8 phi, plo;
-                split_hi_lo(p, phi, plo);
-                o = mfma32(as_bf16x8(vop[jt][gp]), phi, o);
-                o = mfma32(as_bf16x8(vop[jt][gp]), plo, o);
+                split_hi_lo(pp, phi, plo);
+                o = mfma32(as_bf16x8(vop), phi, o);
+                o = mfma32(as_bf16x8(vop), plo, o);
             }
         }
     }
     // ---- O^T += S^T phi(Q)^T (S as hi + lo bf16)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const float sv[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
-                             sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
+        const float sv8[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
+                              sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
         bf16x8 shi, slo;
-        split_hi_lo(sv, shi, slo);
+        split_hi_lo(sv8, shi, slo);
         const bf16x8 pq = as_bf16x8(relu_bf16x8(qv[s]));
         o = mfma32(shi, pq, o);
         o = mfma32(slo, pq, o);

@@ -150,10 +150,10 @@ def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256
     """state[slots[r]] = sum over prompt r of ReLU(k_t)^T v_t (overwrite).
 
     k, v packed [total, H, d]; cu_seqlens int64 [n_req + 1] on the GPU.
-    ``max_len`` (host int) must bound every prompt length; if omitted it is
-    read back from cu_seqlens (a device synchronisation).  ``workspace`` is a
-    GPU uint8 tensor of at least ``hybrid_state_prefill_workspace_bytes``
-    bytes; if omitted one is allocated through torch."""
+    ``max_len`` (host int) is an optional upper bound of the prompt lengths.
+    ``workspace`` is a GPU uint8 tensor of at least
+    ``hybrid_state_prefill_workspace_bytes`` bytes; if omitted one is
+    allocated through torch."""
     total, H, d = k.shape
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k, v must share shape and dtype")
@@ -163,7 +163,7 @@ def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256
     if slots.shape != (n_req,):
         raise ValueError("slots must be [n_req]")
     if max_len is None:
-        max_len = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if n_req > 0 else 0
+        max_len = 0     # only an upper bound; the kernels do not need it
     need = hybrid_state_prefill_workspace_bytes(n_req, H, d, total, max_len, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)

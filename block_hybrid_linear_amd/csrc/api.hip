@@ -33,23 +33,9 @@ ha_status hip_status(hipError_t e, const char* what)
 bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool known_dtype(ha_dtype t) { return t == HA_F32 || t == HA_BF16; }
 
-// Prompt tokens per prefill workgroup: whole chunks, about 4096 tokens, so a
-// group's fp32 partial state (d*d*4 bytes) stays a few percent of the bf16
-// K/V bytes it summarises.
-constexpr int64_t kGroupTargetTokens = 4096;
-
-int64_t group_tokens(int32_t chunk)
-{
-    const int64_t per = kGroupTargetTokens / chunk;
-    return (int64_t)chunk * (per > 1 ? per : 1);
-}
-
-int64_t prefill_groups(int64_t max_len, int32_t chunk)
-{
-    if (max_len <= 0) return 0;
-    const int64_t g = group_tokens(chunk);
-    return (max_len + g - 1) / g;
-}
+// Prefill workspace: the plan (n_req + 2 int64, padded to 256 bytes), then
+// one fp32 partial state per (slice, unit) slot.
+size_t plan_bytes(int32_t n_req) { return ((size_t)(n_req + 2) * sizeof(int64_t) + 255) / 256 * 256; }
 
 // Checks shared by step and commit.  Returns HA_OK or the failure status.
 ha_status check_block_call(const char* fn, int32_t n_req, int32_t n_slots, int32_t heads,
@@ -121,9 +107,10 @@ size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads, int32_
                                             int64_t total_tokens, int64_t max_len, int32_t chunk)
 {
     (void)total_tokens;
-    if (n_req <= 0 || heads <= 0 || d <= 0 || chunk <= 0 || max_len <= 0) return 0;
-    return (size_t)n_req * (size_t)prefill_groups(max_len, chunk) * (size_t)heads * (size_t)d *
-           (size_t)d * sizeof(float);
+    (void)max_len;
+    if (n_req <= 0 || heads <= 0 || d <= 0 || chunk <= 0) return 0;
+    return plan_bytes(n_req) +
+           ((size_t)ha::prefill_slices(d) + (size_t)n_req * (size_t)heads) * (size_t)d * (size_t)d * sizeof(float);
 }
 
 ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_seqlens,
@@ -143,43 +130,32 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
     if (!supported_d(d)) return fail(HA_ERR_UNSUPPORTED, "%s: head dim d=%d not in {16, 32, 64, 128}", fn, d);
     if (n_req > 65535 || heads > 65535)
         return fail(HA_ERR_INVALID_ARG, "%s: n_req and heads must be <= 65535", fn);
-    const int64_t groups = prefill_groups(max_len, chunk);
-    if (groups > 0x7fffffffLL) return fail(HA_ERR_INVALID_ARG, "%s: max_len too large", fn);
     if (n_req == 0) return HA_OK;
     if (!cu_seqlens || !state || !slots)
         return fail(HA_ERR_INVALID_ARG, "%s: cu_seqlens, state and slots must be non-NULL", fn);
     if (total_tokens > 0 && (!k || !v))
         return fail(HA_ERR_INVALID_ARG, "%s: k and v must be non-NULL when total_tokens > 0", fn);
     const size_t need = hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk);
-    if (workspace_bytes < need || (need > 0 && !workspace))
+    if (workspace_bytes < need || !workspace)
         return fail(HA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
                     workspace_bytes, workspace ? "" : ", NULL");
     ha::PhiKVArgs a{};
     a.k = k;
     a.v = v;
+    a.state = state;
+    a.slots = slots;
     a.cu = cu_seqlens;
-    a.partial = static_cast<float*>(workspace);
+    a.plan = static_cast<int64_t*>(workspace);
+    a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_bytes(n_req));
     a.total_tokens = total_tokens;
-    a.group_tokens = group_tokens(chunk);
-    a.groups = (int32_t)groups;
+    a.chunk = chunk;
+    a.slices = ha::prefill_slices(d);
     a.n_req = n_req;
     a.n_slots = n_slots;
     a.heads = heads;
     a.d = d;
     a.dtype_bf16 = dtype == HA_BF16;
-    ha::ReduceArgs ra{};
-    ra.partial = a.partial;
-    ra.cu = cu_seqlens;
-    ra.state = state;
-    ra.slots = slots;
-    ra.total_tokens = total_tokens;
-    ra.group_tokens = a.group_tokens;
-    ra.groups = a.groups;
-    ra.n_req = n_req;
-    ra.n_slots = n_slots;
-    ra.heads = heads;
-    ra.d = d;
-    return hip_status(ha::launch_prefill(a, ra, static_cast<hipStream_t>(stream)), fn);
+    return hip_status(ha::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

@@ -19,39 +19,35 @@ struct StepArgs {
     bool dtype_bf16;
 };
 
-// phi(K)^T V over token rows, shared by the block commit and prompt prefill.
+// ReLU(K)^T V over token rows, shared by the block commit and prompt prefill.
 //   commit : rows of request r are r*blk + [0, B_r); the result is added to
 //            the state slot in place.
-//   prefill: rows of request r are cu[r] + [g*G, min((g+1)*G, L_r)) for group
-//            g; the result is written as a partial state into the workspace.
+//   prefill: the (request, head, chunk) list is split into `slices` equal
+//            ranges; each slice workgroup writes partial states into the
+//            workspace and a reduction sums them per (request, head).
 struct PhiKVArgs {
     const void* k;
     const void* v;
-    float* state;               // commit: state store
-    const int32_t* slots;       // commit
+    float* state;               // state store (commit: updated; prefill: overwritten)
+    const int32_t* slots;
     const int32_t* blk_lens;    // commit (may be NULL)
-    const int64_t* cu;          // prefill
-    float* partial;             // prefill: [n_req][groups][heads][d][d]
+    const int64_t* cu;          // prefill: [n_req + 1]
+    int64_t* plan;              // prefill workspace: [n_req + 2]
+    float* partial;             // prefill workspace: [slices + n_req * heads][d][d]
     int64_t total_tokens;       // prefill
-    int64_t group_tokens;       // prefill: G
-    int32_t groups;             // prefill: groups per request
+    int32_t chunk;              // prefill
+    int32_t slices;             // prefill
     int32_t n_req, n_slots, heads, blk, d;
     bool dtype_bf16;
 };
 
-struct ReduceArgs {
-    const float* partial;
-    const int64_t* cu;
-    float* state;
-    const int32_t* slots;
-    int64_t total_tokens;
-    int64_t group_tokens;
-    int32_t groups;
-    int32_t n_req, n_slots, heads, d;
-};
+// Number of prefill slice workgroups for head dim d (two per compute unit of
+// an MI355X for the 4-wave kernels).  Fixed per d, so results do not depend
+// on the device.
+inline int prefill_slices(int d) { return d == 32 ? 2048 : 512; }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PhiKVArgs& a, const ReduceArgs& r, hipStream_t stream);
+hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream);
 
 }  // namespace ha

@@ -9,21 +9,36 @@
 namespace ha {
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core reduction of ReLU(K)^T V over a token range.
+// bf16 matrix-core reduction of ReLU(K)^T V over a range of token rows.
 //
 //   dS^T[c][f] = sum_j V[j][c] * ReLU(K[j][f])      (A = V^T, B = ReLU(K), k = token)
 //
 // The reduction runs over tokens, which are the strided dimension of the
 // token-major inputs, so K and V go through LDS transposed: each thread loads
-// an 8-token x 8-column block with eight coalesced 16-byte loads (a wave
-// instruction covers whole 256-byte rows), transposes it in registers and
-// writes eight 16-byte rows of K^T / V^T.  Matrix-core operands are then one
-// 16-byte LDS read each.  Stages of T tokens are double-buffered: the next
-// stage's global loads are in flight while the current one is multiplied,
-// with one barrier per stage.
+// an 8-token x 8-column block with eight 16-byte loads, transposes it in
+// registers and writes eight 16-byte rows of K^T / V^T.  Matrix-core operands
+// are then one 16-byte LDS read each.
 //
-// Output tiles are 32 x 32; wave w owns value-row tile ct and the feature
-// tiles listed by tile_of().  Accumulator register r of lane l holds
+// Lane mapping and LDS layout (d = 128): the column group varies fastest
+// across lanes, so a wave's load instruction reads four whole 256-byte head
+// rows -- measurably faster from HBM than 128-byte pieces.  The 16 lanes of
+// one transposed write then target rows 8 apart, which with the 16-byte row
+// padding would share two bank groups; LDS rows are therefore permuted
+// within each 16-row block, row c -> (c & ~15) | ((c + c / 16) & 15), which
+// spreads those 16 rows over all banks and keeps the 16 consecutive rows of
+// an operand read distinct too.  Operand addresses stay affine in the
+// k-step, so they fold into instruction offsets.  (d = 64, 32: the token
+// group varies fastest, which is conflict-free without a permutation.)
+//
+// Stages of T tokens are double-buffered in LDS; PF stages of global loads
+// are in flight while a stage is multiplied (prefill: 3, commit: 1), one
+// barrier per stage.  In the prefill loop every stage issues its loads
+// unconditionally (a stage past the end re-reads the last valid rows, which
+// hit in L2, and is zeroed when stored), so the number of loads in flight is
+// the same on every path.
+//
+// Output tiles are 32 x 32; wave w owns value-row tile ct = (w*TPW)/NT and
+// TPW feature tiles.  Accumulator register r of lane l holds
 // c = 32 ct + 8 (r/4) + 4 (l/32) + r%4 and f = 32 ft + l%32, so every register
 // of a wave is two 128-byte runs of one state row: coalesced read-modify-write.
 // ---------------------------------------------------------------------------
@@ -32,66 +47,56 @@ template <> struct PhiKVShape<128> { static constexpr int NW = 4, T = 64; };
 template <> struct PhiKVShape<64> { static constexpr int NW = 4, T = 128; };
 template <> struct PhiKVShape<32> { static constexpr int NW = 1, T = 64; };
 
-template <int D, bool kCommit>
-__global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void phikv_bf16_mfma(PhiKVArgs a)
-{
-    constexpr int NW = PhiKVShape<D>::NW, T = PhiKVShape<D>::T;
-    constexpr int NT = D / 32;                   // tiles per dimension
-    constexpr int TPW = NT * NT / NW;            // tiles per wave
-    constexpr int PITCH = T + 8;                 // LDS row pitch in bf16 (16 B pad)
-    constexpr int CG = D / 8;                    // 8-column groups per token row
+template <int D>
+struct PhiKVTile {
+    static constexpr int NW = PhiKVShape<D>::NW, T = PhiKVShape<D>::T;
+    static constexpr int NT = D / 32;                   // tiles per dimension
+    static constexpr int TPW = NT * NT / NW;            // tiles per wave
+    static constexpr int PITCH = T + 8;                 // LDS row pitch in bf16 (16 B pad)
+    static constexpr int CG = D / 8;                    // 8-column groups per token row
     static_assert(2 * (T / 8) * CG == NW * kWave, "one 8x8 block per thread per stage");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][D * PITCH];  // [buf][K^T, V^T]
+    static constexpr bool kColsFast = D == 128;         // lane mapping, see above
+    typedef uint16_t Lds[2][2][D * PITCH];              // [buf][K^T, V^T]
+    __device__ __forceinline__ static int row(int c) { return kColsFast ? (c & ~15) | ((c + (c >> 4)) & 15) : c; }
+    // element offset of token group g (8 tokens) of logical LDS row c
+    __device__ __forceinline__ static int slot(int c, int g) { return row(c) * PITCH + 8 * g; }
+};
 
-    // ---- token range of this workgroup
-    int r, h, slot = 0;
-    int64_t row0, nrows;
-    if (kCommit) {
-        r = blockIdx.x / a.heads;
-        h = blockIdx.x % a.heads;
-        int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
-        Br = Br > a.blk ? a.blk : Br;
-        slot = a.slots[r];
-        if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;
-        row0 = (int64_t)r * a.blk;
-        nrows = Br;
-    } else {
-        const int g = blockIdx.x;
-        h = blockIdx.y;
-        r = blockIdx.z;
-        const int64_t s0 = a.cu[r], s1 = a.cu[r + 1];
-        if (s0 < 0 || s1 > a.total_tokens || s1 < s0) return;     // malformed: treated as empty
-        row0 = s0 + (int64_t)g * a.group_tokens;
-        const int64_t end = (s1 - row0 < a.group_tokens) ? s1 : row0 + a.group_tokens;
-        if (row0 >= end) return;                                   // beyond this prompt
-        nrows = end - row0;
-    }
-    const int64_t rs = (int64_t)a.heads * D;
-    const uint16_t* kb = static_cast<const uint16_t*>(a.k) + row0 * rs + (int64_t)h * D;
-    const uint16_t* vb = static_cast<const uint16_t*>(a.v) + row0 * rs + (int64_t)h * D;
-
+// Adds ReLU(K)^T V over rows [0, nrows) of (kb, vb) (rows rs elements apart)
+// into acc.  nrows >= 1.  Every thread of the workgroup must call it.
+template <int D, int PF>
+__device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint16_t* vb, int64_t rs,
+                                                 int64_t nrows, typename PhiKVTile<D>::Lds& lds,
+                                                 f32x16 (&acc)[PhiKVTile<D>::TPW])
+{
+    using P = PhiKVTile<D>;
+    constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG;
     const int tid = threadIdx.x;
     const int lane = tid % kWave, w = tid / kWave;
     const int l32 = lane % 32, hh = lane / 32;
 
-    // ---- this thread's 8x8 staging block: tensor (K or V), token group, column group
+    // this thread's 8x8 staging block: tensor (K or V), token group, column group
     const int blocks_per_tensor = (T / 8) * CG;
     const int tensor = tid / blocks_per_tensor;          // 0 = K, 1 = V
     const int bidx = tid % blocks_per_tensor;
-    const int tg = bidx / CG, cg = bidx % CG;
-    const uint16_t* src = (tensor == 0 ? kb : vb) + (int64_t)(tg * 8) * rs + cg * 8;
+    const int tg = P::kColsFast ? bidx / CG : bidx % (T / 8);
+    const int cg = P::kColsFast ? bidx % CG : bidx / (T / 8);
+    const uint16_t* src = (tensor == 0 ? kb : vb) + cg * 8;
 
     auto load_stage = [&](int64_t t0, u32x4 (&x)[8]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int64_t t = t0 + tg * 8 + e;
-            x[e] = u32x4{0, 0, 0, 0};
-            if (t < nrows) x[e] = *reinterpret_cast<const u32x4*>(src + t0 * rs + (int64_t)e * rs);
+            const int64_t tc = t < nrows ? t : nrows - 1;   // unconditional load; zeroed at store
+            x[e] = *reinterpret_cast<const u32x4*>(src + tc * rs);
         }
     };
-    // transpose the 8x8 bf16 block and write eight 16-byte rows (one per column)
-    auto store_stage = [&](int buf, const u32x4 (&x)[8]) {
-        uint16_t* dst = &lds[buf][tensor][(cg * 8) * PITCH + tg * 8];
+    // zero rows past the range, transpose the 8x8 bf16 block, write 8 rows
+    auto store_stage = [&](int buf, int64_t t0, const u32x4 (&xin)[8]) {
+        u32x4 x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (t0 + tg * 8 + e < nrows) ? xin[e] : u32x4{0, 0, 0, 0};
+        uint16_t* dst = lds[buf][tensor];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             u32x4 y;
@@ -100,176 +105,430 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void phikv_bf16_mfma(Phi
                 const uint32_t lo = x[2 * p][c / 2], hi = x[2 * p + 1][c / 2];
                 y[p] = (c % 2 == 0) ? ((lo & 0xffffu) | (hi << 16)) : ((lo >> 16) | (hi & 0xffff0000u));
             }
-            *reinterpret_cast<u32x4*>(dst + c * PITCH) = y;
+            *reinterpret_cast<u32x4*>(dst + P::slot(cg * 8 + c, tg)) = y;
         }
     };
-
-    f32x16 acc[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
-
-    const int nstages = (int)((nrows + T - 1) / T);
-    u32x4 x[8];
-    load_stage(0, x);
-
-    // commit: the state tiles are read while the first stage is in flight
-    float sold[TPW][16];
-    float* st = nullptr;
-    if (kCommit) {
-        st = a.state + ((int64_t)slot * a.heads + h) * D * D;
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int t = w * TPW + u, ct = t / NT, ft = t % NT;
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int c = ct * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-                sold[u][rr] = st[(int64_t)c * D + ft * 32 + l32];
-            }
-        }
-    }
-
-    for (int sg = 0; sg < nstages; ++sg) {
-        const int buf = sg & 1;
-        store_stage(buf, x);
-        __syncthreads();
-        if (sg + 1 < nstages) load_stage((int64_t)(sg + 1) * T, x);
+    auto mma_stage = [&](int buf) {
         const uint16_t* kt = lds[buf][0];
         const uint16_t* vt = lds[buf][1];
 #pragma unroll
         for (int s = 0; s < T / 16; ++s) {
-            const int j = 16 * s + 8 * hh;
+            const int g = 2 * s + hh;                       // token group of this lane's 8 tokens
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
                 const int t = w * TPW + u, ct = t / NT, ft = t % NT;
-                const u16x8 av = *reinterpret_cast<const u16x8*>(vt + (ct * 32 + l32) * PITCH + j);
-                const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + (ft * 32 + l32) * PITCH + j);
+                const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(ct * 32 + l32, g));
+                const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(ft * 32 + l32, g));
                 acc[u] = mfma32(as_bf16x8(av), as_bf16x8(relu_bf16x8(bk)), acc[u]);
             }
         }
-    }
+    };
 
-    // ---- epilogue
-    float* dstp;
-    if (kCommit) {
-        dstp = st;
+    const int nstages = (int)((nrows + T - 1) / T);
+    u32x4 x0[8], x1[8], x2[8];
+    load_stage(0, x0);
+    if (PF > 1) load_stage((int64_t)T, x1);
+    if (PF > 2) load_stage((int64_t)2 * T, x2);
+    auto run_stage = [&](int sg, u32x4 (&x)[8], bool more) {
+        const int buf = sg & 1;
+        // The barrier also guarantees every wave finished reading this buffer
+        // two stages ago, before it is overwritten.
+        store_stage(buf, (int64_t)sg * T, x);
+        __syncthreads();
+        if (more) load_stage((int64_t)(sg + PF) * T, x);
+        mma_stage(buf);
+    };
+    if (PF == 1) {
+        for (int sg = 0; sg < nstages; ++sg) run_stage(sg, x0, sg + 1 < nstages);
     } else {
-        dstp = a.partial + (((int64_t)r * a.groups + blockIdx.x) * a.heads + h) * D * D;
+        for (int sg = 0; sg < nstages; sg += 3) {
+            run_stage(sg, x0, true);
+            run_stage(sg + 1, x1, true);
+            run_stage(sg + 2, x2, true);
+        }
     }
+    __syncthreads();   // LDS is reused by the caller's next range
+}
+
+// Writes (store = true) or reads (store = false) one wave's tiles of a d x d state.
+template <int D>
+__device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[PhiKVTile<D>::TPW], bool store)
+{
+    using P = PhiKVTile<D>;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int l32 = lane % 32, hh = lane / 32;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int t = w * TPW + u, ct = t / NT, ft = t % NT;
+    for (int u = 0; u < P::TPW; ++u) {
+        const int t = w * P::TPW + u, ct = t / P::NT, ft = t % P::NT;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             const int c = ct * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-            float val = acc[u][rr];
-            if (kCommit) val = sold[u][rr] + val;
-            dstp[(int64_t)c * D + ft * 32 + l32] = val;
+            float* p = base + (int64_t)c * D + ft * 32 + l32;
+            if (store) *p = acc[u][rr];
+            else acc[u][rr] = *p;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Plain fp32-arithmetic reduction (fp32 inputs, and bf16 with d = 16): one
-// thread per state element, looping over the token range.
+// Commit: one workgroup per (request, head); the accumulators start from the
+// old state tiles, so the matrix cores add ReLU(K)^T V onto S in fp32.
 // ---------------------------------------------------------------------------
-template <typename T, bool kCommit>
-__global__ __launch_bounds__(256) void phikv_generic(PhiKVArgs a)
+template <int D>
+__global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(PhiKVArgs a)
 {
-    const int D = a.d;
-    int r, h, slot = 0;
-    int64_t row0, nrows;
-    if (kCommit) {
-        r = blockIdx.x / a.heads;
-        h = blockIdx.x % a.heads;
-        int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
-        Br = Br > a.blk ? a.blk : Br;
-        slot = a.slots[r];
-        if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;
-        row0 = (int64_t)r * a.blk;
-        nrows = Br;
-    } else {
-        const int g = blockIdx.x;
-        h = blockIdx.y;
-        r = blockIdx.z;
-        const int64_t s0 = a.cu[r], s1 = a.cu[r + 1];
-        if (s0 < 0 || s1 > a.total_tokens || s1 < s0) return;
-        row0 = s0 + (int64_t)g * a.group_tokens;
-        const int64_t end = (s1 - row0 < a.group_tokens) ? s1 : row0 + a.group_tokens;
-        if (row0 >= end) return;
-        nrows = end - row0;
-    }
+    using P = PhiKVTile<D>;
+    __shared__ __attribute__((aligned(16))) typename P::Lds lds;
+    const int r = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
+    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    Br = Br > a.blk ? a.blk : Br;
+    const int slot = a.slots[r];
+    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;
     const int64_t rs = (int64_t)a.heads * D;
-    const T* kb = static_cast<const T*>(a.k) + row0 * rs + (int64_t)h * D;
-    const T* vb = static_cast<const T*>(a.v) + row0 * rs + (int64_t)h * D;
-    float* dstp = kCommit ? a.state + ((int64_t)slot * a.heads + h) * D * D
-                          : a.partial + (((int64_t)r * a.groups + blockIdx.x) * a.heads + h) * D * D;
-    for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
-        const int c = e / D, f = e % D;
-        float acc = 0.f;
-        for (int64_t t = 0; t < nrows; ++t)
-            acc = fmaf(Elem<T>::load(vb, t * rs + c), relu(Elem<T>::load(kb, t * rs + f)), acc);
-        dstp[e] = kCommit ? dstp[e] + acc : acc;
+    const int64_t off = (int64_t)r * a.blk * rs + (int64_t)h * D;
+    float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
+    f32x16 acc[P::TPW];
+    tiles_io<D>(st, acc, false);
+    phikv_accumulate<D, 1>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
+                           Br, lds, acc);
+    tiles_io<D>(st, acc, true);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill, step 1 (one workgroup): the plan.  Prompt r is cut into
+// nch_r = ceil(L_r / chunk) chunks per head; the (request, head, chunk) list
+// is laid out request by request, head by head.  plan[r] = heads * sum over
+// r' < r of nch_r' (exclusive prefix), plan[n_req] = C (all chunks) and
+// plan[n_req + 1] = chunks per slice ceil(C / slices).  Malformed offsets
+// (outside [0, total_tokens] or decreasing) count as empty prompts.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t chunks_of(const PhiKVArgs& a, int r)
+{
+    const int64_t s0 = a.cu[r], s1 = a.cu[r + 1];
+    if (s0 < 0 || s1 > a.total_tokens || s1 < s0) return 0;
+    return (s1 - s0 + a.chunk - 1) / a.chunk;
+}
+
+__global__ __launch_bounds__(256) void prefill_plan(PhiKVArgs a)
+{
+    __shared__ int64_t part[257];
+    const int n = a.n_req, tid = threadIdx.x;
+    const int per = (n + 255) / 256;
+    const int r0 = tid * per < n ? tid * per : n;
+    const int r1 = (r0 + per < n) ? r0 + per : n;
+    int64_t s = 0;
+    for (int r = r0; r < r1; ++r) s += chunks_of(a, r);
+    part[tid + 1] = s;
+    __syncthreads();
+    if (tid == 0) {
+        part[0] = 0;
+        for (int i = 1; i <= 256; ++i) part[i] += part[i - 1];
+    }
+    __syncthreads();
+    int64_t run = part[tid];
+    for (int r = r0; r < r1; ++r) {
+        a.plan[r] = run * a.heads;
+        run += chunks_of(a, r);
+    }
+    if (tid == 0) {
+        const int64_t C = part[256] * a.heads;
+        a.plan[n] = C;
+        const int64_t S = (C + a.slices - 1) / a.slices;
+        a.plan[n + 1] = S > 0 ? S : 1;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Deterministic reduction of prefill partials: S[slot] = sum_g partial[g] in
-// ascending group order (0 if the prompt is empty).  Each thread owns four
+// Prefill, step 2: slice workgroups.  Workgroup w owns the chunk range
+// [w S, (w+1) S) of the flat list -- the same number of chunks for every
+// workgroup, whatever the prompt lengths -- and writes one fp32 partial state
+// per (request, head) unit u its range touches, into slot w + u.  (Slot
+// w + u is unique: slices and units are both consecutive intervals of the
+// same list, so a later slice never overlaps an earlier unit.)
+// ---------------------------------------------------------------------------
+struct SliceCursor {
+    int r;              // request
+    int64_t c0, c1;     // remaining chunk range of this slice
+};
+
+__device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur)
+{
+    const int64_t C = a.plan[a.n_req], S = a.plan[a.n_req + 1];
+    cur.c0 = (int64_t)blockIdx.x * S;
+    cur.c1 = cur.c0 + S < C ? cur.c0 + S : C;
+    if (cur.c0 >= cur.c1) return false;
+    int lo = 0, hi = a.n_req;                 // last r with plan[r] <= c0
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (a.plan[mid] <= cur.c0) lo = mid;
+        else hi = mid;
+    }
+    cur.r = lo;
+    return true;
+}
+
+// Next piece of the slice: unit (r, h), token rows [t0, t1) of prompt r.
+__device__ __forceinline__ void slice_piece(const PhiKVArgs& a, SliceCursor& cur, int& h, int64_t& t0, int64_t& t1)
+{
+    while (a.plan[cur.r + 1] <= cur.c0) ++cur.r;   // skip finished and empty prompts
+    const int64_t nch = (a.plan[cur.r + 1] - a.plan[cur.r]) / a.heads;
+    const int64_t local = cur.c0 - a.plan[cur.r];
+    h = (int)(local / nch);
+    const int64_t k0 = local % nch;
+    const int64_t k1 = (k0 + (cur.c1 - cur.c0) < nch) ? k0 + (cur.c1 - cur.c0) : nch;
+    const int64_t L = a.cu[cur.r + 1] - a.cu[cur.r];
+    t0 = k0 * a.chunk;
+    t1 = k1 * a.chunk < L ? k1 * a.chunk : L;
+    cur.c0 += k1 - k0;
+}
+
+// A slice is processed as one stream of T-token stages; a stage never spans
+// two (request, head) units.  Cursor state is uniform across the workgroup.
+struct StageCursor {
+    SliceCursor sl;     // chunk position of the next piece
+    int r, h;           // unit of the current piece
+    int64_t t, t1;      // current stage's first row and the piece's end (rows of prompt r)
+    bool live;
+};
+
+__device__ __forceinline__ void stage_next_piece(const PhiKVArgs& a, StageCursor& s)
+{
+    s.live = s.sl.c0 < s.sl.c1;
+    if (!s.live) return;
+    slice_piece(a, s.sl, s.h, s.t, s.t1);
+    s.r = s.sl.r;
+}
+
+__device__ __forceinline__ void stage_advance(const PhiKVArgs& a, StageCursor& s, int T)
+{
+    if (!s.live) return;
+    s.t += T;
+    if (s.t >= s.t1) stage_next_piece(a, s);
+}
+
+template <int D>
+__global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_bf16_mfma(PhiKVArgs a)
+{
+    using P = PhiKVTile<D>;
+    constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG, PF = 3;
+    __shared__ __attribute__((aligned(16))) typename P::Lds lds;
+    StageCursor cp, ld;                        // compute and load cursors
+    if (!slice_begin(a, cp.sl)) return;
+    stage_next_piece(a, cp);
+    ld = cp;
+
+    const int64_t rs = (int64_t)a.heads * D;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k);
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v);
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, w = tid / kWave;
+    const int l32 = lane % 32, hh = lane / 32;
+    const int blocks_per_tensor = (T / 8) * CG;
+    const int tensor = tid / blocks_per_tensor;          // 0 = K, 1 = V
+    const int bidx = tid % blocks_per_tensor;
+    const int tg = P::kColsFast ? bidx / CG : bidx % (T / 8);
+    const int cg = P::kColsFast ? bidx % CG : bidx / (T / 8);
+    const uint16_t* tbase = (tensor == 0 ? kbase : vbase) + cg * 8;
+
+    // loads of the stage under the load cursor (rows past the piece re-read its
+    // last row; a finished cursor re-reads the last row it had)
+    auto load_stage = [&](u32x4 (&x)[8]) {
+        const uint16_t* src = tbase + a.cu[ld.r] * rs + (int64_t)ld.h * D;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t t = ld.t + tg * 8 + e;
+            const int64_t tc = t < ld.t1 ? t : ld.t1 - 1;
+            x[e] = *reinterpret_cast<const u32x4*>(src + tc * rs);
+        }
+        stage_advance(a, ld, T);
+    };
+    // The stage buffer is reloaded right after it is stored, so rows past the
+    // piece are zeroed in place (no second copy of the stage in registers).
+    auto store_stage = [&](int buf, int64_t valid, u32x4 (&x)[8]) {
+        if (valid < T) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (tg * 8 + e >= valid) x[e] = u32x4{0, 0, 0, 0};
+        }
+        uint16_t* dst = lds[buf][tensor];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x4 y;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t lo = x[2 * p][c / 2], hi = x[2 * p + 1][c / 2];
+                y[p] = (c % 2 == 0) ? ((lo & 0xffffu) | (hi << 16)) : ((lo >> 16) | (hi & 0xffff0000u));
+            }
+            *reinterpret_cast<u32x4*>(dst + P::slot(cg * 8 + c, tg)) = y;
+        }
+    };
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+    auto mma_stage = [&](int buf) {
+        const uint16_t* kt = lds[buf][0];
+        const uint16_t* vt = lds[buf][1];
+#pragma unroll
+        for (int s = 0; s < T / 16; ++s) {
+            const int g = 2 * s + hh;
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int t = w * TPW + u, ct = t / NT, ft = t % NT;
+                const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(ct * 32 + l32, g));
+                const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(ft * 32 + l32, g));
+                acc[u] = mfma32(as_bf16x8(av), as_bf16x8(relu_bf16x8(bk)), acc[u]);
+            }
+        }
+    };
+
+    u32x4 x0[8], x1[8], x2[8];
+    load_stage(x0);
+    load_stage(x1);
+    load_stage(x2);
+    int sg = 0;
+    // One stage: store the compute cursor's stage, issue the loads PF stages
+    // ahead, multiply, and flush the unit's partial state when its piece ends.
+    auto run_stage = [&](u32x4 (&x)[8]) {
+        if (!cp.live) return;                  // uniform
+        const int buf = sg & 1;
+        store_stage(buf, cp.t1 - cp.t, x);
+        __syncthreads();
+        load_stage(x);
+        mma_stage(buf);
+        ++sg;
+        if (cp.t + T >= cp.t1) {
+            const int64_t unit = (int64_t)cp.r * a.heads + cp.h;
+            tiles_io<D>(a.partial + ((int64_t)blockIdx.x + unit) * D * D, acc, true);
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+        }
+        stage_advance(a, cp, T);
+    };
+    while (cp.live) {
+        run_stage(x0);
+        run_stage(x1);
+        run_stage(x2);
+    }
+}
+
+// Plain fp32-arithmetic version of the slice workgroup (fp32 inputs, and bf16
+// with d = 16): one thread per state element, looping over the piece's rows.
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
+{
+    SliceCursor cur;
+    if (!slice_begin(a, cur)) return;
+    const int D = a.d;
+    const int64_t rs = (int64_t)a.heads * D;
+    while (cur.c0 < cur.c1) {
+        int h;
+        int64_t t0, t1;
+        slice_piece(a, cur, h, t0, t1);
+        const T* kb = static_cast<const T*>(a.k) + (a.cu[cur.r] + t0) * rs + (int64_t)h * D;
+        const T* vb = static_cast<const T*>(a.v) + (a.cu[cur.r] + t0) * rs + (int64_t)h * D;
+        float* dst = a.partial + ((int64_t)blockIdx.x + (int64_t)cur.r * a.heads + h) * D * D;
+        for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
+            const int c = e / D, f = e % D;
+            float acc = 0.f;
+            for (int64_t t = 0; t < t1 - t0; ++t)
+                acc = fmaf(Elem<T>::load(vb, t * rs + c), relu(Elem<T>::load(kb, t * rs + f)), acc);
+            dst[e] = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill, step 3: S[slot] = sum of the unit's partials in ascending slice
+// order (deterministic), 0 for an empty prompt.  Each thread owns four
 // consecutive floats of one (request, head) state.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a)
+__global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
 {
     const int h = blockIdx.y, r = blockIdx.z;
     const int slot = a.slots[r];
     if (slot < 0 || slot >= a.n_slots) return;
-    const int64_t n4 = (int64_t)a.d * a.d / 4;
-    const int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e4 >= n4) return;
-    const int64_t s0 = a.cu[r], s1 = a.cu[r + 1];
-    int64_t ng = 0;
-    if (s0 >= 0 && s1 <= a.total_tokens && s1 > s0) ng = (s1 - s0 + a.group_tokens - 1) / a.group_tokens;
-    if (ng > a.groups) ng = a.groups;
     const int64_t dd = (int64_t)a.d * a.d;
+    const int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e4 >= dd / 4) return;
+    const int64_t S = a.plan[a.n_req + 1];
+    const int64_t nch = (a.plan[r + 1] - a.plan[r]) / a.heads;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t g = 0; g < ng; ++g) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(a.partial + ((r * (int64_t)a.groups + g) * a.heads + h) * dd);
-        sum += p[e4];
+    if (nch > 0) {
+        const int64_t cfirst = a.plan[r] + h * nch, clast = cfirst + nch - 1;
+        const int64_t unit = (int64_t)r * a.heads + h;
+        for (int64_t w = cfirst / S; w <= clast / S; ++w)
+            sum += reinterpret_cast<const f32x4*>(a.partial + (w + unit) * dd)[e4];
     }
     reinterpret_cast<f32x4*>(a.state + ((int64_t)slot * a.heads + h) * dd)[e4] = sum;
 }
 
 // ---------------------------------------------------------------------------
-template <bool kCommit>
-static void launch_phikv(const PhiKVArgs& a, dim3 grid, hipStream_t stream)
+// Plain fp32-arithmetic commit (fp32 inputs, and bf16 with d = 16): one
+// thread per state element, looping over the block's rows.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void commit_generic(PhiKVArgs a)
 {
-    if (a.dtype_bf16 && a.d >= 32) {
-        switch (a.d) {
-        case 32: phikv_bf16_mfma<32, kCommit><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a); break;
-        case 64: phikv_bf16_mfma<64, kCommit><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a); break;
-        default: phikv_bf16_mfma<128, kCommit><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a); break;
-        }
-    } else if (a.dtype_bf16) {
-        phikv_generic<uint16_t, kCommit><<<grid, 256, 0, stream>>>(a);
-    } else {
-        phikv_generic<float, kCommit><<<grid, 256, 0, stream>>>(a);
+    const int D = a.d;
+    const int r = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
+    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    Br = Br > a.blk ? a.blk : Br;
+    const int slot = a.slots[r];
+    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;
+    const int64_t rs = (int64_t)a.heads * D;
+    const T* kb = static_cast<const T*>(a.k) + (int64_t)r * a.blk * rs + (int64_t)h * D;
+    const T* vb = static_cast<const T*>(a.v) + (int64_t)r * a.blk * rs + (int64_t)h * D;
+    float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
+    for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
+        const int c = e / D, f = e % D;
+        float acc = 0.f;
+        for (int j = 0; j < Br; ++j)
+            acc = fmaf(Elem<T>::load(vb, j * rs + c), relu(Elem<T>::load(kb, j * rs + f)), acc);
+        st[e] += acc;
     }
 }
 
+// ---------------------------------------------------------------------------
 hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream)
 {
-    launch_phikv<true>(a, dim3(a.n_req * a.heads), stream);
+    const dim3 grid(a.n_req * a.heads);
+    if (a.dtype_bf16 && a.d >= 32) {
+        switch (a.d) {
+        case 32: commit_bf16_mfma<32><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a); break;
+        case 64: commit_bf16_mfma<64><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a); break;
+        default: commit_bf16_mfma<128><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a); break;
+        }
+    } else if (a.dtype_bf16) {
+        commit_generic<uint16_t><<<grid, 256, 0, stream>>>(a);
+    } else {
+        commit_generic<float><<<grid, 256, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PhiKVArgs& a, const ReduceArgs& ra, hipStream_t stream)
+hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream)
 {
-    if (a.groups > 0) {
-        launch_phikv<false>(a, dim3(a.groups, a.heads, a.n_req), stream);
-        const hipError_t e = hipGetLastError();
+    prefill_plan<<<1, 256, 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.total_tokens > 0) {
+        const dim3 grid(a.slices);
+        if (a.dtype_bf16 && a.d >= 32) {
+            switch (a.d) {
+            case 32: prefill_slices_bf16_mfma<32><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a); break;
+            case 64: prefill_slices_bf16_mfma<64><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a); break;
+            default: prefill_slices_bf16_mfma<128><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a); break;
+            }
+        } else if (a.dtype_bf16) {
+            prefill_slices_generic<uint16_t><<<grid, 256, 0, stream>>>(a);
+        } else {
+            prefill_slices_generic<float><<<grid, 256, 0, stream>>>(a);
+        }
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t n4 = (int64_t)ra.d * ra.d / 4;
-    prefill_reduce<<<dim3((unsigned)((n4 + 255) / 256), ra.heads, ra.n_req), 256, 0, stream>>>(ra);
+    const int64_t n4 = (int64_t)a.d * a.d / 4;
+    prefill_reduce<<<dim3((unsigned)((n4 + 255) / 256), a.heads, a.n_req), 256, 0, stream>>>(a);
     return hipGetLastError();
 }
 

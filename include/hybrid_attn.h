@@ -125,17 +125,23 @@ ha_status hybrid_state_commit(const void* k, const void* v, float* state,
  * request with an empty prompt gets S = 0, which is also the reset path.
  *
  * cu_seqlens: device int64[n_req + 1], non-decreasing, cu_seqlens[0] = 0,
- *   cu_seqlens[n_req] = total_tokens.  Requests whose rows fall outside
- *   [0, total_tokens) are treated as empty.
- * total_tokens, max_len: HOST scalars; max_len must be >= every prompt
- *   length (tokens of a longer prompt past max_len are not folded).
- * chunk: the prompt is cut into chunks of `chunk` tokens; workgroups reduce
- *   whole chunks into fp32 partial states kept in `workspace`, which a second
- *   kernel sums per (request, head) in a fixed order (deterministic).  The
- *   result does not depend on chunk beyond fp32 rounding.
+ *   cu_seqlens[n_req] = total_tokens.  A request whose rows fall outside
+ *   [0, total_tokens] (or run backwards) is treated as an empty prompt.
+ * total_tokens: HOST scalar, rows of k and v.
+ * max_len: HOST scalar >= 0, an upper bound of the prompt lengths; the
+ *   current kernels do not need it (kept for ABI stability).
+ * chunk: prompts are cut into chunks of `chunk` tokens; the list of all
+ *   (request, head, chunk) triples is split into a fixed number of equal
+ *   ranges, one per workgroup, so the work is balanced whatever the prompt
+ *   lengths.  Each workgroup writes one fp32 partial state per (request,
+ *   head) its range touches into `workspace`; a second kernel sums the
+ *   partials of each (request, head) in a fixed order (deterministic: the
+ *   same inputs give bit-identical states).  The result does not depend on
+ *   chunk beyond fp32 rounding.
  * workspace: device scratch of at least
- *   hybrid_state_prefill_workspace_bytes(...) bytes (NULL allowed if that is
- *   0); its contents on entry do not matter.
+ *   hybrid_state_prefill_workspace_bytes(...) bytes (non-NULL when
+ *   n_req > 0); its contents on entry do not matter.  Calls sharing one
+ *   workspace must be ordered on one stream.
  */
 ha_status hybrid_state_prefill(const void* k, const void* v,
                                const int64_t* cu_seqlens,

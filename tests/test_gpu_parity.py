@@ -266,3 +266,40 @@ def test_state_roundtrip_layout():
     torch.cuda.synchronize()
     ref = oracle.step(q, k, np.zeros(v.shape), state_to_oracle(state), scale=d ** -0.5)
     assert_parity(out, ref, torch.bfloat16, "layout")
+
+
+def test_prefill_many_ragged_requests():
+    """Hundreds of prompts, many shorter than a chunk, some empty: the
+    balanced split crosses request and head boundaries inside workgroups."""
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(0, 700, size=300)]
+    lengths[5] = 0
+    lengths[6] = 1
+    lengths[7] = 5000
+    state, ref, _, _ = prefill_case(lengths, 2, 64, torch.bfloat16, 13000, chunk=64)
+    assert_parity(state_to_oracle(state), ref, torch.bfloat16, "many prompts")
+
+
+def test_prefill_malformed_offsets_are_empty():
+    """Offsets running backwards or past total_tokens count as empty prompts
+    (S = 0) instead of reading out of bounds."""
+    H, d, total = 2, 128, 300
+    k, v = (synth.normal((total, H, d), 13500 + t) for t in range(2))
+    cu = torch.tensor([0, 100, 50, 300, 400], dtype=torch.int64)
+    state = torch.full((4, H, d, d), 5.0, device=DEV)
+    slots = torch.arange(4, dtype=torch.int32, device=DEV)
+    bh.hybrid_state_prefill(k.to(DEV), v.to(DEV), cu.to(DEV), state, slots)
+    torch.cuda.synchronize()
+    got = state_to_oracle(state)
+    assert np.all(got[1] == 0.0) and np.all(got[3] == 0.0)
+    ref = oracle.prefill(k[:100], v[:100], [0, 100])
+    assert_parity(got[:1], ref, torch.bfloat16, "valid prompt 0")
+    ref2 = oracle.prefill(k[50:300], v[50:300], [0, 250])
+    assert_parity(got[2:3], ref2, torch.bfloat16, "valid prompt 2")
+
+
+def test_prefill_deterministic():
+    lengths = [20000, 3000, 17]
+    a, _, _, _ = prefill_case(lengths, 4, 128, torch.bfloat16, 14000)
+    b, _, _, _ = prefill_case(lengths, 4, 128, torch.bfloat16, 14000)
+    assert torch.equal(a, b)

@@ -224,7 +224,19 @@ def main():
     ap.add_argument("--workload", default=PREFILL_DECODE.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (5 times): the known-size kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        n = 1 << 28                                   # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
+        x = torch.ones(n, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 5 copies of 1 GiB")
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU only "
               "(every (request, head) unit is independent, see the sharding notes)", file=sys.stderr)

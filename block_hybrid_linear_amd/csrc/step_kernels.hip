@@ -10,8 +10,9 @@ namespace ha {
 // ---------------------------------------------------------------------------
 // bf16 matrix-core step, head dim D in {32, 64, 128}, blk <= 32 * NQ.
 //
-// One workgroup per (request, head) with NQ x D/32 waves; wave (qt, ct) owns
-// query rows [32 qt, 32 qt + 32) and value columns [32 ct, 32 ct + 32).
+// One workgroup per (request, head) with D/32 waves; wave ct owns value
+// columns [32 ct, 32 ct + 32) for all NQ query tiles of 32 rows, so each
+// wave reads its S^T tile exactly once and splits it into hi/lo bf16 once.
 // Everything is computed transposed so that each lane ends up holding one
 // query row:
 //   L^T = K Q^T          (keys x queries): lane l holds query i = l % 32 and
@@ -53,12 +54,12 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p)
 }
 
 template <int D, int NQ>
-__global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a)
+__global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;              // k-steps over the head dimension
-    constexpr int NC = D / 32;              // value-column tiles
+    constexpr int NC = D / 32;              // value-column tiles = waves
     constexpr int NKT = NQ;                 // key tiles (keys = queries = block rows)
-    constexpr int NT = NQ * NC * kWave;     // threads
+    constexpr int NT = NC * kWave;          // threads
     constexpr int R = NQ * 32;              // staged rows
     constexpr int P = D + 8;                // LDS row pitch (bf16)
     constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -74,8 +75,7 @@ __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a
     if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
 
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, w = tid / kWave;
-    const int qt = w / NC, ct = w % NC;
+    const int lane = tid % kWave, ct = tid / kWave;
     const int l32 = lane % 32, hh = lane / 32;
     const int64_t rs = (int64_t)a.heads * D;                 // token row stride
     const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
@@ -118,106 +118,116 @@ __global__ __launch_bounds__(NQ * D / 32 * kWave) void step_bf16_mfma(StepArgs a
         *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
     }
     __syncthreads();
-    if (qt * 32 >= Br) return;                               // no valid query in this tile
 
-    // ---- Q operand (B of L^T and, ReLU'd, B of S^T phi(Q)^T)
-    const int i = qt * 32 + l32;
-    u16x8 qv[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qv[s] = *reinterpret_cast<const u16x8*>(sq + i * P + 16 * s + 8 * hh);
-
-    // ---- L^T = K Q^T per key tile
-    f32x16 lt[NKT];
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-        f32x16 acc = {};
-        if (jt < nkt) {
-            const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)), as_bf16x8(qv[s]), acc);
-        }
-        lt[jt] = acc;
-    }
-    // ---- row softmax over the Br valid keys (one query per lane pair)
-    float m = -INFINITY;
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-            const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
-            lt[jt][rr] = x;
-            m = fmaxf(m, x);
-        }
-    }
-    m = fmaxf(m, __shfl_xor(m, 32));
-    float sum = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const float p = __builtin_amdgcn_exp2f(lt[jt][rr] - m);   // exp2(-inf) = 0 for masked keys
-            lt[jt][rr] = p;
-            sum += p;
-        }
-    }
-    sum += __shfl_xor(sum, 32);
-    const float inv = __builtin_amdgcn_rcpf(sum);
-
-    // ---- O^T = V^T P^T (P as hi + lo bf16).  V^T operand of k-step (jt, gp):
-    // keys jt*32 + 16gp + 4hh + {0..3} and the same + 8, matching registers
-    // 8gp .. 8gp+7 of L^T; column of lane i in 16-lane group g is
-    // 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4 with q = i/4 (= cA above).
+    // ---- softmax part for every query tile (overlaps the S stream):
+    //      L^T = K Q^T, row softmax, O^T = V^T P^T (P as hi + lo bf16)
     const int g = lane / 16, jl = lane % 16;
     const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
-    f32x16 o = {};
+    f32x16 o[NQ];
 #pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-        if (jt < nkt) {
+    for (int qt = 0; qt < NQ; ++qt) {
+        o[qt] = f32x16{};
+        if (qt >= nkt) continue;
+        const uint16_t* qr = sq + (qt * 32 + l32) * P + 8 * hh;
+        f32x16 lt[NKT];
 #pragma unroll
-            for (int gp = 0; gp < 2; ++gp) {
-                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
-                u16x8 vop;
+        for (int jt = 0; jt < NKT; ++jt) {
+            f32x16 acc = {};
+            if (jt < nkt) {
+                const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vop[e] = static_cast<uint16_t>(v0[e]);
-                    vop[4 + e] = static_cast<uint16_t>(v1[e]);
+                for (int s = 0; s < KS; ++s)
+                    acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
+                                 as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), acc);
+            }
+            lt[jt] = acc;
+        }
+        // row softmax over the Br valid keys (one query per lane pair)
+        float m = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < NKT; ++jt) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+                const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
+                lt[jt][rr] = x;
+                m = fmaxf(m, x);
+            }
+        }
+        m = fmaxf(m, __shfl_xor(m, 32));
+        float sum = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < NKT; ++jt) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const float p = __builtin_amdgcn_exp2f(lt[jt][rr] - m);   // exp2(-inf) = 0 for masked keys
+                lt[jt][rr] = p;
+                sum += p;
+            }
+        }
+        sum += __shfl_xor(sum, 32);
+        const float inv = __builtin_amdgcn_rcpf(sum);
+        // V^T operand of k-step (jt, gp): keys jt*32 + 16gp + 4hh + {0..3} and the
+        // same + 8, matching registers 8gp .. 8gp+7 of L^T; the column of lane i in
+        // 16-lane group g is 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4, q = i/4 (= cA).
+#pragma unroll
+        for (int jt = 0; jt < NKT; ++jt) {
+            if (jt < nkt) {
+#pragma unroll
+                for (int gp = 0; gp < 2; ++gp) {
+                    const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+                    const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+                    const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+                    u16x8 vop;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        vop[e] = static_cast<uint16_t>(v0[e]);
+                        vop[4 + e] = static_cast<uint16_t>(v1[e]);
+                    }
+                    float pp[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
+                    bf16x8 phi, plo;
+                    split_hi_lo(pp, phi, plo);
+                    o[qt] = mfma32(as_bf16x8(vop), phi, o[qt]);
+                    o[qt] = mfma32(as_bf16x8(vop), plo, o[qt]);
                 }
-                float pp[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
-                bf16x8 phi, plo;
-                split_hi_lo(pp, phi, plo);
-                o = mfma32(as_bf16x8(vop), phi, o);
-                o = mfma32(as_bf16x8(vop), plo, o);
             }
         }
     }
-    // ---- O^T += S^T phi(Q)^T (S as hi + lo bf16)
+    // ---- linear part: O^T += S^T phi(Q)^T for every query tile, S as hi + lo
+    // bf16 split once and reused across the query tiles
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const float sv8[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
                               sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
         bf16x8 shi, slo;
         split_hi_lo(sv8, shi, slo);
-        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv[s]));
-        o = mfma32(shi, pq, o);
-        o = mfma32(slo, pq, o);
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) {
+            if (qt < nkt) {
+                const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
+                const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
+                o[qt] = mfma32(shi, pq, o[qt]);
+                o[qt] = mfma32(slo, pq, o[qt]);
+            }
+        }
     }
     // ---- store: lane holds query i, columns 32 ct + 16 hh + 0..15
-    if (i < Br) {
-        u16x8 o0, o1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o0[e] = f32_to_bf16_bits(o[e]);
-            o1[e] = f32_to_bf16_bits(o[8 + e]);
+    for (int qt = 0; qt < NQ; ++qt) {
+        const int i = qt * 32 + l32;
+        if (qt < nkt && i < Br) {
+            u16x8 o0, o1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o0[e] = f32_to_bf16_bits(o[qt][e]);
+                o1[e] = f32_to_bf16_bits(o[qt][8 + e]);
+            }
+            u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
+            op[0] = o0;
+            op[1] = o1;
         }
-        u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
-        op[0] = o0;
-        op[1] = o1;
     }
 }
 
@@ -402,8 +412,8 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
 template <int D>
 static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
 {
-    if (a.blk <= 32) step_bf16_mfma<D, 1><<<units, 1 * D / 32 * kWave, 0, stream>>>(a);
-    else if (a.blk <= 64) step_bf16_mfma<D, 2><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
+    if (a.blk <= 32) step_bf16_mfma<D, 1><<<units, D / 32 * kWave, 0, stream>>>(a);
+    else if (a.blk <= 64) step_bf16_mfma<D, 2><<<units, D / 32 * kWave, 0, stream>>>(a);
     else step_bf16_mfma_long<D><<<units, 4 * D / 32 * kWave, 0, stream>>>(a);
 }
 

@@ -114,16 +114,20 @@ class Job:
         self.cost["step"] = step_cost(n * H, B, d)
         self.cost["commit"] = commit_cost(n * H, B, d)
 
+    # Calls are prepared once (validated and marshalled) and re-enqueued with
+    # one ctypes call each, as a serving loop would.
     def _prefill(self):
-        bh.hybrid_state_prefill(self.pk, self.pv, self.cu, self.state, self.slots, max_len=self.max_len,
-                                chunk=self.wl.chunk, workspace=self.ws)
+        if not hasattr(self, "_prefill_call"):
+            self._prefill_call = bh.prepare_prefill(self.pk, self.pv, self.cu, self.state, self.slots,
+                                                    max_len=self.max_len, chunk=self.wl.chunk, workspace=self.ws)
+        self._prefill_call()
 
     def _step_fn(self, i):
-        return lambda: bh.hybrid_attn_step(self.q[i], self.k[i], self.v[i], self.state, self.slots, out=self.out,
-                                           scale=self.wl.scale)
+        return bh.prepare_step(self.q[i], self.k[i], self.v[i], self.state, self.slots, self.out,
+                               scale=self.wl.scale)
 
     def _commit_fn(self, i):
-        return lambda: bh.hybrid_state_commit(self.k[i], self.v[i], self.state, self.slots)
+        return bh.prepare_commit(self.k[i], self.v[i], self.state, self.slots)
 
     def reset(self):
         self.state.zero_()

@@ -14,7 +14,9 @@ with the same names:
 PyTorch only provides device memory and streams.
 """
 from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_state_commit,
-                      hybrid_state_prefill, hybrid_state_prefill_workspace_bytes, load_library)
+                      hybrid_state_prefill, hybrid_state_prefill_workspace_bytes, load_library, prepare_commit,
+                      prepare_prefill, prepare_step)
 
 __all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_state_commit",
-           "hybrid_state_prefill", "hybrid_state_prefill_workspace_bytes", "load_library"]
+           "hybrid_state_prefill", "hybrid_state_prefill_workspace_bytes", "load_library", "prepare_commit",
+           "prepare_prefill", "prepare_step"]

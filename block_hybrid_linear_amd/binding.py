@@ -95,9 +95,7 @@ def abi_version() -> int:
     return load_library().hybrid_abi_version()
 
 
-def hybrid_attn_step(q, k, v, state, slots, out=None, blk_lens=None, scale=None, stream=None):
-    """out = Softmax(scale Q K^T) V + ReLU(Q) S[slots] for q/k/v [n_req, blk, H, d];
-    state [n_slots, H, d, d] fp32 (each d x d block stores S transposed)."""
+def _step_args(q, k, v, state, slots, out, blk_lens, scale):
     n_req, blk, H, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
@@ -105,25 +103,42 @@ def hybrid_attn_step(q, k, v, state, slots, out=None, blk_lens=None, scale=None,
         raise ValueError(f"state must be [n_slots, {H}, {d}, {d}]")
     if slots.shape != (n_req,):
         raise ValueError("slots must be [n_req]")
-    if out is None:
-        out = torch.zeros_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype:
+    if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q")
     if blk_lens is not None and blk_lens.shape != (n_req,):
         raise ValueError("blk_lens must be [n_req]")
     if scale is None:
         scale = d ** -0.5
-    lib = load_library()
-    st = lib.hybrid_attn_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(state, "state", torch.float32),
-                              _dev(slots, "slots", torch.int32), _dev(out, "out"),
-                              _opt(blk_lens, "blk_lens", torch.int32), n_req, state.shape[0], H, blk, d,
-                              float(scale), _dtype_code(q), _stream(stream))
-    _check("hybrid_attn_step", st)
+    return (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(state, "state", torch.float32),
+            _dev(slots, "slots", torch.int32), _dev(out, "out"), _opt(blk_lens, "blk_lens", torch.int32),
+            n_req, state.shape[0], H, blk, d, float(scale), _dtype_code(q))
+
+
+def hybrid_attn_step(q, k, v, state, slots, out=None, blk_lens=None, scale=None, stream=None):
+    """out = Softmax(scale Q K^T) V + ReLU(Q) S[slots] for q/k/v [n_req, blk, H, d];
+    state [n_slots, H, d, d] fp32 (each d x d block stores S transposed)."""
+    if out is None:
+        out = torch.zeros_like(q)
+    args = _step_args(q, k, v, state, slots, out, blk_lens, scale)
+    _check("hybrid_attn_step", load_library().hybrid_attn_step(*args, _stream(stream)))
     return out
 
 
-def hybrid_state_commit(k, v, state, slots, blk_lens=None, stream=None):
-    """state[slots] += ReLU(K)^T V (stored transposed), in place."""
+def prepare_step(q, k, v, state, slots, out, blk_lens=None, scale=None, stream=None):
+    """Validates and marshals once; returns a callable that enqueues the same
+    step again (one ctypes call) -- for loops that re-run a step on buffers
+    whose contents change but whose storage does not."""
+    args = _step_args(q, k, v, state, slots, out, blk_lens, scale) + (_stream(stream),)
+    fn = load_library().hybrid_attn_step
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_attn_step", st)
+    return run
+
+
+def _commit_args(k, v, state, slots, blk_lens):
     n_req, blk, H, d = k.shape
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k, v must share shape and dtype")
@@ -133,27 +148,34 @@ def hybrid_state_commit(k, v, state, slots, blk_lens=None, stream=None):
         raise ValueError("slots must be [n_req]")
     if blk_lens is not None and blk_lens.shape != (n_req,):
         raise ValueError("blk_lens must be [n_req]")
-    lib = load_library()
-    st = lib.hybrid_state_commit(_dev(k, "k"), _dev(v, "v"), _dev(state, "state", torch.float32),
-                                 _dev(slots, "slots", torch.int32), _opt(blk_lens, "blk_lens", torch.int32),
-                                 n_req, state.shape[0], H, blk, d, _dtype_code(k), _stream(stream))
-    _check("hybrid_state_commit", st)
+    return (_dev(k, "k"), _dev(v, "v"), _dev(state, "state", torch.float32), _dev(slots, "slots", torch.int32),
+            _opt(blk_lens, "blk_lens", torch.int32), n_req, state.shape[0], H, blk, d, _dtype_code(k))
+
+
+def hybrid_state_commit(k, v, state, slots, blk_lens=None, stream=None):
+    """state[slots] += ReLU(K)^T V (stored transposed), in place."""
+    args = _commit_args(k, v, state, slots, blk_lens)
+    _check("hybrid_state_commit", load_library().hybrid_state_commit(*args, _stream(stream)))
     return state
+
+
+def prepare_commit(k, v, state, slots, blk_lens=None, stream=None):
+    """Prepared form of hybrid_state_commit (see prepare_step)."""
+    args = _commit_args(k, v, state, slots, blk_lens) + (_stream(stream),)
+    fn = load_library().hybrid_state_commit
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_state_commit", st)
+    return run
 
 
 def hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk=256) -> int:
     return int(load_library().hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk))
 
 
-def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, workspace=None,
-                         stream=None):
-    """state[slots[r]] = sum over prompt r of ReLU(k_t)^T v_t (overwrite).
-
-    k, v packed [total, H, d]; cu_seqlens int64 [n_req + 1] on the GPU.
-    ``max_len`` (host int) is an optional upper bound of the prompt lengths.
-    ``workspace`` is a GPU uint8 tensor of at least
-    ``hybrid_state_prefill_workspace_bytes`` bytes; if omitted one is
-    allocated through torch."""
+def _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace):
     total, H, d = k.shape
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k, v must share shape and dtype")
@@ -167,11 +189,36 @@ def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256
     need = hybrid_state_prefill_workspace_bytes(n_req, H, d, total, max_len, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
-    lib = load_library()
-    st = lib.hybrid_state_prefill(_dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens, "cu_seqlens", torch.int64),
-                                  total, max_len, _dev(state, "state", torch.float32),
-                                  _dev(slots, "slots", torch.int32), n_req, state.shape[0], H, d, chunk,
-                                  _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                  _dtype_code(k), _stream(stream))
-    _check("hybrid_state_prefill", st)
+    args = (_dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens, "cu_seqlens", torch.int64), total, max_len,
+            _dev(state, "state", torch.float32), _dev(slots, "slots", torch.int32), n_req, state.shape[0], H, d,
+            chunk, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _dtype_code(k))
+    return args, workspace
+
+
+def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, workspace=None,
+                         stream=None):
+    """state[slots[r]] = sum over prompt r of ReLU(k_t)^T v_t (overwrite).
+
+    k, v packed [total, H, d]; cu_seqlens int64 [n_req + 1] on the GPU.
+    ``max_len`` (host int) is an optional upper bound of the prompt lengths.
+    ``workspace`` is a GPU uint8 tensor of at least
+    ``hybrid_state_prefill_workspace_bytes`` bytes; if omitted one is
+    allocated through torch."""
+    args, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    _check("hybrid_state_prefill", load_library().hybrid_state_prefill(*args, _stream(stream)))
     return state
+
+
+def prepare_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, workspace=None, stream=None):
+    """Prepared form of hybrid_state_prefill (see prepare_step); keeps its
+    workspace alive."""
+    args, ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    args = args + (_stream(stream),)
+    fn = load_library().hybrid_state_prefill
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_state_prefill", st)
+    run.workspace = ws
+    return run

@@ -11,12 +11,19 @@ with the same names:
     hybrid_state_commit   S += ReLU(K_blk)^T V_blk when a block is finished
     hybrid_state_prefill  S = sum over a prompt of ReLU(k)^T v
 
+and, for comparison, the exact step the method replaces:
+
+    hybrid_exact_step     softmax attention of the active block over its
+                          whole prefix KV cache and itself
+
 PyTorch only provides device memory and streams.
 """
-from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_state_commit,
-                      hybrid_state_prefill, hybrid_state_prefill_workspace_bytes, load_library, prepare_commit,
+from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_exact_step,
+                      hybrid_exact_step_workspace_bytes, hybrid_state_commit, hybrid_state_prefill,
+                      hybrid_state_prefill_workspace_bytes, load_library, prepare_commit, prepare_exact_step,
                       prepare_prefill, prepare_step)
 
-__all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_state_commit",
-           "hybrid_state_prefill", "hybrid_state_prefill_workspace_bytes", "load_library", "prepare_commit",
+__all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_exact_step",
+           "hybrid_exact_step_workspace_bytes", "hybrid_state_commit", "hybrid_state_prefill",
+           "hybrid_state_prefill_workspace_bytes", "load_library", "prepare_commit", "prepare_exact_step",
            "prepare_prefill", "prepare_step"]

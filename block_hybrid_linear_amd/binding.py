@@ -47,7 +47,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                              ctypes.c_int, vp]
         lib.hybrid_state_prefill_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32]
         lib.hybrid_state_prefill_workspace_bytes.restype = sz
-        for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill):
+        lib.hybrid_exact_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz,
+                                          ctypes.c_int, vp]
+        lib.hybrid_exact_step_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.hybrid_exact_step_workspace_bytes.restype = sz
+        for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill, lib.hybrid_exact_step):
             fn.restype = ctypes.c_int
         lib.hybrid_last_error.argtypes = []
         lib.hybrid_last_error.restype = ctypes.c_char_p
@@ -220,5 +224,65 @@ def prepare_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, wor
         st = fn(*args)
         if st != HA_OK:
             _check("hybrid_state_prefill", st)
+    run.workspace = ws
+    return run
+
+
+def hybrid_exact_step_workspace_bytes(n_req, heads, blk, d) -> int:
+    return int(load_library().hybrid_exact_step_workspace_bytes(n_req, heads, blk, d))
+
+
+def _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace):
+    n_req, blk, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != (H, d) or v_cache.shape != k_cache.shape:
+        raise ValueError(f"k_cache, v_cache must be [total_prefix, {H}, {d}]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("the prefix cache must have the dtype of q")
+    if cu_prefix.shape != (n_req + 1,):
+        raise ValueError("cu_prefix must be [n_req + 1]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if blk_lens is not None and blk_lens.shape != (n_req,):
+        raise ValueError("blk_lens must be [n_req]")
+    if scale is None:
+        scale = d ** -0.5
+    need = hybrid_exact_step_workspace_bytes(n_req, H, blk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    total = k_cache.shape[0]
+    args = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache") if total else None,
+            _dev(v_cache, "v_cache") if total else None, _dev(cu_prefix, "cu_prefix", torch.int64), total,
+            _dev(out, "out"), _opt(blk_lens, "blk_lens", torch.int32), n_req, H, blk, d, float(scale), chunk,
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _dtype_code(q))
+    return args, workspace
+
+
+def hybrid_exact_step(q, k, v, k_cache, v_cache, cu_prefix, out=None, blk_lens=None, scale=None, chunk=256,
+                      workspace=None, stream=None):
+    """out = Softmax(scale Q [K_p; K]^T) [V_p; V]: exact attention of the active
+    block q/k/v [n_req, blk, H, d] over its prefix (k_cache/v_cache packed
+    [total_prefix, H, d], request r owns rows cu_prefix[r]..cu_prefix[r+1]-1)
+    and itself -- the step block-hybrid attention replaces."""
+    if out is None:
+        out = torch.zeros_like(q)
+    args, _ws = _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace)
+    _check("hybrid_exact_step", load_library().hybrid_exact_step(*args, _stream(stream)))
+    return out
+
+
+def prepare_exact_step(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens=None, scale=None, chunk=256,
+                       workspace=None, stream=None):
+    """Prepared form of hybrid_exact_step (see prepare_step); keeps its
+    workspace alive."""
+    args, ws = _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace)
+    args = args + (_stream(stream),)
+    fn = load_library().hybrid_exact_step
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_exact_step", st)
     run.workspace = ws
     return run

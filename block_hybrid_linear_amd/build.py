@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhybrid_attn.so")
-SOURCES = ("api.hip", "step_kernels.hip", "state_kernels.hip")
+SOURCES = ("api.hip", "step_kernels.hip", "state_kernels.hip", "exact_kernels.hip")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

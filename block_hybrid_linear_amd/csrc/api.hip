@@ -33,8 +33,8 @@ ha_status hip_status(hipError_t e, const char* what)
 bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool known_dtype(ha_dtype t) { return t == HA_F32 || t == HA_BF16; }
 
-// Prefill workspace: the plan (n_req + 2 int64, padded to 256 bytes), then
-// one fp32 partial state per (slice, unit) slot.
+// Prefill and exact-step workspaces: the plan (n_req + 2 int64, padded to 256
+// bytes), then one fp32 partial per (slice, unit) slot.
 size_t plan_bytes(int32_t n_req) { return ((size_t)(n_req + 2) * sizeof(int64_t) + 255) / 256 * 256; }
 
 // Checks shared by step and commit.  Returns HA_OK or the failure status.
@@ -156,6 +156,57 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
     a.d = d;
     a.dtype_bf16 = dtype == HA_BF16;
     return hip_status(ha::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads, int32_t blk, int32_t d)
+{
+    if (n_req <= 0 || heads <= 0 || blk <= 0 || blk > HYBRID_ATTN_MAX_BLK || d <= 0) return 0;
+    return plan_bytes(n_req) + ((size_t)ha::exact_slices(d) + (size_t)n_req * (size_t)heads) *
+                                   (size_t)ha::exact_slot_floats(blk, d) * sizeof(float);
+}
+
+ha_status hybrid_exact_step(const void* q, const void* k, const void* v, const void* k_cache,
+                            const void* v_cache, const int64_t* cu_prefix, int64_t total_prefix,
+                            void* out, const int32_t* blk_lens, int32_t n_req, int32_t heads,
+                            int32_t blk, int32_t d, float scale, int32_t chunk, void* workspace,
+                            size_t workspace_bytes, ha_dtype dtype, void* stream)
+{
+    static const char* fn = "hybrid_exact_step";
+    ha_status st = check_block_call(fn, n_req, 1, heads, blk, d, dtype);
+    if (st != HA_OK) return st;
+    if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    if (chunk <= 0) return fail(HA_ERR_INVALID_ARG, "%s: chunk must be > 0 (got %d)", fn, chunk);
+    if (total_prefix < 0) return fail(HA_ERR_INVALID_ARG, "%s: total_prefix must be >= 0", fn);
+    if (n_req == 0) return HA_OK;
+    if (!q || !k || !v || !out || !cu_prefix)
+        return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, out and cu_prefix must be non-NULL", fn);
+    if (total_prefix > 0 && (!k_cache || !v_cache))
+        return fail(HA_ERR_INVALID_ARG, "%s: k_cache and v_cache must be non-NULL when total_prefix > 0", fn);
+    const size_t need = hybrid_exact_step_workspace_bytes(n_req, heads, blk, d);
+    if (workspace_bytes < need || !workspace)
+        return fail(HA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
+                    workspace_bytes, workspace ? "" : ", NULL");
+    ha::ExactArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.cu = cu_prefix;
+    a.total_prefix = total_prefix;
+    a.out = out;
+    a.blk_lens = blk_lens;
+    a.plan = static_cast<int64_t*>(workspace);
+    a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_bytes(n_req));
+    a.chunk = chunk;
+    a.slices = ha::exact_slices(d);
+    a.n_req = n_req;
+    a.heads = heads;
+    a.blk = blk;
+    a.d = d;
+    a.scale = scale;
+    a.dtype_bf16 = dtype == HA_BF16;
+    return hip_status(ha::launch_exact(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

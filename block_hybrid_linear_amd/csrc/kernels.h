@@ -46,8 +46,40 @@ struct PhiKVArgs {
 // on the device.
 inline int prefill_slices(int d) { return d == 32 ? 2048 : 512; }
 
+// Exact softmax attention of the active block over [prefix; block] (the step
+// without linearisation).  The (request, head, key chunk) list is split into
+// `slices` equal ranges; each slice workgroup writes, per (request, head) it
+// touches, an unnormalised partial output with its running max and sum, and
+// a combine kernel merges them per (request, head).
+struct ExactArgs {
+    const void* q;
+    const void* k;
+    const void* v;              // active block [n_req][blk][heads][d]
+    const void* kc;
+    const void* vc;             // prefix cache [total_prefix][heads][d]
+    const int64_t* cu;          // [n_req + 1] prefix offsets into the cache
+    int64_t total_prefix;
+    void* out;
+    const int32_t* blk_lens;
+    int64_t* plan;              // workspace: [n_req + 2]
+    float* partial;             // workspace: [slices + n_req * heads][exact_slot_floats]
+    int32_t chunk, slices, n_req, heads, blk, d;
+    float scale;
+    bool dtype_bf16;
+};
+
+// Slice workgroups of the exact step (four per compute unit of an MI355X),
+// fixed so that results do not depend on the device.
+inline int exact_slices(int d) { (void)d; return 1024; }
+// Rows of one partial slot: the query rows of the kernel that runs for blk
+// (one, two or four 32-row tiles).  A slot holds rows x d unnormalised
+// outputs, then the running max and the running sum of each row.
+__host__ __device__ inline int exact_slot_rows(int blk) { return blk <= 32 ? 32 : (blk <= 64 ? 64 : 128); }
+inline int exact_slot_floats(int blk, int d) { return exact_slot_rows(blk) * (d + 2); }
+
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream);
+hipError_t launch_exact(const ExactArgs& a, hipStream_t stream);
 
 }  // namespace ha

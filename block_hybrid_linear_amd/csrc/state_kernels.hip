@@ -310,7 +310,7 @@ template <int D>
 __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_bf16_mfma(PhiKVArgs a)
 {
     using P = PhiKVTile<D>;
-    constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG, PF = 3;
+    constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG;
     __shared__ __attribute__((aligned(16))) typename P::Lds lds;
     StageCursor cp, ld;                        // compute and load cursors
     if (!slice_begin(a, cp.sl)) return;

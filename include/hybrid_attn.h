@@ -157,6 +157,51 @@ size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads,
                                             int32_t d, int64_t total_tokens,
                                             int64_t max_len, int32_t chunk);
 
+/*
+ * The exact step that block-hybrid attention replaces (paper abstract: without
+ * linearisation every denoising step attends to all previous blocks through
+ * the KV cache), for comparison at the same shapes:
+ *
+ *   out[r, i, h, :] = sum_{j < P_r + B_r} P_ij w_j,
+ *   P_ij = softmax_j(scale q_i . u_j)
+ *
+ * over the keys u = [prefix keys of request r; its B_r active keys] and the
+ * values w likewise, for i < B_r.  No state is involved.
+ *
+ * q, k, v, out: the active block as in hybrid_attn_step.
+ * k_cache, v_cache: the prefix KV cache, packed [total_prefix][heads][d] in
+ *   the dtype of q; request r's prefix is rows cu_prefix[r] ..
+ *   cu_prefix[r+1]-1 (device int64[n_req + 1]).  A request whose rows fall
+ *   outside [0, total_prefix] (or run backwards) has an empty prefix.  The
+ *   cache pointers may be NULL when total_prefix == 0.
+ * total_prefix: HOST scalar >= 0.
+ * chunk: keys are cut into chunks of `chunk` and the (request, head, chunk)
+ *   list is split into a fixed number of equal ranges, one per workgroup;
+ *   each writes an unnormalised partial output with its running max and sum
+ *   per (request, head) into `workspace`, and a second kernel merges the
+ *   partials of each (request, head) in a fixed order (deterministic).
+ * workspace: device scratch of at least hybrid_exact_step_workspace_bytes()
+ *   bytes (non-NULL when n_req > 0); contents on entry do not matter; calls
+ *   sharing one workspace must be ordered on one stream.
+ * Errors as for hybrid_attn_step, plus chunk < 1, total_prefix < 0, a NULL
+ * cache when total_prefix > 0, or a small workspace (HA_ERR_INVALID_ARG).
+ */
+ha_status hybrid_exact_step(const void* q, const void* k, const void* v,
+                            const void* k_cache, const void* v_cache,
+                            const int64_t* cu_prefix, int64_t total_prefix,
+                            void* out, const int32_t* blk_lens,
+                            int32_t n_req, int32_t heads, int32_t blk,
+                            int32_t d, float scale, int32_t chunk,
+                            void* workspace, size_t workspace_bytes,
+                            ha_dtype dtype, void* stream);
+
+/* Workspace size for hybrid_exact_step (host): a 256-byte-padded plan of
+ * n_req + 2 int64, then (1024 + n_req * heads) partials of R * (d + 2)
+ * floats, R = 32, 64 or 128 for blk <= 32, <= 64 or <= 128.  0 for empty or
+ * invalid sizes. */
+size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads,
+                                         int32_t blk, int32_t d);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* hybrid_last_error(void);
 

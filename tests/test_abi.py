@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("hybrid_attn_step", "hybrid_state_commit", "hybrid_state_prefill",
-              "hybrid_state_prefill_workspace_bytes", "hybrid_last_error", "hybrid_abi_version"):
+              "hybrid_state_prefill_workspace_bytes", "hybrid_exact_step", "hybrid_exact_step_workspace_bytes",
+              "hybrid_last_error", "hybrid_abi_version"):
         assert n in names
 
 
@@ -61,6 +62,12 @@ def prefill(lib, k=1, v=1, cu=1, total=100, max_len=60, state=1, slots=1, n_req=
             chunk=256, ws=1, ws_bytes=1 << 40, dtype=binding.HA_BF16):
     return lib.hybrid_state_prefill(k, v, cu, total, max_len, state, slots, n_req, n_slots, heads, d, chunk,
                                     ws, ws_bytes, dtype, None)
+
+
+def exact(lib, q=1, k=1, v=1, kc=1, vc=1, cu=1, total=100, out=1, n_req=2, heads=4, blk=32, d=64, scale=0.125,
+          chunk=256, ws=1, ws_bytes=1 << 40, dtype=binding.HA_BF16):
+    return lib.hybrid_exact_step(q, k, v, kc, vc, cu, total, out, None, n_req, heads, blk, d, scale, chunk, ws,
+                                 ws_bytes, dtype, None)
 
 
 def last(lib):
@@ -118,12 +125,36 @@ def test_prefill_rejects(lib, kw, status, msg):
     assert msg in last(lib) and "hybrid_state_prefill" in last(lib)
 
 
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=48), binding.HA_ERR_UNSUPPORTED, "head dim"),
+    (dict(dtype=3), binding.HA_ERR_UNSUPPORTED, "dtype"),
+    (dict(blk=0), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(blk=129), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(heads=0), binding.HA_ERR_INVALID_ARG, "heads"),
+    (dict(n_req=-2), binding.HA_ERR_INVALID_ARG, "n_req"),
+    (dict(scale=float("inf")), binding.HA_ERR_INVALID_ARG, "scale"),
+    (dict(chunk=0), binding.HA_ERR_INVALID_ARG, "chunk"),
+    (dict(total=-1), binding.HA_ERR_INVALID_ARG, "total_prefix"),
+    (dict(q=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(cu=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(out=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(kc=None), binding.HA_ERR_INVALID_ARG, "k_cache"),
+    (dict(ws_bytes=10), binding.HA_ERR_INVALID_ARG, "workspace"),
+    (dict(ws=None), binding.HA_ERR_INVALID_ARG, "workspace"),
+])
+def test_exact_rejects(lib, kw, status, msg):
+    assert exact(lib, **kw) == status
+    assert msg in last(lib) and "hybrid_exact_step" in last(lib)
+
+
 def test_empty_batches_are_noops(lib):
     """n_req == 0 returns OK without touching any pointer (all NULL here)."""
     assert step(lib, q=None, k=None, v=None, state=None, slots=None, out=None, n_req=0) == binding.HA_OK
     assert commit(lib, k=None, v=None, state=None, slots=None, n_req=0) == binding.HA_OK
     assert prefill(lib, k=None, v=None, cu=None, state=None, slots=None, ws=None, ws_bytes=0,
                    n_req=0) == binding.HA_OK
+    assert exact(lib, q=None, k=None, v=None, kc=None, vc=None, cu=None, out=None, ws=None, ws_bytes=0,
+                 n_req=0) == binding.HA_OK
 
 
 def test_prefill_workspace_size(lib):
@@ -137,6 +168,19 @@ def test_prefill_workspace_size(lib):
     assert f(40, 2, 16, 0, 0, 7) == plan(40) + (512 + 80) * 16 * 16 * 4
     assert f(0, 1, 16, 0, 10, 1) == 0
     assert f(3, 1, 16, 0, 10, 0) == 0
+
+
+def test_exact_workspace_size(lib):
+    """Plan as for prefill + (1024 + n_req * heads) partials of R rows x
+    (d + 2) floats (output row, max, sum), R = 32 / 64 / 128 for blk up to
+    32 / 64 / 128."""
+    f = bh.hybrid_exact_step_workspace_bytes
+    plan = lambda n: ((n + 2) * 8 + 255) // 256 * 256  # noqa: E731
+    assert f(64, 32, 32, 128) == plan(64) + (1024 + 2048) * 32 * 130 * 4
+    assert f(3, 5, 33, 16) == plan(3) + (1024 + 15) * 64 * 18 * 4
+    assert f(2, 3, 65, 32) == plan(2) + (1024 + 6) * 128 * 34 * 4
+    assert f(1, 1, 128, 64) == plan(1) + (1024 + 1) * 128 * 66 * 4
+    assert f(0, 1, 32, 64) == 0 and f(2, 2, 0, 64) == 0 and f(2, 2, 129, 64) == 0
 
 
 def test_binding_refuses_cpu_tensors():

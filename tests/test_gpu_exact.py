@@ -1,0 +1,146 @@
+"""The exact full-prefix step (the attention block-hybrid attention replaces)
+against the fp64 oracle's softmax over [prefix; active block], through the C
+ABI.
+
+Prefixes span several key chunks with ragged tails, one request has an empty
+prefix, blocks are ragged; every head dim and both dtypes are covered, plus
+the chunk size, malformed offsets, requests with no valid rows, large logits
+and determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_hybrid_linear_amd as bh
+import oracle
+from block_hybrid_linear_amd import synth
+from parity import assert_parity, rows_mask, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SENTINEL = -1024.0  # exact in bf16 and fp32
+
+
+def gen(shape, seed, dtype, std=1.0):
+    return synth.normal(shape, seed, std=std, dtype=dtype).to(DEV)
+
+
+def make_case(prefix_lens, blk, H, d, dtype, seed, std=1.0):
+    n_req = len(prefix_lens)
+    q, k, v = (gen((n_req, blk, H, d), seed + t, dtype, std) for t in range(3))
+    cu = synth.cu_from_lengths(prefix_lens)
+    total = int(cu[-1])
+    kc, vc = (gen((total, H, d), seed + 10 + t, dtype, std) for t in range(2))
+    return q, k, v, kc, vc, cu.to(DEV)
+
+
+def run_exact(q, k, v, kc, vc, cu, blk_lens=None, scale=None, chunk=256):
+    out = torch.full_like(q, SENTINEL)
+    bh.hybrid_exact_step(q, k, v, kc, vc, cu, out=out, blk_lens=blk_lens, scale=scale, chunk=chunk)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_exact(q, k, v, kc, vc, cu, blk_lens, scale, what, chunk=256):
+    n_req, blk = q.shape[:2]
+    out = run_exact(q, k, v, kc, vc, cu, blk_lens, scale, chunk)
+    ref = oracle.exact_step(q, k, v, kc, vc, cu.cpu(), blk_lens=None if blk_lens is None else blk_lens.cpu(),
+                            scale=scale)
+    mask = rows_mask(blk_lens, n_req, blk)
+    o = to64(out)
+    assert np.all(o[~mask] == SENTINEL), f"{what}: rows past B_r were written"
+    return assert_parity(o[mask], ref[mask], q.dtype, what)
+
+
+EXACT_CASES = [  # (d, blk)
+    (128, 32), (128, 64), (128, 100), (128, 128), (128, 1),
+    (64, 33), (64, 128), (32, 17), (32, 64), (16, 4), (16, 32),
+]
+
+
+@pytest.mark.parametrize("d,blk", EXACT_CASES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_exact_step_parity(d, blk, dtype):
+    """4 requests x 3 heads; prefixes 0, 37, 700 and 1500 keys (0, 1, 3 and 6
+    chunks of 256, ragged); blocks full, two-thirds, one row, full."""
+    prefix = [0, 37, 700, 1500]
+    seed = 9000 + 100 * d + blk
+    q, k, v, kc, vc, cu = make_case(prefix, blk, 3, d, dtype, seed)
+    blk_lens = torch.tensor([blk, max(1, (blk * 2) // 3), 1, blk], dtype=torch.int32, device=DEV)
+    e = check_exact(q, k, v, kc, vc, cu, blk_lens, d ** -0.5, f"exact d={d} blk={blk} {dtype}")
+    print(f"d={d} blk={blk} {dtype}: err {e:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 32, 100, 256, 5000])
+def test_exact_step_chunk(chunk):
+    """The chunk size only moves the split points: every chunk gives the
+    oracle's result."""
+    q, k, v, kc, vc, cu = make_case([300, 0, 1029], 48, 2, 128, torch.bfloat16, 9500)
+    check_exact(q, k, v, kc, vc, cu, None, 0.1, f"chunk {chunk}", chunk=chunk)
+
+
+def test_exact_step_no_prefix_is_block_softmax():
+    """With no prefix at all (total_prefix = 0, no cache) the exact step is
+    the softmax part of the hybrid step, i.e. the step with S = 0."""
+    n_req, blk, H, d = 3, 32, 4, 128
+    q, k, v = (gen((n_req, blk, H, d), 9600 + t, torch.bfloat16) for t in range(3))
+    empty = torch.zeros(0, H, d, dtype=torch.bfloat16, device=DEV)
+    cu = torch.zeros(n_req + 1, dtype=torch.int64, device=DEV)
+    out = run_exact(q, k, v, empty, empty, cu)
+    ref = oracle.step(q, k, v, np.zeros((n_req, H, d, d)))
+    assert_parity(out, ref, torch.bfloat16, "empty prefix")
+    hyb = bh.hybrid_attn_step(q, k, v, torch.zeros(n_req, H, d, d, device=DEV),
+                              torch.arange(n_req, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert_parity(out, to64(hyb), torch.bfloat16, "exact vs hybrid with S = 0")
+
+
+def test_exact_step_malformed_offsets_are_empty_prefixes():
+    """Offsets outside [0, total_prefix] or running backwards give that
+    request an empty prefix; the other requests are unaffected."""
+    H, d, blk = 2, 64, 32
+    q, k, v = (gen((4, blk, H, d), 9700 + t, torch.bfloat16) for t in range(3))
+    total = 600
+    kc, vc = (gen((total, H, d), 9710 + t, torch.bfloat16) for t in range(2))
+    cu_host = [0, 300, 200, 600, 900]       # request 1 runs backwards, request 3 ends past the cache
+    out = run_exact(q, k, v, kc, vc, torch.tensor(cu_host, dtype=torch.int64, device=DEV))
+    valid = [(0, 300), (300, 300), (200, 600), (0, 0)]
+    for r, (s0, s1) in enumerate(valid):
+        ref = oracle.exact_step(q[r:r + 1], k[r:r + 1], v[r:r + 1], kc[s0:s1], vc[s0:s1], [0, s1 - s0])
+        assert_parity(out[r:r + 1], ref, torch.bfloat16, f"request {r}")
+
+
+def test_exact_step_empty_rows_are_skipped():
+    """A request with B_r <= 0 is skipped (its rows untouched); B_r > blk
+    counts as blk."""
+    H, d, blk = 2, 128, 32
+    q, k, v, kc, vc, cu = make_case([100, 200, 50], blk, H, d, torch.bfloat16, 9800)
+    lens = torch.tensor([0, 999, -4], dtype=torch.int32, device=DEV)
+    out = run_exact(q, k, v, kc, vc, cu, blk_lens=lens)
+    o = to64(out)
+    assert np.all(o[0] == SENTINEL) and np.all(o[2] == SENTINEL)
+    ref = oracle.exact_step(q[1:2], k[1:2], v[1:2], kc[100:300], vc[100:300], [0, 200])
+    assert_parity(o[1:2], ref, torch.bfloat16, "request 1")
+
+
+def test_exact_step_large_logits():
+    """Logits of order +-100 (q, k ~ N(0, 4^2), scale 1): the running-max
+    rescaling must keep every exponent in range."""
+    q, k, v, kc, vc, cu = make_case([900, 40], 32, 2, 128, torch.bfloat16, 9900, std=4.0)
+    check_exact(q, k, v, kc, vc, cu, None, 1.0, "large logits")
+
+
+def test_exact_step_deterministic():
+    q, k, v, kc, vc, cu = make_case([5000, 3000, 10], 64, 4, 128, torch.bfloat16, 9950)
+    a = run_exact(q, k, v, kc, vc, cu)
+    b = run_exact(q, k, v, kc, vc, cu)
+    assert torch.equal(a, b)
+
+
+def test_exact_step_prepared_matches():
+    q, k, v, kc, vc, cu = make_case([700, 1300], 32, 4, 64, torch.bfloat16, 9970)
+    out = torch.empty_like(q)
+    run = bh.prepare_exact_step(q, k, v, kc, vc, cu, out)
+    run()
+    torch.cuda.synchronize()
+    assert torch.equal(out, run_exact(q, k, v, kc, vc, cu))

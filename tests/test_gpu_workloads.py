@@ -69,6 +69,34 @@ def test_serving_step_full():
     log(f"serving step: rel err {e:.2e} (softmax part {es:.2e}, linear part {el:.2e})")
 
 
+def test_serving_exact_step_sampled():
+    """The exact full-prefix step at the serving shapes (64 requests x 32 heads,
+    d = 128, B = 32, prefixes uniform in [1024, 16384] held as a packed bf16
+    KV cache of ~9 GB); 6 sampled units against the oracle's softmax over
+    [prefix; block]."""
+    W = SERVING_STEP
+    P = synth.uniform_int(W.n_req, *W.prefix_range, synth.seed_of(W.index, tensor=synth.TENSOR_LEN))
+    cu = synth.cu_from_lengths(P)
+    total = int(cu[-1])
+    kc = synth.normal((total, W.heads, W.d), synth.seed_of(W.index, 99, 0, synth.TENSOR_K), device=DEV)
+    vc = synth.normal((total, W.heads, W.d), synth.seed_of(W.index, 99, 0, synth.TENSOR_V), device=DEV)
+    q, k, v = (synth.normal((W.n_req, W.blk, W.heads, W.d), synth.seed_of(W.index, 0, 0, t), device=DEV)
+               for t in range(3))
+    out = bh.hybrid_exact_step(q, k, v, kc, vc, cu.to(DEV), scale=W.scale)
+    units = _units(W.n_req, W.heads, 6, 303)
+    log(f"exact step: {total} cache rows; sampled units {units}")
+    got, ref = [], []
+    for r, h in units:
+        s0, s1 = int(cu[r]), int(cu[r + 1])
+        sl = lambda t: t[r:r + 1, :, h:h + 1].cpu()  # noqa: E731
+        ref.append(oracle.exact_step(sl(q), sl(k), sl(v), kc[s0:s1, h:h + 1].cpu(), vc[s0:s1, h:h + 1].cpu(),
+                                     [0, s1 - s0], scale=W.scale))
+        got.append(sl(out))
+    torch.cuda.synchronize()
+    e = assert_parity(np.stack([to64(g) for g in got]), np.stack(ref), torch.bfloat16, "exact step")
+    log(f"serving exact step: rel err {e:.2e}")
+
+
 def _units(n_req, heads, count, seed):
     rng = np.random.default_rng(seed)
     idx = rng.choice(n_req * heads, size=count, replace=False)

@@ -16,8 +16,10 @@ kernel's achieved GB/s and TFLOP/s against the MI355X peaks (8 TB/s HBM,
 2.5 PFLOP/s dense bf16); ``roofline`` reports the call with the largest share
 of the time.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample
 of the same workload's (request, head) units and scales it to tokens/s.
+``context`` times, for comparison only, the hybrid step against the exact
+full-prefix step it replaces at the concurrent-serving shapes.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-context]
 """
 from __future__ import annotations
 
@@ -62,6 +64,13 @@ def commit_cost(units, B, d, e=2):
 
 def prefill_cost(token_heads, units, d, e=2):
     return token_heads * 2 * d * e + units * d * d * 4, token_heads * 2 * d * d
+
+
+def exact_cost(prefix_token_heads, units, B, d, e=2):
+    """Exact full-prefix step: every prefix key/value row once, plus the block's
+    Q/K/V read and O written; flops of Q K^T and P V over P_r + B keys."""
+    keys = prefix_token_heads + units * B
+    return prefix_token_heads * 2 * d * e + units * 4 * B * d * e, 4 * B * d * keys
 
 
 # ---------------------------------------------------------------------------
@@ -193,12 +202,18 @@ def cpu_baseline(job: Job, budget_s: float) -> dict:
 # was taken on (profiles/traffic.md holds one line per kernel)
 # ---------------------------------------------------------------------------
 
-def source_digest() -> str:
-    h = hashlib.sha256()
+KERNEL_SOURCES = {"step": "step_kernels.hip", "commit": "state_kernels.hip", "prefill": "state_kernels.hip",
+                  "exact": "exact_kernels.hip"}
+
+
+def source_digest(call: str | None = None) -> str:
+    """Digest of the sources that make a call's kernels (its .hip file and the
+    shared device headers), or of every kernel source when call is None."""
     csrc = os.path.join(ROOT, "block_hybrid_linear_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    names = sorted(set(KERNEL_SOURCES.values())) if call is None else [KERNEL_SOURCES[call]]
+    h = hashlib.sha256()
+    for name in names + ["device_common.h", "kernels.h"]:
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -210,9 +225,69 @@ def measured_traffic(call: str, workload: str):
                                                                                     re.escape(call)))
     for line in open(path):
         m = pat.match(line)
-        if m and m.group(1) == source_digest():
+        if m and m.group(1) == source_digest(call):
             return float(m.group(2))
     return None
+
+
+# ---------------------------------------------------------------------------
+# Context: the hybrid step against the exact full-prefix step it replaces, at
+# the concurrent-serving shapes (64 requests x 32 heads, d = 128, B = 32,
+# prefixes uniform in [1024, 16384]: S per request for the hybrid step, a
+# packed bf16 KV cache of ~9 GB for the exact step)
+# ---------------------------------------------------------------------------
+
+def time_call(fn, iters: int, warm: int = 2) -> float:
+    """Average ms per call from HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def exact_context(dev="cuda", rotate: int = 4) -> dict:
+    """The hybrid step cycles through `rotate` distinct input sets (Q/K/V and
+    S, ~201 MB each) so that its inputs come from HBM rather than from the
+    256 MB last-level cache; the exact step's ~9 GB cache cannot stay there."""
+    W = SERVING_STEP
+    n, H, d, B = W.n_req, W.heads, W.d, W.blk
+    P = synth.uniform_int(n, *W.prefix_range, synth.seed_of(W.index, tensor=synth.TENSOR_LEN))
+    cu = synth.cu_from_lengths(P)
+    total = int(cu[-1])
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    sets = []
+    for i in range(rotate):
+        S = synth.normal((n, H, d, d), synth.seed_of(W.index, i, 0, synth.TENSOR_S), dtype=torch.float32,
+                         device=dev)
+        S.mul_(torch.sqrt(P.double() / 2).float().to(dev).view(-1, 1, 1, 1))
+        q, k, v = (synth.normal((n, B, H, d), synth.seed_of(W.index, i, 0, t), device=dev) for t in range(3))
+        sets.append((q, k, v, S, torch.empty_like(q)))
+    kc = synth.normal((total, H, d), synth.seed_of(W.index, PROMPT_BLOCK, 0, synth.TENSOR_K), device=dev)
+    vc = synth.normal((total, H, d), synth.seed_of(W.index, PROMPT_BLOCK, 0, synth.TENSOR_V), device=dev)
+    hyb = [bh.prepare_step(q, k, v, S, slots, out, scale=W.scale) for q, k, v, S, out in sets]
+    q, k, v, _, out = sets[0]
+    exact = bh.prepare_exact_step(q, k, v, kc, vc, cu.to(dev), out, scale=W.scale, chunk=256)
+    it = iter(range(1 << 30))
+    t_h = time_call(lambda: hyb[next(it) % rotate](), 48)
+    t_e = time_call(exact, 10)
+    hb, hf = step_cost(n * H, B, d)
+    eb, ef = exact_cost(total * H, n * H, B, d)
+    res = {"workload": W.name, "n_req": n, "heads": H, "head_dim": d, "block": B,
+           "prefix_range": list(W.prefix_range), "prefix_tokens": total,
+           "hybrid_step_us": round(t_h * 1e3, 2), "hybrid_GBps": round(hb / (t_h * 1e-3) / 1e9, 1),
+           "exact_step_us": round(t_e * 1e3, 2), "exact_GBps": round(eb / (t_e * 1e-3) / 1e9, 1),
+           "exact_TFLOPs": round(ef / (t_e * 1e-3) / 1e12, 2), "exact_alg_bytes": eb, "hybrid_alg_bytes": hb,
+           "speedup_vs_exact": round(t_e / t_h, 2),
+           "traffic": {"step": measured_traffic("step", W.name), "exact": measured_traffic("exact", W.name)}}
+    del kc, vc, sets, hyb, exact
+    torch.cuda.empty_cache()
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -227,6 +302,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=PREFILL_DECODE.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the hybrid-vs-exact step timing at the serving shapes")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle time")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times): the known-size kernel that scales "
@@ -309,6 +386,9 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_context:
+        log("[bench] context: hybrid step vs exact full-prefix step at the serving shapes")
+        result["context"] = exact_context()
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(job, args.cpu_budget)

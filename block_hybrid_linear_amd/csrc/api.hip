@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "../../include/hybrid_attn.h"
@@ -31,6 +32,18 @@ ha_status hip_status(hipError_t e, const char* what)
 }
 
 bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// The kernels move data in 16-byte vectors and address the workspace's
+// partial slots with 256-byte-aligned offsets.
+bool aligned(const void* p, uintptr_t n) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+ha_status check_aligned(const char* fn, std::initializer_list<const void*> data, const void* workspace)
+{
+    for (const void* p : data)
+        if (!aligned(p, 16)) return fail(HA_ERR_INVALID_ARG, "%s: data pointers must be 16-byte aligned", fn);
+    if (!aligned(workspace, 256)) return fail(HA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    return HA_OK;
+}
 bool known_dtype(ha_dtype t) { return t == HA_F32 || t == HA_BF16; }
 
 // Prefill and exact-step workspaces: the plan (n_req + 2 int64, padded to 256
@@ -73,6 +86,7 @@ ha_status hybrid_attn_step(const void* q, const void* k, const void* v, const fl
     if (n_req == 0) return HA_OK;
     if (!q || !k || !v || !state || !slots || !out)
         return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state, slots and out must be non-NULL", fn);
+    if ((st = check_aligned(fn, {q, k, v, state, out}, nullptr)) != HA_OK) return st;
     ha::StepArgs a{q, k, v, state, slots, out, blk_lens, n_req, n_slots, heads, blk, d, scale,
                    dtype == HA_BF16};
     return hip_status(ha::launch_step(a, static_cast<hipStream_t>(stream)), fn);
@@ -88,6 +102,7 @@ ha_status hybrid_state_commit(const void* k, const void* v, float* state, const 
     if (n_req == 0) return HA_OK;
     if (!k || !v || !state || !slots)
         return fail(HA_ERR_INVALID_ARG, "%s: k, v, state and slots must be non-NULL", fn);
+    if ((st = check_aligned(fn, {k, v, state}, nullptr)) != HA_OK) return st;
     ha::PhiKVArgs a{};
     a.k = k;
     a.v = v;
@@ -139,6 +154,7 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
     if (workspace_bytes < need || !workspace)
         return fail(HA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
                     workspace_bytes, workspace ? "" : ", NULL");
+    if (ha_status st = check_aligned(fn, {k, v, state}, workspace); st != HA_OK) return st;
     ha::PhiKVArgs a{};
     a.k = k;
     a.v = v;
@@ -161,7 +177,7 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
 size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads, int32_t blk, int32_t d)
 {
     if (n_req <= 0 || heads <= 0 || blk <= 0 || blk > HYBRID_ATTN_MAX_BLK || d <= 0) return 0;
-    return plan_bytes(n_req) + ((size_t)ha::exact_slices(d) + (size_t)n_req * (size_t)heads) *
+    return plan_bytes(n_req) + ((size_t)ha::exact_slices(d, blk) + (size_t)n_req * (size_t)heads) *
                                    (size_t)ha::exact_slot_floats(blk, d) * sizeof(float);
 }
 
@@ -186,6 +202,7 @@ ha_status hybrid_exact_step(const void* q, const void* k, const void* v, const v
     if (workspace_bytes < need || !workspace)
         return fail(HA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
                     workspace_bytes, workspace ? "" : ", NULL");
+    if ((st = check_aligned(fn, {q, k, v, k_cache, v_cache, out}, workspace)) != HA_OK) return st;
     ha::ExactArgs a{};
     a.q = q;
     a.k = k;
@@ -199,7 +216,7 @@ ha_status hybrid_exact_step(const void* q, const void* k, const void* v, const v
     a.plan = static_cast<int64_t*>(workspace);
     a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_bytes(n_req));
     a.chunk = chunk;
-    a.slices = ha::exact_slices(d);
+    a.slices = ha::exact_slices(d, blk);
     a.n_req = n_req;
     a.heads = heads;
     a.blk = blk;

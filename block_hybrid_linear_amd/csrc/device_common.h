@@ -75,4 +75,22 @@ template <> struct Elem<uint16_t> {
 
 __device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }
 
+// Read of a small per-request array (offsets, plans, lengths) at an index that
+// is the same in every lane, through the scalar cache.  The data is written
+// by the host or by an earlier kernel, never by the reading kernel, and a
+// scalar load does not count against the vector-memory counter, so cursor
+// updates in a streaming loop never wait for the key/value loads in flight.
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* p, int64_t i)
+{
+    typedef const __attribute__((address_space(4))) T* const_ptr;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)i);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)i >> 32));
+    return ((const_ptr)p)[(int64_t)(((uint64_t)hi << 32) | lo)];
+}
+
+// The same read where the index differs between lanes.
+template <typename T>
+__device__ __forceinline__ T lane_load(const T* p, int64_t i) { return p[i]; }
+
 }  // namespace ha

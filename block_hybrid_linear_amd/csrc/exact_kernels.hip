@@ -31,23 +31,29 @@ __device__ __forceinline__ s16x4e lds_read_tr4e(const uint16_t* p)
 // (B_r <= 0) has no chunks (and no output); malformed prefix offsets (outside
 // [0, total_prefix] or running backwards) count as an empty prefix.
 // ---------------------------------------------------------------------------
+
+// Valid rows, prefix length and key chunks of request r; Load is uniform_load
+// where r is the same in every lane, lane_load otherwise.
+template <bool Uniform>
 __device__ __forceinline__ int exact_rows(const ExactArgs& a, int r)
 {
-    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    const int Br = a.blk_lens ? (Uniform ? uniform_load(a.blk_lens, r) : lane_load(a.blk_lens, r)) : a.blk;
     return Br > a.blk ? a.blk : (Br < 0 ? 0 : Br);
 }
 
+template <bool Uniform>
 __device__ __forceinline__ int64_t exact_prefix(const ExactArgs& a, int r)
 {
-    const int64_t s0 = a.cu[r], s1 = a.cu[r + 1];
+    const int64_t s0 = Uniform ? uniform_load(a.cu, r) : lane_load(a.cu, r);
+    const int64_t s1 = Uniform ? uniform_load(a.cu, r + 1) : lane_load(a.cu, r + 1);
     return (s0 < 0 || s1 > a.total_prefix || s1 < s0) ? 0 : s1 - s0;
 }
 
 __device__ __forceinline__ int64_t exact_chunks(const ExactArgs& a, int r)
 {
-    const int Br = exact_rows(a, r);
+    const int Br = exact_rows<false>(a, r);
     if (Br <= 0) return 0;
-    return (exact_prefix(a, r) + Br + a.chunk - 1) / a.chunk;
+    return (exact_prefix<false>(a, r) + Br + a.chunk - 1) / a.chunk;
 }
 
 __global__ __launch_bounds__(256) void exact_plan(ExactArgs a)
@@ -80,11 +86,15 @@ __global__ __launch_bounds__(256) void exact_plan(ExactArgs a)
 }
 
 // Cursor over one slice's chunk range [c0, c1): pieces are (unit, key range).
+// Key j of unit (r, h) is prefix cache row cu[r] + j for j < P, else active
+// row j - P; its element offset is (j < P ? cbase : abase) + j * heads * d in
+// the cache or the active block respectively.
 struct ExactCursor {
-    int r, h;
+    int r, h, Br;
     int64_t c0, c1;     // remaining chunks of the slice
     int64_t j, j1;      // current key stage start and the piece's end (key index within the unit)
-    int64_t p0, P;      // the unit's first prefix row in the cache and its prefix length
+    int64_t P;          // prefix length of the unit
+    int64_t cbase, abase;
     bool live;
 };
 
@@ -92,15 +102,19 @@ __device__ __forceinline__ void exact_next_piece(const ExactArgs& a, ExactCursor
 {
     c.live = c.c0 < c.c1;
     if (!c.live) return;
-    while (a.plan[c.r + 1] <= c.c0) ++c.r;      // skip finished and empty requests
-    const int64_t nch = (a.plan[c.r + 1] - a.plan[c.r]) / a.heads;
-    const int64_t local = c.c0 - a.plan[c.r];
+    while (uniform_load(a.plan, c.r + 1) <= c.c0) ++c.r;     // skip finished and empty requests
+    const int64_t pr = uniform_load(a.plan, c.r);
+    const int64_t nch = (uniform_load(a.plan, c.r + 1) - pr) / a.heads;
+    const int64_t local = c.c0 - pr;
     c.h = (int)(local / nch);
     const int64_t k0 = local % nch;
     const int64_t k1 = (k0 + (c.c1 - c.c0) < nch) ? k0 + (c.c1 - c.c0) : nch;
-    c.P = exact_prefix(a, c.r);
-    c.p0 = c.P > 0 ? a.cu[c.r] : 0;
-    const int64_t N = c.P + exact_rows(a, c.r);
+    const int64_t rs = (int64_t)a.heads * a.d;
+    c.P = exact_prefix<true>(a, c.r);
+    c.Br = exact_rows<true>(a, c.r);
+    c.cbase = (c.P > 0 ? uniform_load(a.cu, c.r) : 0) * rs + (int64_t)c.h * a.d;
+    c.abase = ((int64_t)c.r * a.blk * a.heads + c.h) * a.d - c.P * rs;
+    const int64_t N = c.P + c.Br;
     c.j = k0 * a.chunk;
     c.j1 = k1 * a.chunk < N ? k1 * a.chunk : N;
     c.c0 += k1 - k0;
@@ -108,14 +122,14 @@ __device__ __forceinline__ void exact_next_piece(const ExactArgs& a, ExactCursor
 
 __device__ __forceinline__ bool exact_begin(const ExactArgs& a, ExactCursor& c)
 {
-    const int64_t C = a.plan[a.n_req], S = a.plan[a.n_req + 1];
+    const int64_t C = uniform_load(a.plan, a.n_req), S = uniform_load(a.plan, a.n_req + 1);
     c.c0 = (int64_t)blockIdx.x * S;
     c.c1 = c.c0 + S < C ? c.c0 + S : C;
     if (c.c0 >= c.c1) return false;
     int lo = 0, hi = a.n_req;
     while (hi - lo > 1) {
         const int mid = (lo + hi) / 2;
-        if (a.plan[mid] <= c.c0) lo = mid;
+        if (uniform_load(a.plan, mid) <= c.c0) lo = mid;
         else hi = mid;
     }
     c.r = lo;
@@ -165,11 +179,10 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
     static_assert(RB == 32 * NQ, "one 32-row query tile per NQ");
     const int slot_floats = RB * (D + 2);       // exact_slot_rows(blk) == RB for the blk this runs with
 
-    // key j of unit (r, h): prefix cache row cu[r] + j, or active row j - P
     auto key_row = [&](const ExactCursor& c, int64_t j, const uint16_t* cache, const uint16_t* act) {
         const int64_t jc = j < c.j1 ? j : c.j1 - 1;             // clamp past the piece
-        return jc < c.P ? cache + (c.p0 + jc) * rs + (int64_t)c.h * D
-                        : act + (((int64_t)c.r * a.blk + (jc - c.P)) * a.heads + c.h) * D;
+        const bool pre = jc < c.P;
+        return (pre ? cache : act) + ((pre ? c.cbase : c.abase) + jc * rs);
     };
     auto load_stage = [&](u32x4 (&x)[2 * KCPT]) {
 #pragma unroll
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
     };
     // stage the current piece's query block (rows past B_r repeat row B_r - 1)
     auto load_q = [&]() {
-        const int Br = exact_rows(a, cp.r);
+        const int Br = cp.Br;
         const uint16_t* q0 = qa + ((int64_t)cp.r * a.blk * a.heads + cp.h) * D;
 #pragma unroll
         for (int u = 0; u < QCPT; ++u) {
@@ -222,15 +235,20 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
     load_stage(x1);
     load_stage(x2);
     int sg = 0;
+    // One stage.  Staging and the next loads happen on every path (once the
+    // slice is exhausted they repeat the last valid rows), so every path
+    // around the loop issues the three register sets' loads in the same order
+    // and each stage waits only for its own set; only the arithmetic is
+    // skipped past the end.
     auto run_stage = [&](u32x4 (&x)[2 * KCPT]) {
-        if (!cp.live) return;                                   // uniform
         const int buf = sg & 1;
         store_stage(buf, x);
         __syncthreads();
         load_stage(x);
+        if (!cp.live) return;                                   // uniform
         const uint16_t* sk = skv[buf][0];
         const uint16_t* sv = skv[buf][1];
-        const int nq = (exact_rows(a, cp.r) + 31) / 32;
+        const int nq = (cp.Br + 31) / 32;
         const int kvalid = (int)(cp.j1 - cp.j < TK ? cp.j1 - cp.j : TK);
 #pragma unroll
         for (int qt = 0; qt < NQ; ++qt) {
@@ -342,7 +360,7 @@ __global__ __launch_bounds__(256) void exact_slices_generic(ExactArgs a)
     const float sl2 = a.scale * 1.4426950408889634f;
     while (c.live) {
         const int64_t Pr = c.P;
-        const int Br = exact_rows(a, c.r);
+        const int Br = c.Br;
         const int64_t unit = (int64_t)c.r * a.heads + c.h;
         float* slotp = a.partial + ((int64_t)blockIdx.x + unit) * slot_floats;
         for (int e = threadIdx.x; e < Br * D; e += blockDim.x) {
@@ -350,10 +368,9 @@ __global__ __launch_bounds__(256) void exact_slices_generic(ExactArgs a)
             const T* qi = qa + (((int64_t)c.r * a.blk + i) * a.heads + c.h) * D;
             float m = -INFINITY, l = 0.f, acc = 0.f;
             for (int64_t j = c.j; j < c.j1; ++j) {
-                const T* kj = j < Pr ? kc + (c.p0 + j) * rs + (int64_t)c.h * D
-                                     : ka + (((int64_t)c.r * a.blk + (j - Pr)) * a.heads + c.h) * D;
-                const T* vj = j < Pr ? vc + (c.p0 + j) * rs + (int64_t)c.h * D
-                                     : va + (((int64_t)c.r * a.blk + (j - Pr)) * a.heads + c.h) * D;
+                const int64_t off = (j < Pr ? c.cbase : c.abase) + j * rs;
+                const T* kj = (j < Pr ? kc : ka) + off;
+                const T* vj = (j < Pr ? vc : va) + off;
                 float dot = 0.f;
                 for (int f = 0; f < D; ++f) dot = fmaf(Elem<T>::load(qi, f), Elem<T>::load(kj, f), dot);
                 const float x = sl2 * dot;
@@ -376,35 +393,51 @@ __global__ __launch_bounds__(256) void exact_slices_generic(ExactArgs a)
 
 // ---------------------------------------------------------------------------
 // Combine: out[i][c] = sum_w 2^(m_w - M) O_w[i][c] / sum_w 2^(m_w - M) l_w
-// over the unit's slices in ascending order, M = max_w m_w.  One workgroup
-// per unit; rows past B_r are not written.
+// over the unit's slices w in ascending order, M = max_w m_w.  One workgroup
+// per unit: the row maxima and normalisers first (one thread per row, into
+// LDS), then four adjacent columns per thread.  Rows past B_r are not
+// written.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void exact_combine(ExactArgs a)
 {
+    __shared__ float rowM[kMaxBlk], rowInv[kMaxBlk];
     const int r = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
     const int64_t nch = (a.plan[r + 1] - a.plan[r]) / a.heads;
-    if (nch <= 0) return;
-    const int D = a.d, Br = exact_rows(a, r);
+    if (nch <= 0) return;                       // uniform: no valid rows
+    const int D = a.d, Br = exact_rows<true>(a, r);
     const int RB = exact_slot_rows(a.blk);
-    const int slot_floats = RB * (D + 2);
+    const int64_t slot_floats = (int64_t)RB * (D + 2);
     const int64_t S = a.plan[a.n_req + 1];
     const int64_t cfirst = a.plan[r] + h * nch, clast = cfirst + nch - 1;
     const int64_t w0 = cfirst / S, w1 = clast / S;
     const int64_t unit = (int64_t)r * a.heads + h;
-    T* out = static_cast<T*>(a.out);
-    for (int e = threadIdx.x; e < Br * D; e += blockDim.x) {
-        const int i = e / D, col = e % D;
+    const float* p0 = a.partial + (w0 + unit) * slot_floats;
+    for (int i = threadIdx.x; i < Br; i += blockDim.x) {
         float M = -INFINITY;
-        for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, a.partial[(w + unit) * slot_floats + RB * D + i]);
-        float num = 0.f, den = 0.f;
-        for (int64_t w = w0; w <= w1; ++w) {
-            const float* sp = a.partial + (w + unit) * slot_floats;
+        for (int64_t w = 0; w <= w1 - w0; ++w) M = fmaxf(M, p0[w * slot_floats + RB * D + i]);
+        float den = 0.f;
+        for (int64_t w = 0; w <= w1 - w0; ++w)
+            den += exp2f(p0[w * slot_floats + RB * D + i] - M) * p0[w * slot_floats + RB * D + RB + i];
+        rowM[i] = M;
+        rowInv[i] = 1.f / den;
+    }
+    __syncthreads();
+    T* out = static_cast<T*>(a.out);
+    const int D4 = D / 4;
+    for (int e = threadIdx.x; e < Br * D4; e += blockDim.x) {
+        const int i = e / D4, c = 4 * (e % D4);
+        const float M = rowM[i];
+        f32x4 num = {};
+        for (int64_t w = 0; w <= w1 - w0; ++w) {
+            const float* sp = p0 + w * slot_floats;
             const float f = exp2f(sp[RB * D + i] - M);
-            num += f * sp[(int64_t)i * D + col];
-            den += f * sp[RB * D + RB + i];
+            const f32x4 o = *reinterpret_cast<const f32x4*>(sp + (int64_t)i * D + c);
+            num += f * o;
         }
-        Elem<T>::store(out, (((int64_t)r * a.blk + i) * a.heads + h) * D + col, num / den);
+        const int64_t o0 = (((int64_t)r * a.blk + i) * a.heads + h) * D + c;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Elem<T>::store(out, o0 + u, num[u] * rowInv[i]);
     }
 }
 

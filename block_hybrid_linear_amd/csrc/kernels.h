@@ -68,9 +68,17 @@ struct ExactArgs {
     bool dtype_bf16;
 };
 
-// Slice workgroups of the exact step (four per compute unit of an MI355X),
-// fixed so that results do not depend on the device.
-inline int exact_slices(int d) { (void)d; return 1024; }
+// Slice workgroups of the exact step: as many as the 256 compute units of an
+// MI355X hold at once for the matrix-core variant of (d, blk) -- its waves
+// per SIMD (3, 2, 1 for one, two, four query tiles) times 4 SIMDs over its
+// d / 32 waves per workgroup -- so the balanced split runs in one round.
+// Fixed per (d, blk), so results do not depend on the device.
+inline int exact_slices(int d, int blk)
+{
+    if (d != 32 && d != 64 && d != 128) return 1024;
+    const int waves_per_simd = blk <= 32 ? 3 : (blk <= 64 ? 2 : 1);
+    return 256 * waves_per_simd * 4 / (d / 32);
+}
 // Rows of one partial slot: the query rows of the kernel that runs for blk
 // (one, two or four 32-row tiles).  A slot holds rows x d unnormalised
 // outputs, then the running max and the running sum of each row.

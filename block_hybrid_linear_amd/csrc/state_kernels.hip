@@ -253,30 +253,35 @@ struct SliceCursor {
 
 __device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur)
 {
-    const int64_t C = a.plan[a.n_req], S = a.plan[a.n_req + 1];
+    const int64_t C = uniform_load(a.plan, a.n_req), S = uniform_load(a.plan, a.n_req + 1);
     cur.c0 = (int64_t)blockIdx.x * S;
     cur.c1 = cur.c0 + S < C ? cur.c0 + S : C;
     if (cur.c0 >= cur.c1) return false;
     int lo = 0, hi = a.n_req;                 // last r with plan[r] <= c0
     while (hi - lo > 1) {
         const int mid = (lo + hi) / 2;
-        if (a.plan[mid] <= cur.c0) lo = mid;
+        if (uniform_load(a.plan, mid) <= cur.c0) lo = mid;
         else hi = mid;
     }
     cur.r = lo;
     return true;
 }
 
-// Next piece of the slice: unit (r, h), token rows [t0, t1) of prompt r.
-__device__ __forceinline__ void slice_piece(const PhiKVArgs& a, SliceCursor& cur, int& h, int64_t& t0, int64_t& t1)
+// Next piece of the slice: unit (r, h), token rows [t0, t1) of prompt r,
+// whose first row starts at element p0 of k and v.
+__device__ __forceinline__ void slice_piece(const PhiKVArgs& a, SliceCursor& cur, int& h, int64_t& t0, int64_t& t1,
+                                            int64_t& p0)
 {
-    while (a.plan[cur.r + 1] <= cur.c0) ++cur.r;   // skip finished and empty prompts
-    const int64_t nch = (a.plan[cur.r + 1] - a.plan[cur.r]) / a.heads;
-    const int64_t local = cur.c0 - a.plan[cur.r];
+    while (uniform_load(a.plan, cur.r + 1) <= cur.c0) ++cur.r;   // skip finished and empty prompts
+    const int64_t pr = uniform_load(a.plan, cur.r);
+    const int64_t nch = (uniform_load(a.plan, cur.r + 1) - pr) / a.heads;
+    const int64_t local = cur.c0 - pr;
     h = (int)(local / nch);
     const int64_t k0 = local % nch;
     const int64_t k1 = (k0 + (cur.c1 - cur.c0) < nch) ? k0 + (cur.c1 - cur.c0) : nch;
-    const int64_t L = a.cu[cur.r + 1] - a.cu[cur.r];
+    const int64_t s0 = uniform_load(a.cu, cur.r);
+    const int64_t L = uniform_load(a.cu, cur.r + 1) - s0;
+    p0 = s0 * a.heads * a.d + (int64_t)h * a.d;
     t0 = k0 * a.chunk;
     t1 = k1 * a.chunk < L ? k1 * a.chunk : L;
     cur.c0 += k1 - k0;
@@ -288,6 +293,7 @@ struct StageCursor {
     SliceCursor sl;     // chunk position of the next piece
     int r, h;           // unit of the current piece
     int64_t t, t1;      // current stage's first row and the piece's end (rows of prompt r)
+    int64_t p0;         // element offset of the piece's prompt row 0, head h
     bool live;
 };
 
@@ -295,7 +301,7 @@ __device__ __forceinline__ void stage_next_piece(const PhiKVArgs& a, StageCursor
 {
     s.live = s.sl.c0 < s.sl.c1;
     if (!s.live) return;
-    slice_piece(a, s.sl, s.h, s.t, s.t1);
+    slice_piece(a, s.sl, s.h, s.t, s.t1, s.p0);
     s.r = s.sl.r;
 }
 
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_b
     // loads of the stage under the load cursor (rows past the piece re-read its
     // last row; a finished cursor re-reads the last row it had)
     auto load_stage = [&](u32x4 (&x)[8]) {
-        const uint16_t* src = tbase + a.cu[ld.r] * rs + (int64_t)ld.h * D;
+        const uint16_t* src = tbase + ld.p0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int64_t t = ld.t + tg * 8 + e;
@@ -386,14 +392,18 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_b
     load_stage(x1);
     load_stage(x2);
     int sg = 0;
-    // One stage: store the compute cursor's stage, issue the loads PF stages
-    // ahead, multiply, and flush the unit's partial state when its piece ends.
+    // One stage: store the compute cursor's stage, issue the loads three
+    // stages ahead, multiply, and flush the unit's partial state when its
+    // piece ends.  Staging and loads run on every path (past the end they
+    // repeat the last rows), so every path around the loop issues the three
+    // register sets' loads in the same order and each stage waits only for
+    // its own set; only the arithmetic is skipped past the end.
     auto run_stage = [&](u32x4 (&x)[8]) {
-        if (!cp.live) return;                  // uniform
         const int buf = sg & 1;
         store_stage(buf, cp.t1 - cp.t, x);
         __syncthreads();
         load_stage(x);
+        if (!cp.live) return;                  // uniform
         mma_stage(buf);
         ++sg;
         if (cp.t + T >= cp.t1) {
@@ -422,10 +432,10 @@ __global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
     const int64_t rs = (int64_t)a.heads * D;
     while (cur.c0 < cur.c1) {
         int h;
-        int64_t t0, t1;
-        slice_piece(a, cur, h, t0, t1);
-        const T* kb = static_cast<const T*>(a.k) + (a.cu[cur.r] + t0) * rs + (int64_t)h * D;
-        const T* vb = static_cast<const T*>(a.v) + (a.cu[cur.r] + t0) * rs + (int64_t)h * D;
+        int64_t t0, t1, p0;
+        slice_piece(a, cur, h, t0, t1, p0);
+        const T* kb = static_cast<const T*>(a.k) + p0 + t0 * rs;
+        const T* vb = static_cast<const T*>(a.v) + p0 + t0 * rs;
         float* dst = a.partial + ((int64_t)blockIdx.x + (int64_t)cur.r * a.heads + h) * D * D;
         for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
             const int c = e / D, f = e % D;

@@ -53,7 +53,10 @@
  * is enqueued, so outputs and the state are untouched.  hybrid_last_error()
  * gives a message for the calling thread's last non-OK status.
  *   HA_ERR_INVALID_ARG  NULL pointer, negative or zero size, blk > 128,
- *                       non-finite scale, chunk < 1, workspace too small.
+ *                       non-finite scale, chunk < 1, workspace too small,
+ *                       a q/k/v/out/state/cache pointer not 16-byte aligned
+ *                       or a workspace not 256-byte aligned (allocations
+ *                       from hipMalloc or torch satisfy both).
  *   HA_ERR_UNSUPPORTED  d not in {16, 32, 64, 128} or unknown dtype.
  *   HA_ERR_HIP          the kernel launch failed (hipGetLastError).
  * A call with n_req == 0 does nothing and returns HA_OK (pointers unused).
@@ -196,9 +199,10 @@ ha_status hybrid_exact_step(const void* q, const void* k, const void* v,
                             ha_dtype dtype, void* stream);
 
 /* Workspace size for hybrid_exact_step (host): a 256-byte-padded plan of
- * n_req + 2 int64, then (1024 + n_req * heads) partials of R * (d + 2)
- * floats, R = 32, 64 or 128 for blk <= 32, <= 64 or <= 128.  0 for empty or
- * invalid sizes. */
+ * n_req + 2 int64, then (W + n_req * heads) partials of R * (d + 2) floats,
+ * R = 32, 64 or 128 for blk <= 32, <= 64 or <= 128, and W the number of
+ * slice workgroups: 256 * (3, 2 or 1 for the same blk ranges) * 4 / (d / 32)
+ * for d >= 32, 1024 for d = 16.  0 for empty or invalid sizes. */
 size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads,
                                          int32_t blk, int32_t d);
 

@@ -147,6 +147,30 @@ def test_exact_rejects(lib, kw, status, msg):
     assert msg in last(lib) and "hybrid_exact_step" in last(lib)
 
 
+A = 1 << 12   # a fake, suitably aligned device address (never dereferenced: the calls fail validation)
+
+
+@pytest.mark.parametrize("call,kw,msg", [
+    ("step", dict(q=A + 2), "16-byte"),
+    ("step", dict(state=A + 8), "16-byte"),
+    ("commit", dict(v=A + 4), "16-byte"),
+    ("prefill", dict(k=A + 8), "16-byte"),
+    ("prefill", dict(ws=A + 16), "256-byte"),
+    ("exact", dict(vc=A + 2), "16-byte"),
+    ("exact", dict(out=A + 8), "16-byte"),
+    ("exact", dict(ws=A + 128), "256-byte"),
+])
+def test_misaligned_pointers_rejected(lib, call, kw, msg):
+    fn = {"step": step, "commit": commit, "prefill": prefill, "exact": exact}[call]
+    base = {"step": dict(q=A, k=A, v=A, state=A, slots=A, out=A),
+            "commit": dict(k=A, v=A, state=A, slots=A),
+            "prefill": dict(k=A, v=A, cu=A, state=A, slots=A, ws=A),
+            "exact": dict(q=A, k=A, v=A, kc=A, vc=A, cu=A, out=A, ws=A)}[call]
+    base.update(kw)
+    assert fn(lib, **base) == binding.HA_ERR_INVALID_ARG
+    assert msg in last(lib)
+
+
 def test_empty_batches_are_noops(lib):
     """n_req == 0 returns OK without touching any pointer (all NULL here)."""
     assert step(lib, q=None, k=None, v=None, state=None, slots=None, out=None, n_req=0) == binding.HA_OK
@@ -171,15 +195,18 @@ def test_prefill_workspace_size(lib):
 
 
 def test_exact_workspace_size(lib):
-    """Plan as for prefill + (1024 + n_req * heads) partials of R rows x
+    """Plan as for prefill + (slices + n_req * heads) partials of R rows x
     (d + 2) floats (output row, max, sum), R = 32 / 64 / 128 for blk up to
-    32 / 64 / 128."""
+    32 / 64 / 128; slices = 256 x (3, 2, 1 waves per SIMD) x 4 / (d / 32)
+    for d >= 32, else 1024."""
     f = bh.hybrid_exact_step_workspace_bytes
     plan = lambda n: ((n + 2) * 8 + 255) // 256 * 256  # noqa: E731
-    assert f(64, 32, 32, 128) == plan(64) + (1024 + 2048) * 32 * 130 * 4
+    assert f(64, 32, 32, 128) == plan(64) + (768 + 2048) * 32 * 130 * 4
     assert f(3, 5, 33, 16) == plan(3) + (1024 + 15) * 64 * 18 * 4
     assert f(2, 3, 65, 32) == plan(2) + (1024 + 6) * 128 * 34 * 4
-    assert f(1, 1, 128, 64) == plan(1) + (1024 + 1) * 128 * 66 * 4
+    assert f(1, 1, 128, 64) == plan(1) + (512 + 1) * 128 * 66 * 4
+    assert f(5, 2, 40, 64) == plan(5) + (1024 + 10) * 64 * 66 * 4
+    assert f(5, 2, 8, 32) == plan(5) + (3072 + 10) * 32 * 34 * 4
     assert f(0, 1, 32, 64) == 0 and f(2, 2, 0, 64) == 0 and f(2, 2, 129, 64) == 0
 
 

@@ -11,15 +11,17 @@ resident in HBM before timing; each step's Q/K/V are distinct tensors.
 
 Reported value: tokens/s through the hybrid layer, where a prompt token
 counts once (folded into S) and an active-block token counts once per
-denoising step.  Per-call HIP-event timings inside the timed region give each
-kernel's achieved GB/s and TFLOP/s against the MI355X peaks (8 TB/s HBM,
-2.5 PFLOP/s dense bf16); ``roofline`` reports the call with the largest share
-of the time.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample
+denoising step.  The timed steps replay the step's calls captured once as a
+HIP graph (``--eager`` times the calls launched one by one instead).  K eager
+steps with HIP events around every call, on the stream the kernels run on,
+give each call's achieved GB/s and TFLOP/s against the MI355X peaks (8 TB/s
+HBM, 2.5 PFLOP/s dense bf16); ``roofline`` reports the call with the largest
+share of the time.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample
 of the same workload's (request, head) units and scales it to tokens/s.
 ``context`` times, for comparison only, the hybrid step against the exact
 full-prefix step it replaces at the concurrent-serving shapes.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-context]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu] [--no-context]
 """
 from __future__ import annotations
 
@@ -86,7 +88,6 @@ class Job:
         n, H, d, B = wl.n_req, wl.heads, wl.d, wl.blk
         self.slots = torch.arange(n, dtype=torch.int32, device=dev)
         self.state = torch.zeros(n, H, d, d, device=dev)
-        self.calls = []          # (kind, fn)
         self.tokens = 0
         self.cost = {}           # kind -> (bytes, flops) per call
         if wl.prompt_range:
@@ -101,7 +102,6 @@ class Job:
             self.ws = torch.empty(max(1, bh.hybrid_state_prefill_workspace_bytes(n, H, d, total, self.max_len,
                                                                                   wl.chunk)),
                                   dtype=torch.uint8, device=dev)
-            self.calls.append(("prefill", self._prefill))
             self.tokens += total
             self.cost["prefill"] = prefill_cost(total * H, n * H, d)
         self.q, self.k, self.v = [], [], []
@@ -111,38 +111,38 @@ class Job:
                 self.q.append(synth.normal((n, B, H, d), s(0), std=wl.std, device=dev))
                 self.k.append(synth.normal((n, B, H, d), s(1), std=wl.std, device=dev))
                 self.v.append(synth.normal((n, B, H, d), s(2), std=wl.std, device=dev))
+                self.tokens += n * B
         self.out = torch.empty(n, B, H, d, dtype=torch.bfloat16, device=dev)
+        self.cost["step"] = step_cost(n * H, B, d)
+        self.cost["commit"] = commit_cost(n * H, B, d)
+        self.calls = self.prepare(None)
+
+    def prepare(self, stream):
+        """The step's calls, each validated and marshalled once and re-enqueued
+        with one ctypes call (as a serving loop would), on `stream` (None =
+        the current stream)."""
+        wl = self.wl
+        calls = []
+        if wl.prompt_range:
+            calls.append(("prefill", bh.prepare_prefill(self.pk, self.pv, self.cu, self.state, self.slots,
+                                                        max_len=self.max_len, chunk=wl.chunk, workspace=self.ws,
+                                                        stream=stream)))
         i = 0
         for b in range(wl.n_blocks):
             for t in range(wl.steps_per_block):
-                self.calls.append(("step", self._step_fn(i)))
-                self.tokens += n * B
+                calls.append(("step", bh.prepare_step(self.q[i], self.k[i], self.v[i], self.state, self.slots,
+                                                      self.out, scale=wl.scale, stream=stream)))
                 i += 1
-            if wl.n_blocks > 1 or wl.steps_per_block > 1:
-                self.calls.append(("commit", self._commit_fn(i - 1)))   # the block's last step's K, V
-        self.cost["step"] = step_cost(n * H, B, d)
-        self.cost["commit"] = commit_cost(n * H, B, d)
-
-    # Calls are prepared once (validated and marshalled) and re-enqueued with
-    # one ctypes call each, as a serving loop would.
-    def _prefill(self):
-        if not hasattr(self, "_prefill_call"):
-            self._prefill_call = bh.prepare_prefill(self.pk, self.pv, self.cu, self.state, self.slots,
-                                                    max_len=self.max_len, chunk=self.wl.chunk, workspace=self.ws)
-        self._prefill_call()
-
-    def _step_fn(self, i):
-        return bh.prepare_step(self.q[i], self.k[i], self.v[i], self.state, self.slots, self.out,
-                               scale=self.wl.scale)
-
-    def _commit_fn(self, i):
-        return bh.prepare_commit(self.k[i], self.v[i], self.state, self.slots)
+            if wl.n_blocks > 1 or wl.steps_per_block > 1:     # commit the block's last step's K, V
+                calls.append(("commit", bh.prepare_commit(self.k[i - 1], self.v[i - 1], self.state, self.slots,
+                                                          stream=stream)))
+        return calls
 
     def reset(self):
         self.state.zero_()
 
-    def run(self, events=None):
-        for kind, fn in self.calls:
+    def run(self, events=None, calls=None):
+        for kind, fn in (calls or self.calls):
             if events is not None:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
@@ -151,6 +151,22 @@ class Job:
                 events.append((kind, e0, e1))
             else:
                 fn()
+
+    def capture(self):
+        """The whole step captured once as a HIP graph (every kernel of every
+        call; no allocation, copy or memset inside)."""
+        side = torch.cuda.Stream()
+        calls = self.prepare(side)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run(calls=calls)                 # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            self.run(calls=calls)
+        torch.cuda.synchronize()
+        return g
 
 
 # ---------------------------------------------------------------------------
@@ -302,6 +318,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=PREFILL_DECODE.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the eager calls instead of replays of the step captured as a HIP graph")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the hybrid-vs-exact step timing at the serving shapes")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle time")
@@ -336,9 +354,10 @@ def main():
         job.run()
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps, per-call events recorded on the stream
+    # ---- per-call timings: K eager steps with HIP events around every call,
+    # on the stream the kernels run on
     events = []
-    step_ms = []
+    eager_ms = []
     for s in range(args.steps):
         job.reset()                       # a fresh generation; not inside the timed interval
         torch.cuda.synchronize()
@@ -347,10 +366,36 @@ def main():
         job.run(events)
         b.record()
         torch.cuda.synchronize()
-        step_ms.append(a.elapsed_time(b))
-        log(f"[bench] step {s}: {step_ms[-1]:.3f} ms")
+        eager_ms.append(a.elapsed_time(b))
+        log(f"[bench] eager step {s}: {eager_ms[-1]:.3f} ms")
+
+    # ---- timed region: K whole steps, each the step's calls replayed as one
+    # captured HIP graph (the same kernels and arguments, without per-launch
+    # host overhead), bracketed by synchronisations
+    step_ms = eager_ms
+    mode = "eager"
+    if not args.eager:
+        g = job.capture()
+        for _ in range(args.warmup):
+            job.reset()
+            g.replay()
+        torch.cuda.synchronize()
+        step_ms = []
+        mode = "hip_graph"
+        for s in range(args.steps):
+            job.reset()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            step_ms.append(a.elapsed_time(b))
+            log(f"[bench] graph step {s}: {step_ms[-1]:.3f} ms")
+        del g
     total_ms = sum(step_ms)
     ms_per_step = total_ms / args.steps
+    eager_ms_per_step = sum(eager_ms) / args.steps
 
     kernels = {}
     for kind in job.cost:
@@ -365,7 +410,7 @@ def main():
                          "alg_bytes": byts, "alg_flops": flops, "GBps": round(gbs, 1),
                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOPs": round(tfs, 2),
                          "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 5),
-                         "share_of_step": round(avg_ms * len(ts) / args.steps / ms_per_step, 4)}
+                         "share_of_step": round(avg_ms * len(ts) / args.steps / eager_ms_per_step, 4)}
     dom = max(kernels, key=lambda k: kernels[k]["share_of_step"])
     kd = kernels[dom]
     traffic = measured_traffic(dom, wl.name)
@@ -384,6 +429,8 @@ def main():
                    "qkv_std": wl.std, "tokens_per_step": job.tokens, "parallelism": "single_gpu",
                    "source_digest": source_digest()},
         "roofline": roofline,
+        "timing": {"mode": mode, "eager_ms_per_step": round(eager_ms_per_step, 4),
+                   "kernels_from": "HIP events around each call of the eager steps"},
         "kernels": kernels,
     }
     if not args.no_context:

@@ -8,11 +8,17 @@
 namespace ha {
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core step, head dim D in {32, 64, 128}, blk <= 32 * NQ.
+// bf16 matrix-core step, head dim D in {32, 64, 128}, blk <= 32 * NKT.
 //
-// One workgroup per (request, head) with D/32 waves; wave ct owns value
-// columns [32 ct, 32 ct + 32) for all NQ query tiles of 32 rows, so each
-// wave reads its S^T tile exactly once and splits it into hi/lo bf16 once.
+// One workgroup per (request, head, 32-query tile) with D/32 waves; wave ct
+// owns value columns [32 ct, 32 ct + 32) of the tile's queries, so each wave
+// reads its S^T tile once and splits it into hi/lo bf16 once.  A block of
+// more than 32 rows is split over NKT workgroups (one per query tile) so that
+// small batches still put several workgroups on every compute unit; the
+// workgroups of one (request, head) are numbered so that they land on the
+// same XCD (workgroups are dealt to the 8 XCDs round-robin), where the second
+// read of the unit's S, K and V hits that XCD's L2.
+//
 // Everything is computed transposed so that each lane ends up holding one
 // query row:
 //   L^T = K Q^T          (keys x queries): lane l holds query i = l % 32 and
@@ -26,16 +32,15 @@ namespace ha {
 // bf16 matrix cores as hi + lo bf16 pairs (two passes), which keeps ~16
 // mantissa bits; Q, K, V are bf16 already, so their products are exact.
 //
-// Q, K and V are staged once per workgroup in LDS (row-major, 16-byte pad):
-// every wave loads an equal slice with 16-byte coalesced loads, so each byte
-// is fetched once.  Matrix-core operands of Q and K are then one 16-byte LDS
-// read each; V^T operands use the gfx950 transposing LDS read
-// (ds_read_b64_tr_b16), which hands each lane four consecutive rows of one
-// column.  Rows past B_r are clamped to row B_r - 1 (masked out of the
-// softmax), so every global load is unconditional; they are issued in the
-// order Q/K/V slices, then the wave's S tile, and the scheduler is fenced so
-// the S stream -- two thirds of the bytes -- is in flight while the softmax
-// part is computed.
+// The query tile and all key/value rows are staged once per workgroup in LDS
+// (row-major, 16-byte pad) with 16-byte coalesced loads.  Matrix-core operands
+// of Q and K are then one 16-byte LDS read each; V^T operands use the gfx950
+// transposing LDS read (ds_read_b64_tr_b16), which hands each lane four
+// consecutive rows of one column.  Rows past B_r are clamped to row B_r - 1
+// (masked out of the softmax), so every global load is unconditional; they
+// are issued in the order Q/K/V, then the wave's S tile, and the scheduler is
+// fenced so the S stream -- most of the bytes -- is in flight while the
+// softmax part is computed.
 //
 // Value-column permutation: the A-operand row m of tile ct maps to column
 //   c(m) = 32 ct + 16 * ((m / 4) % 2) + 4 * (m / 8) + m % 4,
@@ -53,26 +58,33 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-template <int D, int NQ>
+// Workgroups per XCD group: the NKT query tiles of 8 consecutive units.
+__host__ __device__ inline int step_grid(int units, int nkt) { return (units + 7) / 8 * 8 * nkt; }
+
+template <int D, int NKT>
 __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;              // k-steps over the head dimension
     constexpr int NC = D / 32;              // value-column tiles = waves
-    constexpr int NKT = NQ;                 // key tiles (keys = queries = block rows)
     constexpr int NT = NC * kWave;          // threads
-    constexpr int R = NQ * 32;              // staged rows
+    constexpr int RK = NKT * 32;            // staged key / value rows
     constexpr int P = D + 8;                // LDS row pitch (bf16)
     constexpr int CPR = D / 8;              // 16-byte chunks per row
-    constexpr int CPT = R * CPR / NT;       // chunks per thread per tensor
-    static_assert(CPT * NT == R * CPR, "even staging split");
-    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
+    constexpr int CQ = 32 * CPR / NT;       // Q chunks per thread
+    constexpr int CK = RK * CPR / NT;       // K (and V) chunks per thread
+    static_assert(CQ * NT == 32 * CPR && CK * NT == RK * CPR, "even staging split");
+    __shared__ __attribute__((aligned(16))) uint16_t sq[32 * P], sk[RK * P], sv[RK * P];
 
-    const int unit = blockIdx.x;
+    // workgroup -> (unit, query tile): the NKT tiles of a unit share b % 8
+    const int b = blockIdx.x;
+    const int qt = (b / 8) % NKT;
+    const int unit = b / (8 * NKT) * 8 + b % 8;
+    if (unit >= a.n_req * a.heads) return;
     const int r = unit / a.heads, h = unit % a.heads;
     int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
     Br = Br > a.blk ? a.blk : Br;
     const int slot = a.slots[r];
-    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
+    if (Br <= qt * 32 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave, ct = tid / kWave;
@@ -91,12 +103,15 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     const float sl2 = a.scale * 1.4426950408889634f;         // logits in log2 units
 
     // ---- global loads: this thread's Q/K/V chunks, then the wave's S^T tile
-    u32x4 cq[CPT], ck[CPT], cv[CPT];
+    u32x4 cq[CQ], ck[CK], cv[CK];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
+    for (int u = 0; u < CK; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        if (u < CQ) {
+            const int rq = qt * 32 + row;
+            cq[u] = *reinterpret_cast<const u32x4*>(q + (int64_t)(rq < Br ? rq : last) * rs + c8);
+        }
         const int64_t off = (int64_t)(row < Br ? row : last) * rs + c8;
-        cq[u] = *reinterpret_cast<const u32x4*>(q + off);
         ck[u] = *reinterpret_cast<const u32x4*>(k + off);
         cv[u] = *reinterpret_cast<const u32x4*>(v + off);
     }
@@ -111,123 +126,112 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     // whole wave's bytes must be in flight before the first wait
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
+    for (int u = 0; u < CK; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
-        *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
+        if (u < CQ) *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
         *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
         *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
     }
     __syncthreads();
 
-    // ---- softmax part for every query tile (overlaps the S stream):
-    //      L^T = K Q^T, row softmax, O^T = V^T P^T (P as hi + lo bf16)
+    // ---- softmax part (overlaps the S stream): L^T = K Q^T, row softmax,
+    //      O^T = V^T P^T (P as hi + lo bf16)
     const int g = lane / 16, jl = lane % 16;
     const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
-    f32x16 o[NQ];
+    f32x16 o = {};
+    const uint16_t* qr = sq + l32 * P + 8 * hh;
+    f32x16 lt[NKT];
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
-        o[qt] = f32x16{};
-        if (qt >= nkt) continue;
-        const uint16_t* qr = sq + (qt * 32 + l32) * P + 8 * hh;
-        f32x16 lt[NKT];
+    for (int jt = 0; jt < NKT; ++jt) {
+        f32x16 acc = {};
+        if (jt < nkt) {
+            const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
 #pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
-            f32x16 acc = {};
-            if (jt < nkt) {
-                const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
-                                 as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), acc);
-            }
-            lt[jt] = acc;
+            for (int s = 0; s < KS; ++s)
+                acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
+                             as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), acc);
         }
-        // row softmax over the Br valid keys (one query per lane pair)
-        float m = -INFINITY;
+        lt[jt] = acc;
+    }
+    // row softmax over the Br valid keys (one query per lane pair)
+    float m = -INFINITY;
 #pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
+    for (int jt = 0; jt < NKT; ++jt) {
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-                const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
-                lt[jt][rr] = x;
-                m = fmaxf(m, x);
-            }
+        for (int rr = 0; rr < 16; ++rr) {
+            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+            const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
+            lt[jt][rr] = x;
+            m = fmaxf(m, x);
         }
-        m = fmaxf(m, __shfl_xor(m, 32));
-        float sum = 0.f;
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float sum = 0.f;
 #pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
+    for (int jt = 0; jt < NKT; ++jt) {
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const float p = __builtin_amdgcn_exp2f(lt[jt][rr] - m);   // exp2(-inf) = 0 for masked keys
-                lt[jt][rr] = p;
-                sum += p;
-            }
+        for (int rr = 0; rr < 16; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(lt[jt][rr] - m);   // exp2(-inf) = 0 for masked keys
+            lt[jt][rr] = p;
+            sum += p;
         }
-        sum += __shfl_xor(sum, 32);
-        const float inv = __builtin_amdgcn_rcpf(sum);
-        // V^T operand of k-step (jt, gp): keys jt*32 + 16gp + 4hh + {0..3} and the
-        // same + 8, matching registers 8gp .. 8gp+7 of L^T; the column of lane i in
-        // 16-lane group g is 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4, q = i/4 (= cA).
+    }
+    sum += __shfl_xor(sum, 32);
+    const float inv = __builtin_amdgcn_rcpf(sum);
+    // V^T operand of k-step (jt, gp): keys jt*32 + 16gp + 4hh + {0..3} and the
+    // same + 8, matching registers 8gp .. 8gp+7 of L^T; the column of lane i in
+    // 16-lane group g is 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4, q = i/4 (= cA).
 #pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
-            if (jt < nkt) {
+    for (int jt = 0; jt < NKT; ++jt) {
+        if (jt < nkt) {
 #pragma unroll
-                for (int gp = 0; gp < 2; ++gp) {
-                    const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-                    const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-                    const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
-                    u16x8 vop;
+            for (int gp = 0; gp < 2; ++gp) {
+                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+                u16x8 vop;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        vop[e] = static_cast<uint16_t>(v0[e]);
-                        vop[4 + e] = static_cast<uint16_t>(v1[e]);
-                    }
-                    float pp[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
-                    bf16x8 phi, plo;
-                    split_hi_lo(pp, phi, plo);
-                    o[qt] = mfma32(as_bf16x8(vop), phi, o[qt]);
-                    o[qt] = mfma32(as_bf16x8(vop), plo, o[qt]);
+                for (int e = 0; e < 4; ++e) {
+                    vop[e] = static_cast<uint16_t>(v0[e]);
+                    vop[4 + e] = static_cast<uint16_t>(v1[e]);
                 }
+                float pp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
+                bf16x8 phi, plo;
+                split_hi_lo(pp, phi, plo);
+                o = mfma32(as_bf16x8(vop), phi, o);
+                o = mfma32(as_bf16x8(vop), plo, o);
             }
         }
     }
-    // ---- linear part: O^T += S^T phi(Q)^T for every query tile, S as hi + lo
-    // bf16 split once and reused across the query tiles
+    // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16 (fenced so its
+    // phi(Q) operand reads are not hoisted into the softmax part, where the
+    // logits already occupy the registers)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const float sv8[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
                               sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
         bf16x8 shi, slo;
         split_hi_lo(sv8, shi, slo);
-#pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) {
-            if (qt < nkt) {
-                const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
-                const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-                o[qt] = mfma32(shi, pq, o[qt]);
-                o[qt] = mfma32(slo, pq, o[qt]);
-            }
-        }
+        const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + l32 * P + 16 * s + 8 * hh);
+        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
+        o = mfma32(shi, pq, o);
+        o = mfma32(slo, pq, o);
     }
-    // ---- store: lane holds query i, columns 32 ct + 16 hh + 0..15
+    // ---- store: lane holds query qt*32 + l32, columns 32 ct + 16 hh + 0..15
+    const int i = qt * 32 + l32;
+    if (i < Br) {
+        u16x8 o0, o1;
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
-        const int i = qt * 32 + l32;
-        if (qt < nkt && i < Br) {
-            u16x8 o0, o1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o0[e] = f32_to_bf16_bits(o[qt][e]);
-                o1[e] = f32_to_bf16_bits(o[qt][8 + e]);
-            }
-            u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
-            op[0] = o0;
-            op[1] = o1;
+        for (int e = 0; e < 8; ++e) {
+            o0[e] = f32_to_bf16_bits(o[e]);
+            o1[e] = f32_to_bf16_bits(o[8 + e]);
         }
+        u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
+        op[0] = o0;
+        op[1] = o1;
     }
 }
 
@@ -412,8 +416,8 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
 template <int D>
 static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
 {
-    if (a.blk <= 32) step_bf16_mfma<D, 1><<<units, D / 32 * kWave, 0, stream>>>(a);
-    else if (a.blk <= 64) step_bf16_mfma<D, 2><<<units, D / 32 * kWave, 0, stream>>>(a);
+    if (a.blk <= 32) step_bf16_mfma<D, 1><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
+    else if (a.blk <= 64) step_bf16_mfma<D, 2><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
     else step_bf16_mfma_long<D><<<units, 4 * D / 32 * kWave, 0, stream>>>(a);
 }
 

@@ -5,8 +5,9 @@ One bench step is one pass of the whole hot path over one batch of synthetic
 input -- the long-prompt prefill + decode workload of one hybrid layer, all
 heads: 8 requests x 32 heads x d = 128 with ragged prompts of 16k-64k tokens
 (bf16, N(0,1)) folded into the fp32 state by hybrid_state_prefill (chunk
-256), then 16 blocks of B = 64 tokens, each denoised by 4 hybrid_attn_step
-calls and committed by one hybrid_state_commit.  Inputs are generated and
+256), then 16 blocks of B = 64 tokens, each denoised by 3 hybrid_attn_step
+calls and a last step fused with the block's commit
+(hybrid_attn_step_commit).  Inputs are generated and
 resident in HBM before timing; each step's Q/K/V are distinct tensors.
 
 Reported value: tokens/s through the hybrid layer, where a prompt token
@@ -64,6 +65,11 @@ def commit_cost(units, B, d, e=2):
     return units * (2 * B * d * e + 2 * d * d * 4), units * (2 * B * d * d)
 
 
+def step_commit_cost(units, B, d, e=2):
+    """Step and commit in one pass: Q/K/V and S read once, O and S written."""
+    return units * (4 * B * d * e + 2 * d * d * 4), units * (4 * B * B * d + 4 * B * d * d)
+
+
 def prefill_cost(token_heads, units, d, e=2):
     return token_heads * 2 * d * e + units * d * d * 4, token_heads * 2 * d * d
 
@@ -114,7 +120,7 @@ class Job:
                 self.tokens += n * B
         self.out = torch.empty(n, B, H, d, dtype=torch.bfloat16, device=dev)
         self.cost["step"] = step_cost(n * H, B, d)
-        self.cost["commit"] = commit_cost(n * H, B, d)
+        self.cost["step_commit"] = step_commit_cost(n * H, B, d)
         self.calls = self.prepare(None)
 
     def prepare(self, stream):
@@ -127,15 +133,19 @@ class Job:
             calls.append(("prefill", bh.prepare_prefill(self.pk, self.pv, self.cu, self.state, self.slots,
                                                         max_len=self.max_len, chunk=wl.chunk, workspace=self.ws,
                                                         stream=stream)))
+        commits = wl.n_blocks > 1 or wl.steps_per_block > 1
         i = 0
         for b in range(wl.n_blocks):
             for t in range(wl.steps_per_block):
-                calls.append(("step", bh.prepare_step(self.q[i], self.k[i], self.v[i], self.state, self.slots,
-                                                      self.out, scale=wl.scale, stream=stream)))
+                if commits and t == wl.steps_per_block - 1:
+                    # the block's last step, fused with the commit of its K, V
+                    calls.append(("step_commit", bh.prepare_step_commit(
+                        self.q[i], self.k[i], self.v[i], self.state, self.slots, self.out, scale=wl.scale,
+                        stream=stream)))
+                else:
+                    calls.append(("step", bh.prepare_step(self.q[i], self.k[i], self.v[i], self.state, self.slots,
+                                                          self.out, scale=wl.scale, stream=stream)))
                 i += 1
-            if wl.n_blocks > 1 or wl.steps_per_block > 1:     # commit the block's last step's K, V
-                calls.append(("commit", bh.prepare_commit(self.k[i - 1], self.v[i - 1], self.state, self.slots,
-                                                          stream=stream)))
         return calls
 
     def reset(self):
@@ -218,7 +228,8 @@ def cpu_baseline(job: Job, budget_s: float) -> dict:
 # was taken on (profiles/traffic.md holds one line per kernel)
 # ---------------------------------------------------------------------------
 
-KERNEL_SOURCES = {"step": "step_kernels.hip", "commit": "state_kernels.hip", "prefill": "state_kernels.hip",
+KERNEL_SOURCES = {"step": "step_kernels.hip", "step_commit": "step_kernels.hip", "commit": "state_kernels.hip",
+                  "prefill": "state_kernels.hip",
                   "exact": "exact_kernels.hip"}
 
 

@@ -10,6 +10,7 @@ with the same names:
     hybrid_attn_step      one denoising step of a hybrid layer
     hybrid_state_commit   S += ReLU(K_blk)^T V_blk when a block is finished
     hybrid_state_prefill  S = sum over a prompt of ReLU(k)^T v
+    hybrid_attn_step_commit  a block's last step fused with its commit
 
 and, for comparison, the exact step the method replaces:
 
@@ -18,12 +19,12 @@ and, for comparison, the exact step the method replaces:
 
 PyTorch only provides device memory and streams.
 """
-from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_exact_step,
+from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_attn_step_commit, hybrid_exact_step,
                       hybrid_exact_step_workspace_bytes, hybrid_state_commit, hybrid_state_prefill,
                       hybrid_state_prefill_workspace_bytes, load_library, prepare_commit, prepare_exact_step,
-                      prepare_prefill, prepare_step)
+                      prepare_prefill, prepare_step, prepare_step_commit)
 
-__all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_exact_step",
+__all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_attn_step_commit", "hybrid_exact_step",
            "hybrid_exact_step_workspace_bytes", "hybrid_state_commit", "hybrid_state_prefill",
            "hybrid_state_prefill_workspace_bytes", "load_library", "prepare_commit", "prepare_exact_step",
-           "prepare_prefill", "prepare_step"]
+           "prepare_prefill", "prepare_step", "prepare_step_commit"]

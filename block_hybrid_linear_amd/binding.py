@@ -43,6 +43,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         lib.hybrid_attn_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, ctypes.c_int, vp]
         lib.hybrid_state_commit.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+        lib.hybrid_attn_step_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                                ctypes.c_int, vp]
         lib.hybrid_state_prefill.argtypes = [vp, vp, vp, i64, i64, vp, vp, i32, i32, i32, i32, i32, vp, sz,
                                              ctypes.c_int, vp]
         lib.hybrid_state_prefill_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32]
@@ -51,7 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           ctypes.c_int, vp]
         lib.hybrid_exact_step_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.hybrid_exact_step_workspace_bytes.restype = sz
-        for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill, lib.hybrid_exact_step):
+        for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill, lib.hybrid_exact_step,
+                   lib.hybrid_attn_step_commit):
             fn.restype = ctypes.c_int
         lib.hybrid_last_error.argtypes = []
         lib.hybrid_last_error.restype = ctypes.c_char_p
@@ -139,6 +142,29 @@ def prepare_step(q, k, v, state, slots, out, blk_lens=None, scale=None, stream=N
         st = fn(*args)
         if st != HA_OK:
             _check("hybrid_attn_step", st)
+    return run
+
+
+def hybrid_attn_step_commit(q, k, v, state, slots, out=None, blk_lens=None, scale=None, stream=None):
+    """The step from the current state (as hybrid_attn_step), then
+    state[slots] += ReLU(K)^T V in the same pass: the last denoising step of a
+    block fused with its commit.  Requests must use distinct slots."""
+    if out is None:
+        out = torch.zeros_like(q)
+    args = _step_args(q, k, v, state, slots, out, blk_lens, scale)
+    _check("hybrid_attn_step_commit", load_library().hybrid_attn_step_commit(*args, _stream(stream)))
+    return out
+
+
+def prepare_step_commit(q, k, v, state, slots, out, blk_lens=None, scale=None, stream=None):
+    """Prepared form of hybrid_attn_step_commit (see prepare_step)."""
+    args = _step_args(q, k, v, state, slots, out, blk_lens, scale) + (_stream(stream),)
+    fn = load_library().hybrid_attn_step_commit
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_attn_step_commit", st)
     return run
 
 

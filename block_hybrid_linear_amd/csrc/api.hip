@@ -87,9 +87,27 @@ ha_status hybrid_attn_step(const void* q, const void* k, const void* v, const fl
     if (!q || !k || !v || !state || !slots || !out)
         return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state, slots and out must be non-NULL", fn);
     if ((st = check_aligned(fn, {q, k, v, state, out}, nullptr)) != HA_OK) return st;
-    ha::StepArgs a{q, k, v, state, slots, out, blk_lens, n_req, n_slots, heads, blk, d, scale,
+    ha::StepArgs a{q, k, v, state, nullptr, slots, out, blk_lens, n_req, n_slots, heads, blk, d, scale,
                    dtype == HA_BF16};
     return hip_status(ha::launch_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v, float* state,
+                                  const int32_t* slots, void* out, const int32_t* blk_lens,
+                                  int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
+                                  float scale, ha_dtype dtype, void* stream)
+{
+    static const char* fn = "hybrid_attn_step_commit";
+    ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
+    if (st != HA_OK) return st;
+    if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    if (n_req == 0) return HA_OK;
+    if (!q || !k || !v || !state || !slots || !out)
+        return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state, slots and out must be non-NULL", fn);
+    if ((st = check_aligned(fn, {q, k, v, state, out}, nullptr)) != HA_OK) return st;
+    ha::StepArgs a{q, k, v, state, state, slots, out, blk_lens, n_req, n_slots, heads, blk, d, scale,
+                   dtype == HA_BF16};
+    return hip_status(ha::launch_step_commit(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 ha_status hybrid_state_commit(const void* k, const void* v, float* state, const int32_t* slots,

@@ -11,6 +11,7 @@ struct StepArgs {
     const void* k;
     const void* v;
     const float* state;
+    float* state_rw;            // fused step + commit: the same store, updated in place
     const int32_t* slots;
     void* out;
     const int32_t* blk_lens;
@@ -86,6 +87,7 @@ __host__ __device__ inline int exact_slot_rows(int blk) { return blk <= 32 ? 32 
 inline int exact_slot_floats(int blk, int d) { return exact_slot_rows(blk) * (d + 2); }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream);
 hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream);
 hipError_t launch_exact(const ExactArgs& a, hipStream_t stream);

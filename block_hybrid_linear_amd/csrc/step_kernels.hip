@@ -58,6 +58,87 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// Softmax part of one 32-query tile whose rows start at qtile in LDS:
+// L^T = K Q^T over the key tiles, row softmax over the Br valid keys (one
+// query per lane pair), O^T = V^T P^T with P as hi + lo bf16.  Returns the
+// wave's accumulator (value columns of tile ct, transposed).
+template <int D, int NKT>
+__device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint16_t* sk, const uint16_t* sv,
+                                               int Br, int nkt, float sl2, int ct, int lane)
+{
+    constexpr int KS = D / 16, P = D + 8;
+    const int l32 = lane % 32, hh = lane / 32;
+    const int g = lane / 16, jl = lane % 16;
+    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
+    f32x16 o = {};
+    const uint16_t* qr = qtile + l32 * P + 8 * hh;
+    f32x16 lt[NKT];
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+        f32x16 acc = {};
+        if (jt < nkt) {
+            const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
+                             as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), acc);
+        }
+        lt[jt] = acc;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+            const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
+            lt[jt][rr] = x;
+            m = fmaxf(m, x);
+        }
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float sum = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(lt[jt][rr] - m);   // exp2(-inf) = 0 for masked keys
+            lt[jt][rr] = p;
+            sum += p;
+        }
+    }
+    sum += __shfl_xor(sum, 32);
+    const float inv = __builtin_amdgcn_rcpf(sum);
+    // V^T operand of k-step (jt, gp): keys jt*32 + 16gp + 4hh + {0..3} and the
+    // same + 8, matching registers 8gp .. 8gp+7 of L^T; the column of lane i in
+    // 16-lane group g is 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4, q = i/4 (= cA).
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+        if (jt < nkt) {
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+                u16x8 vop;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vop[e] = static_cast<uint16_t>(v0[e]);
+                    vop[4 + e] = static_cast<uint16_t>(v1[e]);
+                }
+                float pp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
+                bf16x8 phi, plo;
+                split_hi_lo(pp, phi, plo);
+                o = mfma32(as_bf16x8(vop), phi, o);
+                o = mfma32(as_bf16x8(vop), plo, o);
+            }
+        }
+    }
+    return o;
+}
+
 // Workgroups per XCD group: the NKT query tiles of 8 consecutive units.
 __host__ __device__ inline int step_grid(int units, int nkt) { return (units + 7) / 8 * 8 * nkt; }
 
@@ -134,77 +215,8 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     }
     __syncthreads();
 
-    // ---- softmax part (overlaps the S stream): L^T = K Q^T, row softmax,
-    //      O^T = V^T P^T (P as hi + lo bf16)
-    const int g = lane / 16, jl = lane % 16;
-    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
-    f32x16 o = {};
-    const uint16_t* qr = sq + l32 * P + 8 * hh;
-    f32x16 lt[NKT];
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-        f32x16 acc = {};
-        if (jt < nkt) {
-            const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
-                             as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), acc);
-        }
-        lt[jt] = acc;
-    }
-    // row softmax over the Br valid keys (one query per lane pair)
-    float m = -INFINITY;
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-            const float x = j < Br ? lt[jt][rr] * sl2 : -INFINITY;
-            lt[jt][rr] = x;
-            m = fmaxf(m, x);
-        }
-    }
-    m = fmaxf(m, __shfl_xor(m, 32));
-    float sum = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const float p = __builtin_amdgcn_exp2f(lt[jt][rr] - m);   // exp2(-inf) = 0 for masked keys
-            lt[jt][rr] = p;
-            sum += p;
-        }
-    }
-    sum += __shfl_xor(sum, 32);
-    const float inv = __builtin_amdgcn_rcpf(sum);
-    // V^T operand of k-step (jt, gp): keys jt*32 + 16gp + 4hh + {0..3} and the
-    // same + 8, matching registers 8gp .. 8gp+7 of L^T; the column of lane i in
-    // 16-lane group g is 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4, q = i/4 (= cA).
-#pragma unroll
-    for (int jt = 0; jt < NKT; ++jt) {
-        if (jt < nkt) {
-#pragma unroll
-            for (int gp = 0; gp < 2; ++gp) {
-                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
-                u16x8 vop;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vop[e] = static_cast<uint16_t>(v0[e]);
-                    vop[4 + e] = static_cast<uint16_t>(v1[e]);
-                }
-                float pp[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
-                bf16x8 phi, plo;
-                split_hi_lo(pp, phi, plo);
-                o = mfma32(as_bf16x8(vop), phi, o);
-                o = mfma32(as_bf16x8(vop), plo, o);
-            }
-        }
-    }
+    // ---- softmax part (overlaps the S stream)
+    f32x16 o = softmax_tile<D, NKT>(sq, sk, sv, Br, nkt, sl2, ct, lane);
     // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16 (fenced so its
     // phi(Q) operand reads are not hoisted into the softmax part, where the
     // logits already occupy the registers)
@@ -232,6 +244,163 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
         u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
         op[0] = o0;
         op[1] = o1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused step + commit (the last denoising step of a block followed by its
+// commit, worked example: block 2's output uses S_1, then
+// S_{1,2} = S_1 + phi(K_2)^T V_2), bf16, blk <= 32 * NKT.
+//
+// One workgroup per (request, head): it stages every query tile, computes the
+// step's outputs from the old S exactly as the step kernel does, and then adds
+// phi(K)^T V into the state.  The commit reuses the staged K and V: wave ct
+// owns state rows [32 ct, 32 ct + 32) (value dims) and, per 32-feature tile,
+// reads its old S^T tile in the accumulator layout (an L2 hit: the wave has
+// just streamed those rows), runs the MFMA reduction over the block's keys
+// (A = V^T through the transposing LDS read, keys past B_r zeroed;
+// B = ReLU(K) through the same read), and writes the tile back.  Each wave
+// reads and writes only its own rows, and a unit's state is touched by one
+// workgroup, so the in-place update needs no synchronisation beyond the
+// requirement that requests use distinct slots.
+// ---------------------------------------------------------------------------
+template <int D, int NKT>
+__global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs a)
+{
+    constexpr int KS = D / 16;
+    constexpr int NC = D / 32;
+    constexpr int NT = NC * kWave;
+    constexpr int R = NKT * 32;             // staged rows of Q, K and V
+    constexpr int P = D + 8;
+    constexpr int CPR = D / 8;
+    constexpr int CPT = R * CPR / NT;
+    static_assert(CPT * NT == R * CPR, "even staging split");
+    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
+
+    const int unit = blockIdx.x;
+    const int r = unit / a.heads, h = unit % a.heads;
+    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    Br = Br > a.blk ? a.blk : Br;
+    const int slot = a.slots[r];
+    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, ct = tid / kWave;
+    const int l32 = lane % 32, hh = lane / 32;
+    const int64_t rs = (int64_t)a.heads * D;
+    const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + base;
+    const uint16_t* k = static_cast<const uint16_t*>(a.k) + base;
+    const uint16_t* v = static_cast<const uint16_t*>(a.v) + base;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + base;
+    float* st = a.state_rw + ((int64_t)slot * a.heads + h) * D * D;
+
+    const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
+    const int nkt = (Br + 31) / 32;
+    const int last = Br - 1;
+    const float sl2 = a.scale * 1.4426950408889634f;
+
+    u32x4 cq[CPT], ck[CPT], cv[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        const int64_t off = (int64_t)(row < Br ? row : last) * rs + c8;
+        cq[u] = *reinterpret_cast<const u32x4*>(q + off);
+        ck[u] = *reinterpret_cast<const u32x4*>(k + off);
+        cv[u] = *reinterpret_cast<const u32x4*>(v + off);
+    }
+    f32x4 sraw[KS][2];
+    const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        sraw[s][0] = srow[4 * s];
+        sraw[s][1] = srow[4 * s + 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
+        *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
+        *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
+    }
+    __syncthreads();
+
+    // ---- the step, from the old state
+    f32x16 o[NKT];
+#pragma unroll
+    for (int qt = 0; qt < NKT; ++qt)
+        o[qt] = qt < nkt ? softmax_tile<D, NKT>(sq + qt * 32 * P, sk, sv, Br, nkt, sl2, ct, lane) : f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const float sv8[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
+                              sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
+        bf16x8 shi, slo;
+        split_hi_lo(sv8, shi, slo);
+#pragma unroll
+        for (int qt = 0; qt < NKT; ++qt) {
+            if (qt < nkt) {
+                const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
+                const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
+                o[qt] = mfma32(shi, pq, o[qt]);
+                o[qt] = mfma32(slo, pq, o[qt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int qt = 0; qt < NKT; ++qt) {
+        const int i = qt * 32 + l32;
+        if (qt < nkt && i < Br) {
+            u16x8 o0, o1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o0[e] = f32_to_bf16_bits(o[qt][e]);
+                o1[e] = f32_to_bf16_bits(o[qt][8 + e]);
+            }
+            u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
+            op[0] = o0;
+            op[1] = o1;
+        }
+    }
+
+    // ---- the commit: S^T[c][f] += sum_j V[j][c] ReLU(K[j][f]) over j < Br
+    __builtin_amdgcn_sched_barrier(0);
+    const int g = lane / 16, jl = lane % 16;
+    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
+#pragma unroll 1
+    for (int ft = 0; ft < NC; ++ft) {
+        // accumulator register rr of lane (l32, hh): row 32 ct + 16 hh + rr, feature 32 ft + l32
+        float* tile = st + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
+        f32x16 acc;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
+        const int kcol = 32 * ft + 16 * (g % 2) + 4 * (jl % 4);
+#pragma unroll
+        for (int jt = 0; jt < NKT; ++jt) {
+            if (jt < nkt) {
+#pragma unroll
+                for (int gp = 0; gp < 2; ++gp) {
+                    const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+                    const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+                    const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+                    const s16x4 k0 = lds_read_tr4(sk + row0 * P + kcol);
+                    const s16x4 k1 = lds_read_tr4(sk + (row0 + 8) * P + kcol);
+                    const int key0 = jt * 32 + 16 * gp + 4 * hh;    // keys key0 + e, key0 + 8 + e
+                    u16x8 vop, kop;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        vop[e] = key0 + e < Br ? static_cast<uint16_t>(v0[e]) : uint16_t(0);
+                        vop[4 + e] = key0 + 8 + e < Br ? static_cast<uint16_t>(v1[e]) : uint16_t(0);
+                        kop[e] = static_cast<uint16_t>(k0[e]);
+                        kop[4 + e] = static_cast<uint16_t>(k1[e]);
+                    }
+                    acc = mfma32(as_bf16x8(vop), as_bf16x8(relu_bf16x8(kop)), acc);
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
     }
 }
 
@@ -419,6 +588,46 @@ static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
     if (a.blk <= 32) step_bf16_mfma<D, 1><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
     else if (a.blk <= 64) step_bf16_mfma<D, 2><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
     else step_bf16_mfma_long<D><<<units, 4 * D / 32 * kWave, 0, stream>>>(a);
+}
+
+hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
+{
+    const int units = a.n_req * a.heads;
+    const dim3 block(a.d / 32 * kWave);
+    if (a.dtype_bf16 && a.d >= 32 && a.blk <= 64) {
+        const bool two = a.blk > 32;
+        switch (a.d) {
+        case 32:
+            if (two) step_commit_bf16_mfma<32, 2><<<units, block, 0, stream>>>(a);
+            else step_commit_bf16_mfma<32, 1><<<units, block, 0, stream>>>(a);
+            break;
+        case 64:
+            if (two) step_commit_bf16_mfma<64, 2><<<units, block, 0, stream>>>(a);
+            else step_commit_bf16_mfma<64, 1><<<units, block, 0, stream>>>(a);
+            break;
+        default:
+            if (two) step_commit_bf16_mfma<128, 2><<<units, block, 0, stream>>>(a);
+            else step_commit_bf16_mfma<128, 1><<<units, block, 0, stream>>>(a);
+            break;
+        }
+        return hipGetLastError();
+    }
+    // other shapes: the step, then the commit, on the same stream
+    const hipError_t e = launch_step(a, stream);
+    if (e != hipSuccess) return e;
+    PhiKVArgs c{};
+    c.k = a.k;
+    c.v = a.v;
+    c.state = a.state_rw;
+    c.slots = a.slots;
+    c.blk_lens = a.blk_lens;
+    c.n_req = a.n_req;
+    c.n_slots = a.n_slots;
+    c.heads = a.heads;
+    c.blk = a.blk;
+    c.d = a.d;
+    c.dtype_bf16 = a.dtype_bf16;
+    return launch_commit(c, stream);
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream)

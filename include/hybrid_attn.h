@@ -111,13 +111,34 @@ ha_status hybrid_attn_step(const void* q, const void* k, const void* v,
  *
  *   S_{slots[r], h} += sum_{j < B_r} phi(k_j)^T v_j        (in place, fp32)
  *
- * Not idempotent: committing the same block twice adds it twice.
+ * Not idempotent: committing the same block twice adds it twice.  Requests
+ * of one call must use distinct slots (two requests committing into one slot
+ * in the same call race).
  */
 ha_status hybrid_state_commit(const void* k, const void* v, float* state,
                               const int32_t* slots, const int32_t* blk_lens,
                               int32_t n_req, int32_t n_slots, int32_t heads,
                               int32_t blk, int32_t d, ha_dtype dtype,
                               void* stream);
+
+/*
+ * The last denoising step of a block fused with its commit (worked example:
+ * block 2's output uses S_1, then S_{1,2} = S_1 + phi(K_2)^T V_2):
+ *
+ *   out = hybrid_attn_step(q, k, v, state)            (from the OLD state)
+ *   S_{slots[r], h} += sum_{j < B_r} phi(k_j)^T v_j    (in place)
+ *
+ * with the same arguments, rules and results as hybrid_attn_step followed by
+ * hybrid_state_commit on the same k, v (up to fp32 rounding of the state),
+ * but one pass over the inputs: the state is read once and written once.
+ * Requests of one call must use distinct slots (as for hybrid_state_commit).
+ */
+ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v,
+                                  float* state, const int32_t* slots,
+                                  void* out, const int32_t* blk_lens,
+                                  int32_t n_req, int32_t n_slots,
+                                  int32_t heads, int32_t blk, int32_t d,
+                                  float scale, ha_dtype dtype, void* stream);
 
 /*
  * Fold whole prompts into the state, OVERWRITING each request's slot:

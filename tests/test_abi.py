@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("hybrid_attn_step", "hybrid_state_commit", "hybrid_state_prefill",
+    for n in ("hybrid_attn_step", "hybrid_attn_step_commit", "hybrid_state_commit", "hybrid_state_prefill",
               "hybrid_state_prefill_workspace_bytes", "hybrid_exact_step", "hybrid_exact_step_workspace_bytes",
               "hybrid_last_error", "hybrid_abi_version"):
         assert n in names
@@ -52,6 +52,12 @@ def step(lib, q=1, k=1, v=1, state=1, slots=1, out=1, n_req=2, n_slots=2, heads=
          scale=0.125, dtype=binding.HA_BF16):
     return lib.hybrid_attn_step(q, k, v, state, slots, out, None, n_req, n_slots, heads, blk, d, scale,
                                 dtype, None)
+
+
+def step_commit(lib, q=1, k=1, v=1, state=1, slots=1, out=1, n_req=2, n_slots=2, heads=4, blk=32, d=64,
+                scale=0.125, dtype=binding.HA_BF16):
+    return lib.hybrid_attn_step_commit(q, k, v, state, slots, out, None, n_req, n_slots, heads, blk, d, scale,
+                                       dtype, None)
 
 
 def commit(lib, k=1, v=1, state=1, slots=1, n_req=2, n_slots=2, heads=4, blk=32, d=64, dtype=binding.HA_BF16):
@@ -93,6 +99,8 @@ def last(lib):
 def test_step_rejects(lib, kw, status, msg):
     assert step(lib, **kw) == status
     assert msg in last(lib) and "hybrid_attn_step" in last(lib)
+    assert step_commit(lib, **kw) == status
+    assert msg in last(lib) and "hybrid_attn_step_commit" in last(lib)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -153,6 +161,7 @@ A = 1 << 12   # a fake, suitably aligned device address (never dereferenced: the
 @pytest.mark.parametrize("call,kw,msg", [
     ("step", dict(q=A + 2), "16-byte"),
     ("step", dict(state=A + 8), "16-byte"),
+    ("step_commit", dict(out=A + 4), "16-byte"),
     ("commit", dict(v=A + 4), "16-byte"),
     ("prefill", dict(k=A + 8), "16-byte"),
     ("prefill", dict(ws=A + 16), "256-byte"),
@@ -161,8 +170,9 @@ A = 1 << 12   # a fake, suitably aligned device address (never dereferenced: the
     ("exact", dict(ws=A + 128), "256-byte"),
 ])
 def test_misaligned_pointers_rejected(lib, call, kw, msg):
-    fn = {"step": step, "commit": commit, "prefill": prefill, "exact": exact}[call]
+    fn = {"step": step, "step_commit": step_commit, "commit": commit, "prefill": prefill, "exact": exact}[call]
     base = {"step": dict(q=A, k=A, v=A, state=A, slots=A, out=A),
+            "step_commit": dict(q=A, k=A, v=A, state=A, slots=A, out=A),
             "commit": dict(k=A, v=A, state=A, slots=A),
             "prefill": dict(k=A, v=A, cu=A, state=A, slots=A, ws=A),
             "exact": dict(q=A, k=A, v=A, kc=A, vc=A, cu=A, out=A, ws=A)}[call]
@@ -174,6 +184,7 @@ def test_misaligned_pointers_rejected(lib, call, kw, msg):
 def test_empty_batches_are_noops(lib):
     """n_req == 0 returns OK without touching any pointer (all NULL here)."""
     assert step(lib, q=None, k=None, v=None, state=None, slots=None, out=None, n_req=0) == binding.HA_OK
+    assert step_commit(lib, q=None, k=None, v=None, state=None, slots=None, out=None, n_req=0) == binding.HA_OK
     assert commit(lib, k=None, v=None, state=None, slots=None, n_req=0) == binding.HA_OK
     assert prefill(lib, k=None, v=None, cu=None, state=None, slots=None, ws=None, ws_bytes=0,
                    n_req=0) == binding.HA_OK

@@ -161,6 +161,88 @@ def test_commit_parity(d, blk, dtype):
     assert_parity(state_to_oracle(state), ref2, dtype, "state after second commit")
 
 
+# --------------------------------------------------------------------------
+# Fused last step + commit
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (128, 33), (128, 1), (128, 100), (64, 64), (64, 17),
+                                   (32, 64), (32, 5), (16, 32)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_step_commit_parity(d, blk, dtype):
+    """Output from the old state and the updated state both match the oracle's
+    step then commit; slots not named are untouched; on the matrix-core path
+    the output is bit-identical to hybrid_attn_step's."""
+    n_req, H, n_slots = 3, 5, 4
+    seed = 17000 + 100 * d + blk
+    q, k, v = (gen((n_req, blk, H, d), seed + t, dtype) for t in range(3))
+    lens = torch.tensor([blk, max(1, (blk * 2) // 3), 1], dtype=torch.int32, device=DEV)
+    slots = torch.tensor([2, 0, 3], dtype=torch.int32, device=DEV)
+    state = synth.normal((n_slots, H, d, d), seed + 3, std=10.0, dtype=torch.float32).to(DEV)
+    S0 = state_to_oracle(state)
+    plain = bh.hybrid_attn_step(q, k, v, state, slots, blk_lens=lens)
+    out = torch.full_like(q, SENTINEL)
+    bh.hybrid_attn_step_commit(q, k, v, state, slots, out=out, blk_lens=lens)
+    torch.cuda.synchronize()
+    mask = rows_mask(lens, n_req, blk)
+    o = to64(out)
+    assert np.all(o[~mask] == SENTINEL), "rows past B_r were written"
+    ref = oracle.step(q, k, v, S0, slots=slots, blk_lens=lens, scale=d ** -0.5)
+    assert_parity(o[mask], ref[mask], dtype, "fused step output")
+    S1 = oracle.commit(k, v, S0, slots=slots, blk_lens=lens)
+    got = state_to_oracle(state)
+    assert np.array_equal(got[1], S0[1]), "a slot not named was modified"
+    assert_parity(got, S1, dtype, "state after fused commit")
+    if dtype == torch.bfloat16 and d >= 32 and blk <= 64:
+        assert torch.equal(out[torch.from_numpy(mask).to(DEV)], plain[torch.from_numpy(mask).to(DEV)])
+
+
+def test_step_commit_skips_invalid_slot_and_empty_rows():
+    n_req, blk, H, d = 3, 64, 2, 128
+    q, k, v = (gen((n_req, blk, H, d), 17500 + t, torch.bfloat16) for t in range(3))
+    state = synth.normal((2, H, d, d), 17503, dtype=torch.float32).to(DEV)
+    before = state.clone()
+    slots = torch.tensor([7, 0, 1], dtype=torch.int32, device=DEV)       # request 0: invalid slot
+    lens = torch.tensor([64, 40, 0], dtype=torch.int32, device=DEV)       # request 2: no rows
+    out = torch.full_like(q, SENTINEL)
+    bh.hybrid_attn_step_commit(q, k, v, state, slots, out=out, blk_lens=lens)
+    torch.cuda.synchronize()
+    o = to64(out)
+    assert np.all(o[0] == SENTINEL) and np.all(o[2] == SENTINEL) and np.all(o[1, 40:] == SENTINEL)
+    assert torch.equal(state[1], before[1]), "slot of the empty request was modified"
+    S1 = oracle.commit(k[1:2], v[1:2], state_to_oracle(before[0:1]), blk_lens=[40])
+    assert_parity(state_to_oracle(state[0:1]), S1, torch.bfloat16, "state of request 1")
+    ref = oracle.step(q[1:2], k[1:2], v[1:2], state_to_oracle(before[0:1]), blk_lens=[40])
+    assert_parity(o[1:2, :40], ref[:, :40], torch.bfloat16, "output of request 1")
+
+
+def test_step_commit_block_loop_matches_separate_calls():
+    """A block loop with the last step fused into the commit tracks the loop
+    with separate calls: outputs within the rule, states within fp32 rounding."""
+    n_req, blk, H, d = 4, 64, 4, 128
+    s_a = torch.zeros(n_req, H, d, d, device=DEV)
+    s_b = torch.zeros_like(s_a)
+    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
+    S_ref = np.zeros((n_req, H, d, d))
+    for b in range(6):
+        for t in range(3):
+            q, k, v = (gen((n_req, blk, H, d), 18000 + 100 * b + 10 * t + i, torch.bfloat16) for i in range(3))
+            last = t == 2
+            out_a = bh.hybrid_attn_step(q, k, v, s_a, slots)
+            if last:
+                bh.hybrid_state_commit(k, v, s_a, slots)
+                out_b = bh.hybrid_attn_step_commit(q, k, v, s_b, slots)
+            else:
+                out_b = bh.hybrid_attn_step(q, k, v, s_b, slots)
+            ref = oracle.step(q, k, v, S_ref)
+            assert_parity(out_b, ref, torch.bfloat16, f"block {b} step {t}")
+            assert_parity(out_a, ref, torch.bfloat16, f"block {b} step {t} (separate)")
+        S_ref = oracle.commit(k, v, S_ref)
+    torch.cuda.synchronize()
+    assert_parity(state_to_oracle(s_b), S_ref, torch.bfloat16, "final state (fused)")
+    rel = float((s_b - s_a).abs().max() / s_a.abs().max())
+    assert rel < 1e-5, rel
+
+
 def test_commit_order_independent():
     """Commits of several blocks in any order give the same state (fp32
     reassociation only), equal to the oracle's sum."""

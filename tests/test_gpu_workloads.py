@@ -110,9 +110,10 @@ def _gather(t, units):
 
 def test_block_loop_sampled():
     """32 requests x 32 heads, d = 128: 32 blocks of 32 tokens, 8 steps per
-    block (fresh N(0, 0.5^2) Q/K/V each step), one commit per block of the
-    block's last step.  Every step's output and the final state are compared
-    on 6 sampled units against the oracle's fp64 chain."""
+    block (fresh N(0, 0.5^2) Q/K/V each step), the block's last step fused
+    with its commit (hybrid_attn_step_commit), as the benchmark runs it.
+    Every step's output and the final state are compared on 6 sampled units
+    against the oracle's fp64 chain."""
     W = BLOCK_LOOP
     units = _units(W.n_req, W.heads, 6, 404)
     state = torch.zeros(W.n_req, W.heads, W.d, W.d, device=DEV)
@@ -123,11 +124,11 @@ def test_block_loop_sampled():
         for t in range(W.steps_per_block):
             q, k, v = (synth.normal((W.n_req, W.blk, W.heads, W.d), synth.seed_of(W.index, b, t, i), std=W.std,
                                     device=DEV) for i in range(3))
-            out = bh.hybrid_attn_step(q, k, v, state, slots, scale=W.scale)
+            step = bh.hybrid_attn_step_commit if t == W.steps_per_block - 1 else bh.hybrid_attn_step
+            out = step(q, k, v, state, slots, scale=W.scale)
             qs, ks, vs, os_ = _gather(q, units), _gather(k, units), _gather(v, units), _gather(out, units)
             ref = oracle.step(qs, ks, vs, S_ref, scale=W.scale)
             worst = max(worst, assert_parity(os_, ref, torch.bfloat16, f"block {b} step {t}"))
-        bh.hybrid_state_commit(k, v, state, slots)
         S_ref = oracle.commit(ks, vs, S_ref)
     torch.cuda.synchronize()
     got = np.stack([state_to_oracle(state)[r, h:h + 1] for r, h in units])
@@ -137,9 +138,10 @@ def test_block_loop_sampled():
 
 def test_prefill_decode_sampled():
     """8 requests x 32 heads, d = 128, prompts uniform in [16384, 65536]
-    (packed, chunk 256) prefilled, then 16 blocks of 64 tokens x 4 steps +
-    commit.  4 sampled units: prefilled state, every step's output and the
-    final state against the oracle."""
+    (packed, chunk 256) prefilled, then 16 blocks of 64 tokens x 4 steps, the
+    last one fused with the block's commit, as the benchmark runs it.  4
+    sampled units: prefilled state, every step's output and the final state
+    against the oracle."""
     W = PREFILL_DECODE
     lens = synth.uniform_int(W.n_req, *W.prompt_range, synth.seed_of(W.index, tensor=synth.TENSOR_LEN))
     cu = synth.cu_from_lengths(lens)
@@ -163,11 +165,11 @@ def test_prefill_decode_sampled():
         for t in range(W.steps_per_block):
             q, k, v = (synth.normal((W.n_req, W.blk, W.heads, W.d), synth.seed_of(W.index, b, t, i), device=DEV)
                        for i in range(3))
-            out = bh.hybrid_attn_step(q, k, v, state, slots, scale=W.scale)
+            step = bh.hybrid_attn_step_commit if t == W.steps_per_block - 1 else bh.hybrid_attn_step
+            out = step(q, k, v, state, slots, scale=W.scale)
             qs, ks, vs, os_ = _gather(q, units), _gather(k, units), _gather(v, units), _gather(out, units)
             worst = max(worst, assert_parity(os_, oracle.step(qs, ks, vs, S_ref, scale=W.scale), torch.bfloat16,
                                              f"block {b} step {t}"))
-        bh.hybrid_state_commit(k, v, state, slots)
         S_ref = oracle.commit(ks, vs, S_ref)
     torch.cuda.synchronize()
     got = np.stack([state_to_oracle(state)[r, h:h + 1] for r, h in units])

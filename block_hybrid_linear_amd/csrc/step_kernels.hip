@@ -61,11 +61,14 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p)
 // Softmax part of one 32-query tile whose rows start at qtile in LDS:
 // L^T = K Q^T over the key tiles, row softmax over the Br valid keys (one
 // query per lane pair), O^T = V^T P^T with P as hi + lo bf16.  Returns the
-// wave's accumulator (value columns of tile ct, transposed).
+// wave's accumulator (value columns of tile ct, transposed).  Contraction of
+// the scaling and the max subtraction into one fma is switched off so that
+// every kernel that inlines this computes bit-identical probabilities.
 template <int D, int NKT>
 __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint16_t* sk, const uint16_t* sv,
-                                               int Br, int nkt, float sl2, int ct, int lane)
+                                               int Br, float sl2, int ct, int lane)
 {
+#pragma clang fp contract(off)
     constexpr int KS = D / 16, P = D + 8;
     const int l32 = lane % 32, hh = lane / 32;
     const int g = lane / 16, jl = lane % 16;
@@ -76,13 +79,11 @@ __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint
 #pragma unroll
     for (int jt = 0; jt < NKT; ++jt) {
         f32x16 acc = {};
-        if (jt < nkt) {
-            const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
+        const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
-                             as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), acc);
-        }
+        for (int s = 0; s < KS; ++s)
+            acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
+                         as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), acc);
         lt[jt] = acc;
     }
     float m = -INFINITY;
@@ -114,29 +115,43 @@ __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint
     // 16-lane group g is 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4, q = i/4 (= cA).
 #pragma unroll
     for (int jt = 0; jt < NKT; ++jt) {
-        if (jt < nkt) {
 #pragma unroll
-            for (int gp = 0; gp < 2; ++gp) {
-                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
-                u16x8 vop;
+        for (int gp = 0; gp < 2; ++gp) {
+            const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+            const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+            u16x8 vop;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vop[e] = static_cast<uint16_t>(v0[e]);
-                    vop[4 + e] = static_cast<uint16_t>(v1[e]);
-                }
-                float pp[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
-                bf16x8 phi, plo;
-                split_hi_lo(pp, phi, plo);
-                o = mfma32(as_bf16x8(vop), phi, o);
-                o = mfma32(as_bf16x8(vop), plo, o);
+            for (int e = 0; e < 4; ++e) {
+                vop[e] = static_cast<uint16_t>(v0[e]);
+                vop[4 + e] = static_cast<uint16_t>(v1[e]);
             }
+            float pp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pp[e] = lt[jt][8 * gp + e] * inv;
+            bf16x8 phi, plo;
+            split_hi_lo(pp, phi, plo);
+            o = mfma32(as_bf16x8(vop), phi, o);
+            o = mfma32(as_bf16x8(vop), plo, o);
         }
     }
     return o;
+}
+
+// Writes a wave's output accumulator (query l32, columns 32 ct + 16 hh + r)
+// as bf16 into a row-major LDS tile of 32 rows (pitch D + 8).
+template <int D>
+__device__ __forceinline__ void store_tile_lds(uint16_t* tile, const f32x16& o, int l32, int hh, int ct)
+{
+    u16x8 o0, o1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        o0[e] = f32_to_bf16_bits(o[e]);
+        o1[e] = f32_to_bf16_bits(o[8 + e]);
+    }
+    u16x8* op = reinterpret_cast<u16x8*>(tile + l32 * (D + 8) + 32 * ct + 16 * hh);
+    op[0] = o0;
+    op[1] = o1;
 }
 
 // Workgroups per XCD group: the NKT query tiles of 8 consecutive units.
@@ -179,7 +194,6 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     const float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
 
     const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;  // A row -> column
-    const int nkt = (Br + 31) / 32;                          // <= NKT
     const int last = Br - 1;
     const float sl2 = a.scale * 1.4426950408889634f;         // logits in log2 units
 
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     __syncthreads();
 
     // ---- softmax part (overlaps the S stream)
-    f32x16 o = softmax_tile<D, NKT>(sq, sk, sv, Br, nkt, sl2, ct, lane);
+    f32x16 o = softmax_tile<D, NKT>(sq, sk, sv, Br, sl2, ct, lane);
     // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16 (fenced so its
     // phi(Q) operand reads are not hoisted into the softmax part, where the
     // logits already occupy the registers)
@@ -232,18 +246,18 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
         o = mfma32(shi, pq, o);
         o = mfma32(slo, pq, o);
     }
-    // ---- store: lane holds query qt*32 + l32, columns 32 ct + 16 hh + 0..15
-    const int i = qt * 32 + l32;
-    if (i < Br) {
-        u16x8 o0, o1;
+    // ---- store through LDS: lane holds query qt*32 + l32, columns
+    // 32 ct + 16 hh + 0..15; the tile is written back row-major so that each
+    // store instruction covers whole head rows
+    __syncthreads();                                   // every wave is done with sq
+    store_tile_lds<D>(sq, o, l32, hh, ct);
+    __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o0[e] = f32_to_bf16_bits(o[e]);
-            o1[e] = f32_to_bf16_bits(o[8 + e]);
-        }
-        u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
-        op[0] = o0;
-        op[1] = o1;
+    for (int u = 0; u < CQ; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        if (qt * 32 + row < Br)
+            *reinterpret_cast<u32x4*>(out + (int64_t)(qt * 32 + row) * rs + c8) =
+                *reinterpret_cast<const u32x4*>(sq + row * P + c8);
     }
 }
 
@@ -296,7 +310,6 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
     float* st = a.state_rw + ((int64_t)slot * a.heads + h) * D * D;
 
     const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
-    const int nkt = (Br + 31) / 32;
     const int last = Br - 1;
     const float sl2 = a.scale * 1.4426950408889634f;
 
@@ -329,8 +342,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
     // ---- the step, from the old state
     f32x16 o[NKT];
 #pragma unroll
-    for (int qt = 0; qt < NKT; ++qt)
-        o[qt] = qt < nkt ? softmax_tile<D, NKT>(sq + qt * 32 * P, sk, sv, Br, nkt, sl2, ct, lane) : f32x16{};
+    for (int qt = 0; qt < NKT; ++qt) o[qt] = softmax_tile<D, NKT>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -340,28 +352,22 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
         split_hi_lo(sv8, shi, slo);
 #pragma unroll
         for (int qt = 0; qt < NKT; ++qt) {
-            if (qt < nkt) {
-                const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
-                const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-                o[qt] = mfma32(shi, pq, o[qt]);
-                o[qt] = mfma32(slo, pq, o[qt]);
-            }
+            const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
+            const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
+            o[qt] = mfma32(shi, pq, o[qt]);
+            o[qt] = mfma32(slo, pq, o[qt]);
         }
     }
+    // outputs through LDS (sq is free now; the commit below still reads sk, sv)
+    __syncthreads();
 #pragma unroll
-    for (int qt = 0; qt < NKT; ++qt) {
-        const int i = qt * 32 + l32;
-        if (qt < nkt && i < Br) {
-            u16x8 o0, o1;
+    for (int qt = 0; qt < NKT; ++qt) store_tile_lds<D>(sq + qt * 32 * P, o[qt], l32, hh, ct);
+    __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o0[e] = f32_to_bf16_bits(o[qt][e]);
-                o1[e] = f32_to_bf16_bits(o[qt][8 + e]);
-            }
-            u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
-            op[0] = o0;
-            op[1] = o1;
-        }
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        if (row < Br)
+            *reinterpret_cast<u32x4*>(out + (int64_t)row * rs + c8) = *reinterpret_cast<const u32x4*>(sq + row * P + c8);
     }
 
     // ---- the commit: S^T[c][f] += sum_j V[j][c] ReLU(K[j][f]) over j < Br
@@ -378,25 +384,23 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
         const int kcol = 32 * ft + 16 * (g % 2) + 4 * (jl % 4);
 #pragma unroll
         for (int jt = 0; jt < NKT; ++jt) {
-            if (jt < nkt) {
 #pragma unroll
-                for (int gp = 0; gp < 2; ++gp) {
-                    const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-                    const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-                    const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
-                    const s16x4 k0 = lds_read_tr4(sk + row0 * P + kcol);
-                    const s16x4 k1 = lds_read_tr4(sk + (row0 + 8) * P + kcol);
-                    const int key0 = jt * 32 + 16 * gp + 4 * hh;    // keys key0 + e, key0 + 8 + e
-                    u16x8 vop, kop;
+            for (int gp = 0; gp < 2; ++gp) {
+                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+                const s16x4 k0 = lds_read_tr4(sk + row0 * P + kcol);
+                const s16x4 k1 = lds_read_tr4(sk + (row0 + 8) * P + kcol);
+                const int key0 = jt * 32 + 16 * gp + 4 * hh;    // keys key0 + e, key0 + 8 + e
+                u16x8 vop, kop;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        vop[e] = key0 + e < Br ? static_cast<uint16_t>(v0[e]) : uint16_t(0);
-                        vop[4 + e] = key0 + 8 + e < Br ? static_cast<uint16_t>(v1[e]) : uint16_t(0);
-                        kop[e] = static_cast<uint16_t>(k0[e]);
-                        kop[4 + e] = static_cast<uint16_t>(k1[e]);
-                    }
-                    acc = mfma32(as_bf16x8(vop), as_bf16x8(relu_bf16x8(kop)), acc);
+                for (int e = 0; e < 4; ++e) {
+                    vop[e] = key0 + e < Br ? static_cast<uint16_t>(v0[e]) : uint16_t(0);
+                    vop[4 + e] = key0 + 8 + e < Br ? static_cast<uint16_t>(v1[e]) : uint16_t(0);
+                    kop[e] = static_cast<uint16_t>(k0[e]);
+                    kop[4 + e] = static_cast<uint16_t>(k1[e]);
                 }
+                acc = mfma32(as_bf16x8(vop), as_bf16x8(relu_bf16x8(kop)), acc);
             }
         }
 #pragma unroll

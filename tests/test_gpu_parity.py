@@ -123,6 +123,38 @@ def test_step_invalid_slot_and_empty_rows_skip():
     assert_parity(o[:1], ref, torch.bfloat16, "valid request")
 
 
+def _bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significand bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (64, 64), (32, 64), (128, 1), (64, 20)])
+def test_step_outputs_correctly_rounded(d, blk, fused):
+    """The matrix-core step keeps fp32 S and P at ~16 significand bits (hi + lo
+    bf16), so every bf16 output is within one bf16 ulp of the exact value plus
+    fp32 accumulation error (1e-5 of the output's scale).  A dropped lo term
+    or a stale accumulator register shows up here while staying inside the
+    whole-output rule."""
+    n_req, H = 3, 4
+    seed = 8500 + 100 * d + blk
+    q, k, v = (gen((n_req, blk, H, d), seed + t, torch.bfloat16) for t in range(3))
+    lens = torch.tensor([blk, max(1, blk // 2), 1], dtype=torch.int32, device=DEV)
+    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
+    state = synth.normal((n_req, H, d, d), seed + 3, std=10.0, dtype=torch.float32).to(DEV)
+    S0 = state_to_oracle(state)
+    call = bh.hybrid_attn_step_commit if fused else bh.hybrid_attn_step
+    out = call(q, k, v, state, slots, blk_lens=lens)
+    torch.cuda.synchronize()
+    ref = oracle.step(q, k, v, S0, blk_lens=lens, scale=d ** -0.5)
+    mask = rows_mask(lens, n_req, blk)
+    o, r = to64(out)[mask], ref[mask]
+    bound = _bf16_ulp(r) + 1e-5 * np.abs(r).max()
+    bad = np.abs(o - r) > bound
+    assert not bad.any(), f"{bad.sum()} outputs off by more than one bf16 ulp, worst {np.abs(o - r)[bad].max():.3e}"
+
+
 def test_step_deterministic():
     n_req, blk, H, d = 4, 64, 4, 128
     q, k, v = (gen((n_req, blk, H, d), 8400 + t, torch.bfloat16) for t in range(3))

@@ -266,24 +266,26 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 // commit, worked example: block 2's output uses S_1, then
 // S_{1,2} = S_1 + phi(K_2)^T V_2), bf16, blk <= 32 * NKT.
 //
-// One workgroup per (request, head): it stages every query tile, computes the
-// step's outputs from the old S exactly as the step kernel does, and then adds
-// phi(K)^T V into the state.  The commit reuses the staged K and V: wave ct
-// owns state rows [32 ct, 32 ct + 32) (value dims) and, per 32-feature tile,
-// reads its old S^T tile in the accumulator layout (an L2 hit: the wave has
-// just streamed those rows), runs the MFMA reduction over the block's keys
-// (A = V^T through the transposing LDS read, keys past B_r zeroed;
-// B = ReLU(K) through the same read), and writes the tile back.  Each wave
-// reads and writes only its own rows, and a unit's state is touched by one
-// workgroup, so the in-place update needs no synchronisation beyond the
-// requirement that requests use distinct slots.
+// One workgroup per (request, head) with NKT x D/32 waves: wave (qt, ct)
+// computes the outputs of query tile qt, value columns [32 ct, 32 ct + 32),
+// from the old S exactly as the step kernel does (its own S^T tile, split
+// hi + lo).  After the outputs are staged and stored, every wave has consumed
+// its S^T tile, and the commit adds phi(K)^T V into the state, reusing the
+// staged K and V: wave (qt, ct) owns state rows [32 ct, 32 ct + 32) and the
+// 32-feature tiles ft with ft % NKT == qt; per tile it reads the old values
+// in the accumulator layout (an L2 hit: the rows were just streamed), runs
+// the MFMA reduction over the block's keys (A = V^T through the transposing
+// LDS read, keys past B_r zeroed; B = ReLU(K) through the same read) and
+// writes the tile back.  Each state element is read for the step before the
+// barrier and written once after it, by one wave; a unit's state is touched
+// by one workgroup, so requests only need distinct slots.
 // ---------------------------------------------------------------------------
 template <int D, int NKT>
-__global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs a)
+__global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;
     constexpr int NC = D / 32;
-    constexpr int NT = NC * kWave;
+    constexpr int NT = NKT * NC * kWave;
     constexpr int R = NKT * 32;             // staged rows of Q, K and V
     constexpr int P = D + 8;
     constexpr int CPR = D / 8;
@@ -299,7 +301,8 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
     if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
 
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, ct = tid / kWave;
+    const int lane = tid % kWave, w = tid / kWave;
+    const int qt = w / NC, ct = w % NC;
     const int l32 = lane % 32, hh = lane / 32;
     const int64_t rs = (int64_t)a.heads * D;
     const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
@@ -340,9 +343,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
     __syncthreads();
 
     // ---- the step, from the old state
-    f32x16 o[NKT];
-#pragma unroll
-    for (int qt = 0; qt < NKT; ++qt) o[qt] = softmax_tile<D, NKT>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane);
+    f32x16 o = softmax_tile<D, NKT>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -350,18 +351,14 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
                               sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
         bf16x8 shi, slo;
         split_hi_lo(sv8, shi, slo);
-#pragma unroll
-        for (int qt = 0; qt < NKT; ++qt) {
-            const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
-            const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-            o[qt] = mfma32(shi, pq, o[qt]);
-            o[qt] = mfma32(slo, pq, o[qt]);
-        }
+        const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
+        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
+        o = mfma32(shi, pq, o);
+        o = mfma32(slo, pq, o);
     }
     // outputs through LDS (sq is free now; the commit below still reads sk, sv)
     __syncthreads();
-#pragma unroll
-    for (int qt = 0; qt < NKT; ++qt) store_tile_lds<D>(sq + qt * 32 * P, o[qt], l32, hh, ct);
+    store_tile_lds<D>(sq + qt * 32 * P, o, l32, hh, ct);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
@@ -375,7 +372,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_commit_bf16_mfma(StepArgs
     const int g = lane / 16, jl = lane % 16;
     const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
 #pragma unroll 1
-    for (int ft = 0; ft < NC; ++ft) {
+    for (int ft = qt; ft < NC; ft += NKT) {
         // accumulator register rr of lane (l32, hh): row 32 ct + 16 hh + rr, feature 32 ft + l32
         float* tile = st + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
         f32x16 acc;
@@ -597,9 +594,9 @@ static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
 hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
 {
     const int units = a.n_req * a.heads;
-    const dim3 block(a.d / 32 * kWave);
     if (a.dtype_bf16 && a.d >= 32 && a.blk <= 64) {
         const bool two = a.blk > 32;
+        const dim3 block((two ? 2 : 1) * a.d / 32 * kWave);
         switch (a.d) {
         case 32:
             if (two) step_commit_bf16_mfma<32, 2><<<units, block, 0, stream>>>(a);

@@ -150,7 +150,7 @@ __device__ __forceinline__ bool exact_begin(const ExactArgs& a, ExactCursor& c)
 // (slice + unit).
 // ---------------------------------------------------------------------------
 template <int D, int NQ>
-__global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactArgs a)
+__global__ __launch_bounds__(D / 32 * kWave) __attribute__((amdgpu_waves_per_eu(NQ == 1 ? 3 : (NQ == 2 ? 2 : 1)))) void exact_slices_bf16_mfma(ExactArgs a)
 {
     constexpr int KS = D / 16, NC = D / 32, NT = NC * kWave;
     constexpr int TK = 32;                         // keys per stage
@@ -216,16 +216,23 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
         }
     };
 
+    // Per stage and query tile, one wave (rotating with the stage, so the work
+    // spreads over the SIMDs) computes the logits and the online-softmax
+    // update and publishes, in LDS, the probabilities as the PV operand of
+    // every lane (hi + lo bf16, in lane order), the rescale factor of each
+    // query, and the running max and sum.  Every wave then rescales its
+    // accumulator and adds V^T P^T for its value columns.
+    __shared__ __attribute__((aligned(16))) u16x8 sp[NQ][2][2][kWave];   // [qt][key half gp][hi, lo][lane]
+    __shared__ float scorr[NQ][32], sm[NQ][32], sl[NQ][32];
     const int g = lane / 16, jl = lane % 16;
     const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
     f32x16 o[NQ];
-    float m[NQ], l[NQ];
-    auto reset = [&]() {
+    auto reset = [&]() {                        // a new piece: accumulators and running max / sum
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) {
-            o[qt] = f32x16{};
-            m[qt] = -INFINITY;
-            l[qt] = 0.f;
+        for (int qt = 0; qt < NQ; ++qt) o[qt] = f32x16{};
+        if (tid < 32 * NQ) {
+            sm[tid / 32][tid % 32] = -INFINITY;
+            sl[tid / 32][tid % 32] = 0.f;
         }
     };
     reset();
@@ -252,15 +259,19 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
         const int kvalid = (int)(cp.j1 - cp.j < TK ? cp.j1 - cp.j : TK);
 #pragma unroll
         for (int qt = 0; qt < NQ; ++qt) {
-            if (qt >= nq) continue;
+            if (qt >= nq || ct != (sg + qt) % NC) continue;     // uniform per wave
             // L^T = K Q^T for this stage's 32 keys (lane: query qt*32 + l32)
             f32x16 lt = {};
             const uint16_t* qr = sq + (qt * 32 + l32) * P + 8 * hh;
             const uint16_t* kr = sk + l32 * P + 8 * hh;
+            // four k-steps of operands at a time keep the register footprint
+            // (and so the occupancy) down
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int s = 0; s < KS; ++s) {
                 lt = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
                             as_bf16x8(*reinterpret_cast<const u16x8*>(qr + 16 * s)), lt);
+                if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
             float mt = -INFINITY;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
@@ -270,8 +281,9 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
                 mt = fmaxf(mt, xv);
             }
             mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float mn = fmaxf(m[qt], mt);
-            const float corr = __builtin_amdgcn_exp2f(m[qt] - mn);   // 0 on the first stage
+            const float mo = sm[qt][l32];
+            const float mn = fmaxf(mo, mt);
+            const float corr = __builtin_amdgcn_exp2f(mo - mn);     // 0 on the piece's first stage
             float ls = 0.f;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
@@ -280,8 +292,28 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
                 ls += p;
             }
             ls += __shfl_xor(ls, 32);
-            l[qt] = l[qt] * corr + ls;
-            m[qt] = mn;
+            const float ln = sl[qt][l32] * corr + ls;
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+                float pp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pp[e] = lt[8 * gp + e];
+                bf16x8 phi, plo;
+                split_hi_lo(pp, phi, plo);
+                sp[qt][gp][0][lane] = __builtin_bit_cast(u16x8, phi);
+                sp[qt][gp][1][lane] = __builtin_bit_cast(u16x8, plo);
+            }
+            if (hh == 0) {
+                sm[qt][l32] = mn;
+                sl[qt][l32] = ln;
+                scorr[qt][l32] = corr;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) {
+            if (qt >= nq) continue;
+            const float corr = scorr[qt][l32];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) o[qt][rr] *= corr;
 #pragma unroll
@@ -295,13 +327,8 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
                     vop[e] = static_cast<uint16_t>(v0[e]);
                     vop[4 + e] = static_cast<uint16_t>(v1[e]);
                 }
-                float pp[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pp[e] = lt[8 * gp + e];
-                bf16x8 phi, plo;
-                split_hi_lo(pp, phi, plo);
-                o[qt] = mfma32(as_bf16x8(vop), phi, o[qt]);
-                o[qt] = mfma32(as_bf16x8(vop), plo, o[qt]);
+                o[qt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][gp][0][lane]), o[qt]);
+                o[qt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][gp][1][lane]), o[qt]);
             }
         }
         ++sg;
@@ -316,17 +343,15 @@ __global__ __launch_bounds__(D / 32 * kWave) void exact_slices_bf16_mfma(ExactAr
 #pragma unroll
                 for (int e = 0; e < 16; ++e) slotp[(int64_t)i * D + 32 * ct + 16 * hh + e] = o[qt][e];
                 if (ct == 0 && hh == 0) {
-                    slotp[RB * D + i] = m[qt];
-                    slotp[RB * D + RB + i] = l[qt];
+                    slotp[RB * D + i] = sm[qt][l32];
+                    slotp[RB * D + RB + i] = sl[qt][l32];
                 }
             }
+            __syncthreads();                       // the running max / sum are read before they are reset
             reset();
             cp.j = cp.j1;
             exact_next_piece(a, cp);
-            if (cp.live) {
-                __syncthreads();                   // every wave is done with the old query block
-                load_q();
-            }
+            if (cp.live) load_q();                 // every wave passed the barrier: the old block is done
         } else {
             cp.j += TK;
         }

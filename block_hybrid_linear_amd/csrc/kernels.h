@@ -70,16 +70,21 @@ struct ExactArgs {
 };
 
 // Slice workgroups of the exact step: as many as the 256 compute units of an
-// MI355X hold at once for the matrix-core variant of (d, blk) -- its waves
-// per SIMD (3, 2, 1 for one, two, four query tiles) times 4 SIMDs over its
-// d / 32 waves per workgroup -- so the balanced split runs in one round.
+// MI355X hold at once for the matrix-core variant of (d, blk), so the
+// balanced split runs in one round.  Per compute unit that is the smaller of
+// 4 SIMDs x waves per SIMD (3, 2, 1 for one, two, four query tiles) / (d / 32)
+// waves per workgroup and what its LDS footprint allows out of 160 KB.
 // Fixed per (d, blk), so results do not depend on the device.
 inline int exact_slices(int d, int blk)
 {
+    const int t = blk <= 32 ? 0 : (blk <= 64 ? 1 : 2);
+    static const int per_cu[3][3] = {{9, 6, 4},      // d = 32
+                                     {5, 4, 2},      // d = 64
+                                     {3, 2, 1}};     // d = 128
     if (d != 32 && d != 64 && d != 128) return 1024;
-    const int waves_per_simd = blk <= 32 ? 3 : (blk <= 64 ? 2 : 1);
-    return 256 * waves_per_simd * 4 / (d / 32);
+    return 256 * per_cu[d == 32 ? 0 : (d == 64 ? 1 : 2)][t];
 }
+
 // Rows of one partial slot: the query rows of the kernel that runs for blk
 // (one, two or four 32-row tiles).  A slot holds rows x d unnormalised
 // outputs, then the running max and the running sum of each row.

@@ -222,8 +222,8 @@ ha_status hybrid_exact_step(const void* q, const void* k, const void* v,
 /* Workspace size for hybrid_exact_step (host): a 256-byte-padded plan of
  * n_req + 2 int64, then (W + n_req * heads) partials of R * (d + 2) floats,
  * R = 32, 64 or 128 for blk <= 32, <= 64 or <= 128, and W the number of
- * slice workgroups: 256 * (3, 2 or 1 for the same blk ranges) * 4 / (d / 32)
- * for d >= 32, 1024 for d = 16.  0 for empty or invalid sizes. */
+ * slice workgroups, 256 x (9, 6, 4 | 5, 4, 2 | 3, 2, 1) for d = 32 | 64 | 128
+ * and the same blk ranges, 1024 for d = 16.  0 for empty or invalid sizes. */
 size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads,
                                          int32_t blk, int32_t d);
 

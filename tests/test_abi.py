@@ -208,8 +208,8 @@ def test_prefill_workspace_size(lib):
 def test_exact_workspace_size(lib):
     """Plan as for prefill + (slices + n_req * heads) partials of R rows x
     (d + 2) floats (output row, max, sum), R = 32 / 64 / 128 for blk up to
-    32 / 64 / 128; slices = 256 x (3, 2, 1 waves per SIMD) x 4 / (d / 32)
-    for d >= 32, else 1024."""
+    32 / 64 / 128; slices = 256 x workgroups per compute unit of the
+    variant, 1024 for d = 16."""
     f = bh.hybrid_exact_step_workspace_bytes
     plan = lambda n: ((n + 2) * 8 + 255) // 256 * 256  # noqa: E731
     assert f(64, 32, 32, 128) == plan(64) + (768 + 2048) * 32 * 130 * 4
@@ -217,7 +217,8 @@ def test_exact_workspace_size(lib):
     assert f(2, 3, 65, 32) == plan(2) + (1024 + 6) * 128 * 34 * 4
     assert f(1, 1, 128, 64) == plan(1) + (512 + 1) * 128 * 66 * 4
     assert f(5, 2, 40, 64) == plan(5) + (1024 + 10) * 64 * 66 * 4
-    assert f(5, 2, 8, 32) == plan(5) + (3072 + 10) * 32 * 34 * 4
+    assert f(5, 2, 8, 32) == plan(5) + (2304 + 10) * 32 * 34 * 4
+    assert f(1, 1, 100, 128) == plan(1) + (256 + 1) * 128 * 130 * 4
     assert f(0, 1, 32, 64) == 0 and f(2, 2, 0, 64) == 0 and f(2, 2, 129, 64) == 0
 
 

@@ -290,8 +290,16 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     constexpr int P = D + 8;
     constexpr int CPR = D / 8;
     constexpr int CPT = R * CPR / NT;
-    static_assert(CPT * NT == R * CPR, "even staging split");
+    // Two query tiles: S^T is staged in LDS (one workgroup per compute unit
+    // fits).  One tile: each wave keeps its S^T operands in registers, as the
+    // step kernel does, so that several workgroups share a compute unit, and
+    // the commit re-reads the old tile from L2.
+    constexpr bool kStageS = NKT > 1;
+    constexpr int PS = D + 4;               // LDS row pitch of the state tile (fp32)
+    constexpr int SPT = D * D / 4 / NT;     // 16-byte state chunks per thread
+    static_assert(CPT * NT == R * CPR && SPT * NT * 4 == D * D, "even staging split");
     __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
+    __shared__ __attribute__((aligned(16))) float ss[kStageS ? D * PS : 4];   // the unit's S^T
 
     const int unit = blockIdx.x;
     const int r = unit / a.heads, h = unit % a.heads;
@@ -325,12 +333,20 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
         ck[u] = *reinterpret_cast<const u32x4*>(k + off);
         cv[u] = *reinterpret_cast<const u32x4*>(v + off);
     }
+    // the unit's S^T (D x D fp32, contiguous) with whole-row coalesced loads,
+    // or this wave's S^T operands
+    f32x4 sc[kStageS ? SPT : 1];
     f32x4 sraw[KS][2];
-    const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
+    if constexpr (kStageS) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        sraw[s][0] = srow[4 * s];
-        sraw[s][1] = srow[4 * s + 1];
+        for (int u = 0; u < SPT; ++u) sc[u] = reinterpret_cast<const f32x4*>(st)[tid + u * NT];
+    } else {
+        const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sraw[s][0] = srow[4 * s];
+            sraw[s][1] = srow[4 * s + 1];
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -340,6 +356,13 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
         *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
         *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
     }
+    if constexpr (kStageS) {
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int c4 = tid + u * NT, row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
+            *reinterpret_cast<f32x4*>(ss + row * PS + col) = sc[u];
+        }
+    }
     __syncthreads();
 
     // ---- the step, from the old state
@@ -347,8 +370,15 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const float sv8[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
-                              sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
+        f32x4 s0, s1;
+        if constexpr (kStageS) {
+            s0 = *reinterpret_cast<const f32x4*>(ss + cA * PS + 16 * s + 8 * hh);
+            s1 = *reinterpret_cast<const f32x4*>(ss + cA * PS + 16 * s + 8 * hh + 4);
+        } else {
+            s0 = sraw[s][0];
+            s1 = sraw[s][1];
+        }
+        const float sv8[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
         bf16x8 shi, slo;
         split_hi_lo(sv8, shi, slo);
         const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
@@ -376,8 +406,14 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
         // accumulator register rr of lane (l32, hh): row 32 ct + 16 hh + rr, feature 32 ft + l32
         float* tile = st + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
         f32x16 acc;
+        if constexpr (kStageS) {
+            const float* old = ss + (32 * ct + 16 * hh) * PS + 32 * ft + l32;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
+            for (int rr = 0; rr < 16; ++rr) acc[rr] = old[rr * PS];
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
+        }
         const int kcol = 32 * ft + 16 * (g % 2) + 4 * (jl % 4);
 #pragma unroll
         for (int jt = 0; jt < NKT; ++jt) {

@@ -12,12 +12,13 @@ resident in HBM before timing; each step's Q/K/V are distinct tensors.
 
 Reported value: tokens/s through the hybrid layer, where a prompt token
 counts once (folded into S) and an active-block token counts once per
-denoising step.  The timed steps replay the step's calls captured once as a
-HIP graph (``--eager`` times the calls launched one by one instead).  K eager
-steps with HIP events around every call, on the stream the kernels run on,
-give each call's achieved GB/s and TFLOP/s against the MI355X peaks (8 TB/s
-HBM, 2.5 PFLOP/s dense bf16); ``roofline`` reports the call with the largest
-share of the time.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample
+denoising step.  The K timed steps run back to back as replays of the step's
+calls captured once as a HIP graph, in one window bracketed by
+synchronisations (``--eager`` times the calls launched one by one instead).
+K eager steps with HIP events around every call, on the stream the kernels
+run on, give each call's achieved GB/s and TFLOP/s against the MI355X peaks
+(8 TB/s HBM, 2.5 PFLOP/s dense bf16); ``roofline`` reports the call with the
+largest share of the time.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample
 of the same workload's (request, head) units and scales it to tokens/s.
 ``context`` times, for comparison only, the hybrid step against the exact
 full-prefix step it replaces at the concurrent-serving shapes.
@@ -27,6 +28,7 @@ full-prefix step it replaces at the concurrent-serving shapes.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -86,16 +88,23 @@ def exact_cost(prefix_token_heads, units, B, d, e=2):
 # ---------------------------------------------------------------------------
 
 class Job:
-    """Inputs resident in HBM plus the list of calls of one bench step."""
+    """Inputs resident in HBM plus the calls of one bench step.
+
+    A step whose distinct inputs are smaller than ROTATE_BYTES (the serving
+    step: 201 MB) gets several input sets, used in turn by successive steps,
+    so that its inputs come from HBM and not from the 256 MB last-level
+    cache; set 0 is the seeded workload itself."""
+
+    ROTATE_BYTES = 1 << 30
 
     def __init__(self, wl, dev="cuda"):
         self.wl = wl
         self.dev = dev
         n, H, d, B = wl.n_req, wl.heads, wl.d, wl.blk
         self.slots = torch.arange(n, dtype=torch.int32, device=dev)
-        self.state = torch.zeros(n, H, d, d, device=dev)
         self.tokens = 0
         self.cost = {}           # kind -> (bytes, flops) per call
+        per_set = n * H * d * d * 4 + wl.n_blocks * wl.steps_per_block * 3 * n * B * H * d * 2
         if wl.prompt_range:
             lens = synth.uniform_int(n, *wl.prompt_range, synth.seed_of(wl.index, tensor=synth.TENSOR_LEN))
             self.prompt_lens = lens
@@ -110,73 +119,79 @@ class Job:
                                   dtype=torch.uint8, device=dev)
             self.tokens += total
             self.cost["prefill"] = prefill_cost(total * H, n * H, d)
-        self.q, self.k, self.v = [], [], []
-        for b in range(wl.n_blocks):
-            for t in range(wl.steps_per_block):
-                s = lambda tid: synth.seed_of(wl.index, b, t, tid)  # noqa: E731
-                self.q.append(synth.normal((n, B, H, d), s(0), std=wl.std, device=dev))
-                self.k.append(synth.normal((n, B, H, d), s(1), std=wl.std, device=dev))
-                self.v.append(synth.normal((n, B, H, d), s(2), std=wl.std, device=dev))
-                self.tokens += n * B
-        self.out = torch.empty(n, B, H, d, dtype=torch.bfloat16, device=dev)
+            per_set += total * H * d * 2 * 2
+        self.n_sets = 1 if wl.prompt_range else max(1, min(8, -(-self.ROTATE_BYTES // per_set)))
+        self.sets = []
+        for r in range(self.n_sets):
+            st = {"state": torch.zeros(n, H, d, d, device=dev), "q": [], "k": [], "v": [],
+                  "out": torch.empty(n, B, H, d, dtype=torch.bfloat16, device=dev)}
+            for b in range(wl.n_blocks):
+                for t in range(wl.steps_per_block):
+                    s = lambda tid: synth.seed_of(wl.index, b, t, tid) + 500_000 * r  # noqa: E731
+                    for name, tid in (("q", 0), ("k", 1), ("v", 2)):
+                        st[name].append(synth.normal((n, B, H, d), s(tid), std=wl.std, device=dev))
+            self.sets.append(st)
+        self.tokens += wl.n_blocks * wl.steps_per_block * n * B
         self.cost["step"] = step_cost(n * H, B, d)
         self.cost["step_commit"] = step_commit_cost(n * H, B, d)
-        self.calls = self.prepare(None)
+        self.calls = [self.prepare(None, r) for r in range(self.n_sets)]
 
-    def prepare(self, stream):
-        """The step's calls, each validated and marshalled once and re-enqueued
-        with one ctypes call (as a serving loop would), on `stream` (None =
-        the current stream)."""
-        wl = self.wl
+    def prepare(self, stream, r=0):
+        """The step's calls on input set r, each validated and marshalled once
+        and re-enqueued with one ctypes call (as a serving loop would), on
+        `stream` (None = the current stream)."""
+        wl, st = self.wl, self.sets[r]
         calls = []
         if wl.prompt_range:
-            calls.append(("prefill", bh.prepare_prefill(self.pk, self.pv, self.cu, self.state, self.slots,
+            calls.append(("prefill", bh.prepare_prefill(self.pk, self.pv, self.cu, st["state"], self.slots,
                                                         max_len=self.max_len, chunk=wl.chunk, workspace=self.ws,
                                                         stream=stream)))
         commits = wl.n_blocks > 1 or wl.steps_per_block > 1
         i = 0
         for b in range(wl.n_blocks):
             for t in range(wl.steps_per_block):
+                args = (st["q"][i], st["k"][i], st["v"][i], st["state"], self.slots, st["out"])
                 if commits and t == wl.steps_per_block - 1:
                     # the block's last step, fused with the commit of its K, V
-                    calls.append(("step_commit", bh.prepare_step_commit(
-                        self.q[i], self.k[i], self.v[i], self.state, self.slots, self.out, scale=wl.scale,
-                        stream=stream)))
+                    calls.append(("step_commit", bh.prepare_step_commit(*args, scale=wl.scale, stream=stream)))
                 else:
-                    calls.append(("step", bh.prepare_step(self.q[i], self.k[i], self.v[i], self.state, self.slots,
-                                                          self.out, scale=wl.scale, stream=stream)))
+                    calls.append(("step", bh.prepare_step(*args, scale=wl.scale, stream=stream)))
                 i += 1
         return calls
 
     def reset(self):
-        self.state.zero_()
+        for st in self.sets:
+            st["state"].zero_()
 
-    def run(self, events=None, calls=None):
-        for kind, fn in (calls or self.calls):
+    def run(self, step, events=None, calls=None):
+        """Enqueue one step; with `events` (pre-created (kind, start, end)
+        triples, one per call) each call is bracketed by its pair."""
+        for c, (kind, fn) in enumerate(calls or self.calls[step % self.n_sets]):
             if events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
+                events[c][1].record()
                 fn()
-                e1.record()
-                events.append((kind, e0, e1))
+                events[c][2].record()
             else:
                 fn()
 
     def capture(self):
-        """The whole step captured once as a HIP graph (every kernel of every
-        call; no allocation, copy or memset inside)."""
-        side = torch.cuda.Stream()
-        calls = self.prepare(side)
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            self.run(calls=calls)                 # warm-up on the capture stream
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            self.run(calls=calls)
-        torch.cuda.synchronize()
-        return g
+        """Each input set's whole step captured once as a HIP graph (every
+        kernel of every call; no allocation, copy or memset inside)."""
+        graphs = []
+        for r in range(self.n_sets):
+            side = torch.cuda.Stream()
+            calls = self.prepare(side, r)
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self.run(r, calls=calls)                 # warm-up on the capture stream
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                self.run(r, calls=calls)
+            torch.cuda.synchronize()
+            graphs.append(g)
+        return graphs
 
 
 # ---------------------------------------------------------------------------
@@ -195,8 +210,9 @@ def cpu_baseline(job: Job, budget_s: float) -> dict:
         hs = slice(0, h_s)
         pk = job.pk[:, hs].cpu() if wl.prompt_range else None
         pv = job.pv[:, hs].cpu() if wl.prompt_range else None
-        qkv = [(job.q[i][:, :, hs].cpu(), job.k[i][:, :, hs].cpu(), job.v[i][:, :, hs].cpu())
-               for i in range(len(job.q))]
+        st = job.sets[0]
+        qkv = [(st["q"][i][:, :, hs].cpu(), st["k"][i][:, :, hs].cpu(), st["v"][i][:, :, hs].cpu())
+               for i in range(len(st["q"]))]
         import numpy as np
         t0 = time.perf_counter()
         S = np.zeros((n, h_s, wl.d, wl.d))
@@ -359,52 +375,58 @@ def main():
     log(f"[bench] building inputs for {wl.name}")
     job = Job(wl)
     torch.cuda.synchronize()
-    log(f"[bench] {len(job.calls)} calls per step, {job.tokens} tokens per step; warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"[bench] {len(job.calls[0])} calls per step, {job.tokens} tokens per step, {job.n_sets} input set(s); "
+        f"warmup {args.warmup}")
+    for w in range(args.warmup):
         job.reset()
-        job.run()
+        job.run(w)
     torch.cuda.synchronize()
 
-    # ---- per-call timings: K eager steps with HIP events around every call,
-    # on the stream the kernels run on
-    events = []
-    eager_ms = []
+    # ---- per-call timings: K eager steps back to back with HIP events around
+    # every call, on the stream the kernels run on.  The events are created
+    # beforehand, the garbage collector is paused, and a spin kernel is queued
+    # first (50 us per call, at least 20 ms), so that the host has enqueued
+    # the steps before the GPU reaches them: the intervals time the kernels,
+    # not host-side gaps.
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    plan = [[(kind, ev(), ev()) for kind, _ in job.calls[s % job.n_sets]] for s in range(args.steps)]
+    n_calls = sum(len(p) for p in plan)
+    gc.collect()
+    gc.disable()
+    job.reset()
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * max(0.02, 50e-6 * n_calls)))
+    a.record()
     for s in range(args.steps):
-        job.reset()                       # a fresh generation; not inside the timed interval
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        job.run(events)
-        b.record()
-        torch.cuda.synchronize()
-        eager_ms.append(a.elapsed_time(b))
-        log(f"[bench] eager step {s}: {eager_ms[-1]:.3f} ms")
-
-    # ---- timed region: K whole steps, each the step's calls replayed as one
-    # captured HIP graph (the same kernels and arguments, without per-launch
-    # host overhead), bracketed by synchronisations
+        job.run(s, plan[s])
+    b.record()
+    torch.cuda.synchronize()
+    events = [e for p in plan for e in p]
+    eager_ms = [a.elapsed_time(b) / args.steps] * args.steps
+    log(f"[bench] {args.steps} eager steps: {a.elapsed_time(b):.3f} ms")
     step_ms = eager_ms
     mode = "eager"
-    if not args.eager:
-        g = job.capture()
-        for _ in range(args.warmup):
-            job.reset()
-            g.replay()
-        torch.cuda.synchronize()
-        step_ms = []
-        mode = "hip_graph"
-        for s in range(args.steps):
-            job.reset()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            step_ms.append(a.elapsed_time(b))
-            log(f"[bench] graph step {s}: {step_ms[-1]:.3f} ms")
-        del g
     total_ms = sum(step_ms)
+    if not args.eager:
+        # the K steps back to back (input sets in turn; the state is reset
+        # once, before the window), bracketed by synchronisations
+        graphs = job.capture()
+        for w in range(args.warmup):
+            graphs[w % job.n_sets].replay()
+        job.reset()
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for s in range(args.steps):
+            graphs[s % job.n_sets].replay()
+        b.record()
+        torch.cuda.synchronize()
+        total_ms = a.elapsed_time(b)
+        mode = "hip_graph"
+        log(f"[bench] {args.steps} graph steps: {total_ms:.3f} ms")
+        del graphs
+    gc.enable()
     ms_per_step = total_ms / args.steps
     eager_ms_per_step = sum(eager_ms) / args.steps
 
@@ -437,7 +459,8 @@ def main():
         "config": {"workload": wl.name, "n_req": wl.n_req, "heads": wl.heads, "head_dim": wl.d,
                    "block": wl.blk, "blocks": wl.n_blocks, "steps_per_block": wl.steps_per_block,
                    "prompt_range": list(wl.prompt_range) or None, "chunk": wl.chunk if wl.prompt_range else None,
-                   "qkv_std": wl.std, "tokens_per_step": job.tokens, "parallelism": "single_gpu",
+                   "qkv_std": wl.std, "tokens_per_step": job.tokens, "input_sets": job.n_sets,
+                   "parallelism": "single_gpu",
                    "source_digest": source_digest()},
         "roofline": roofline,
         "timing": {"mode": mode, "eager_ms_per_step": round(eager_ms_per_step, 4),

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 // barrier and written once after it, by one wave; a unit's state is touched
 // by one workgroup, so requests only need distinct slots.
 // ---------------------------------------------------------------------------
-template <int D, int NKT>
+template <int D, int NKT, bool kCommit>
 __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;
@@ -318,7 +318,8 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     const uint16_t* k = static_cast<const uint16_t*>(a.k) + base;
     const uint16_t* v = static_cast<const uint16_t*>(a.v) + base;
     uint16_t* out = static_cast<uint16_t*>(a.out) + base;
-    float* st = a.state_rw + ((int64_t)slot * a.heads + h) * D * D;
+    const int64_t soff = ((int64_t)slot * a.heads + h) * D * D;
+    const float* st = (kCommit ? a.state_rw : a.state) + soff;
 
     const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
     const int last = Br - 1;
@@ -397,6 +398,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
             *reinterpret_cast<u32x4*>(out + (int64_t)row * rs + c8) = *reinterpret_cast<const u32x4*>(sq + row * P + c8);
     }
 
+    if constexpr (!kCommit) return;
     // ---- the commit: S^T[c][f] += sum_j V[j][c] ReLU(K[j][f]) over j < Br
     __builtin_amdgcn_sched_barrier(0);
     const int g = lane / 16, jl = lane % 16;
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 #pragma unroll 1
     for (int ft = qt; ft < NC; ft += NKT) {
         // accumulator register rr of lane (l32, hh): row 32 ct + 16 hh + rr, feature 32 ft + l32
-        float* tile = st + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
+        float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
         f32x16 acc;
         if constexpr (kStageS) {
             const float* old = ss + (32 * ct + 16 * hh) * PS + 32 * ft + l32;
@@ -635,16 +637,16 @@ hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
         const dim3 block((two ? 2 : 1) * a.d / 32 * kWave);
         switch (a.d) {
         case 32:
-            if (two) step_commit_bf16_mfma<32, 2><<<units, block, 0, stream>>>(a);
-            else step_commit_bf16_mfma<32, 1><<<units, block, 0, stream>>>(a);
+            if (two) step_commit_bf16_mfma<32, 2, true><<<units, block, 0, stream>>>(a);
+            else step_commit_bf16_mfma<32, 1, true><<<units, block, 0, stream>>>(a);
             break;
         case 64:
-            if (two) step_commit_bf16_mfma<64, 2><<<units, block, 0, stream>>>(a);
-            else step_commit_bf16_mfma<64, 1><<<units, block, 0, stream>>>(a);
+            if (two) step_commit_bf16_mfma<64, 2, true><<<units, block, 0, stream>>>(a);
+            else step_commit_bf16_mfma<64, 1, true><<<units, block, 0, stream>>>(a);
             break;
         default:
-            if (two) step_commit_bf16_mfma<128, 2><<<units, block, 0, stream>>>(a);
-            else step_commit_bf16_mfma<128, 1><<<units, block, 0, stream>>>(a);
+            if (two) step_commit_bf16_mfma<128, 2, true><<<units, block, 0, stream>>>(a);
+            else step_commit_bf16_mfma<128, 1, true><<<units, block, 0, stream>>>(a);
             break;
         }
         return hipGetLastError();

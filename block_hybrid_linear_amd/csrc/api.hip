@@ -143,7 +143,7 @@ size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads, int32_
     (void)max_len;
     if (n_req <= 0 || heads <= 0 || d <= 0 || chunk <= 0) return 0;
     return plan_bytes(n_req) +
-           ((size_t)ha::prefill_slices(d) + (size_t)n_req * (size_t)heads) * (size_t)d * (size_t)d * sizeof(float);
+           ((size_t)ha::prefill_slices(d, 1) + (size_t)n_req * (size_t)heads) * (size_t)d * (size_t)d * sizeof(float);
 }
 
 ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_seqlens,
@@ -183,7 +183,8 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
     a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_bytes(n_req));
     a.total_tokens = total_tokens;
     a.chunk = chunk;
-    a.slices = ha::prefill_slices(d);
+    a.hp = ha::prefill_group(d, heads, dtype == HA_BF16);
+    a.slices = ha::prefill_slices(d, a.hp);
     a.n_req = n_req;
     a.n_slots = n_slots;
     a.heads = heads;

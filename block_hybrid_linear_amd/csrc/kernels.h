@@ -38,14 +38,20 @@ struct PhiKVArgs {
     int64_t total_tokens;       // prefill
     int32_t chunk;              // prefill
     int32_t slices;             // prefill
+    int32_t hp;                 // prefill: heads per unit (1 or 2, divides heads)
     int32_t n_req, n_slots, heads, blk, d;
     bool dtype_bf16;
 };
 
-// Number of prefill slice workgroups for head dim d (two per compute unit of
-// an MI355X for the 4-wave kernels).  Fixed per d, so results do not depend
-// on the device.
-inline int prefill_slices(int d) { return d == 32 ? 2048 : 512; }
+// Heads per prefill unit: bf16 with d = 128 and an even head count streams two
+// adjacent heads per workgroup (512 contiguous bytes per token row).
+inline int prefill_group(int d, int heads, bool bf16) { return bf16 && d == 128 && heads % 2 == 0 ? 2 : 1; }
+
+// Number of prefill slice workgroups for head dim d and hp heads per unit
+// (two 4-wave or one 8-wave workgroup per compute unit of an MI355X).  Fixed
+// per (d, hp), so results do not depend on the device.  slices * hp is the
+// same for both hp, and so is the workspace.
+inline int prefill_slices(int d, int hp) { return (d == 32 ? 2048 : 512) / hp; }
 
 // Exact softmax attention of the active block over [prefix; block] (the step
 // without linearisation).  The (request, head, key chunk) list is split into

@@ -47,16 +47,21 @@ template <> struct PhiKVShape<128> { static constexpr int NW = 4, T = 64; };
 template <> struct PhiKVShape<64> { static constexpr int NW = 4, T = 128; };
 template <> struct PhiKVShape<32> { static constexpr int NW = 1, T = 64; };
 
-template <int D>
+// HP adjacent heads per workgroup (prefill with d = 128 takes two: their
+// columns are contiguous in a token row, so every load instruction reads two
+// whole 512-byte row segments, which HBM serves measurably faster than
+// 256-byte ones).  The LDS tiles then hold HP * D rows; wave w works on head
+// w / (NW / HP) of the group.
+template <int D, int HP = 1>
 struct PhiKVTile {
-    static constexpr int NW = PhiKVShape<D>::NW, T = PhiKVShape<D>::T;
-    static constexpr int NT = D / 32;                   // tiles per dimension
-    static constexpr int TPW = NT * NT / NW;            // tiles per wave
+    static constexpr int NW = PhiKVShape<D>::NW * HP, T = PhiKVShape<D>::T;
+    static constexpr int NT = D / 32;                   // tiles per dimension (per head)
+    static constexpr int TPW = NT * NT * HP / NW;       // tiles per wave
     static constexpr int PITCH = T + 8;                 // LDS row pitch in bf16 (16 B pad)
-    static constexpr int CG = D / 8;                    // 8-column groups per token row
+    static constexpr int CG = HP * D / 8;               // 8-column groups per token row segment
     static_assert(2 * (T / 8) * CG == NW * kWave, "one 8x8 block per thread per stage");
     static constexpr bool kColsFast = D == 128;         // lane mapping, see above
-    typedef uint16_t Lds[2][2][D * PITCH];              // [buf][K^T, V^T]
+    typedef uint16_t Lds[2][2][HP * D * PITCH];         // [buf][K^T, V^T]
     __device__ __forceinline__ static int row(int c) { return kColsFast ? (c & ~15) | ((c + (c >> 4)) & 15) : c; }
     // element offset of token group g (8 tokens) of logical LDS row c
     __device__ __forceinline__ static int slot(int c, int g) { return row(c) * PITCH + 8 * g; }
@@ -150,16 +155,17 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
     __syncthreads();   // LDS is reused by the caller's next range
 }
 
-// Writes (store = true) or reads (store = false) one wave's tiles of a d x d state.
-template <int D>
-__device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[PhiKVTile<D>::TPW], bool store)
+// Writes (store = true) or reads (store = false) the tiles of a d x d state
+// that wave w of the WPH waves working on it holds.
+template <int D, int WPH = PhiKVShape<D>::NW>
+__device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (D / 32) / WPH], bool store, int w)
 {
-    using P = PhiKVTile<D>;
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    constexpr int NT = D / 32, TPW = NT * NT / WPH;
+    const int lane = threadIdx.x % kWave;
     const int l32 = lane % 32, hh = lane / 32;
 #pragma unroll
-    for (int u = 0; u < P::TPW; ++u) {
-        const int t = w * P::TPW + u, ct = t / P::NT, ft = t % P::NT;
+    for (int u = 0; u < TPW; ++u) {
+        const int t = w * TPW + u, ct = t / NT, ft = t % NT;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             const int c = ct * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
@@ -188,19 +194,21 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(Ph
     const int64_t off = (int64_t)r * a.blk * rs + (int64_t)h * D;
     float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
     f32x16 acc[P::TPW];
-    tiles_io<D>(st, acc, false);
+    tiles_io<D>(st, acc, false, threadIdx.x / kWave);
     phikv_accumulate<D, 1>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
                            Br, lds, acc);
-    tiles_io<D>(st, acc, true);
+    tiles_io<D>(st, acc, true, threadIdx.x / kWave);
 }
 
 // ---------------------------------------------------------------------------
-// Prefill, step 1 (one workgroup): the plan.  Prompt r is cut into
-// nch_r = ceil(L_r / chunk) chunks per head; the (request, head, chunk) list
-// is laid out request by request, head by head.  plan[r] = heads * sum over
-// r' < r of nch_r' (exclusive prefix), plan[n_req] = C (all chunks) and
-// plan[n_req + 1] = chunks per slice ceil(C / slices).  Malformed offsets
-// (outside [0, total_tokens] or decreasing) count as empty prompts.
+// Prefill, step 1 (one workgroup): the plan.  A unit is a group of hp
+// adjacent heads of one prompt (hp = 1 or 2, upr = heads / hp units per
+// request).  Prompt r is cut into nch_r = ceil(L_r / chunk) chunks per unit;
+// the (request, unit, chunk) list is laid out request by request, unit by
+// unit.  plan[r] = upr * sum over r' < r of nch_r' (exclusive prefix),
+// plan[n_req] = C (all chunks) and plan[n_req + 1] = chunks per slice
+// ceil(C / slices).  Malformed offsets (outside [0, total_tokens] or
+// decreasing) count as empty prompts.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t chunks_of(const PhiKVArgs& a, int r)
 {
@@ -226,12 +234,13 @@ __global__ __launch_bounds__(256) void prefill_plan(PhiKVArgs a)
     }
     __syncthreads();
     int64_t run = part[tid];
+    const int upr = a.heads / a.hp;
     for (int r = r0; r < r1; ++r) {
-        a.plan[r] = run * a.heads;
+        a.plan[r] = run * upr;
         run += chunks_of(a, r);
     }
     if (tid == 0) {
-        const int64_t C = part[256] * a.heads;
+        const int64_t C = part[256] * upr;
         a.plan[n] = C;
         const int64_t S = (C + a.slices - 1) / a.slices;
         a.plan[n + 1] = S > 0 ? S : 1;
@@ -242,9 +251,10 @@ __global__ __launch_bounds__(256) void prefill_plan(PhiKVArgs a)
 // Prefill, step 2: slice workgroups.  Workgroup w owns the chunk range
 // [w S, (w+1) S) of the flat list -- the same number of chunks for every
 // workgroup, whatever the prompt lengths -- and writes one fp32 partial state
-// per (request, head) unit u its range touches, into slot w + u.  (Slot
-// w + u is unique: slices and units are both consecutive intervals of the
-// same list, so a later slice never overlaps an earlier unit.)
+// per head of each unit u its range touches, into slot w + u (hp states per
+// slot).  (Slot w + u is unique: slices and units are both consecutive
+// intervals of the same list, so a later slice never overlaps an earlier
+// unit.)
 // ---------------------------------------------------------------------------
 struct SliceCursor {
     int r;              // request
@@ -267,21 +277,22 @@ __device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur
     return true;
 }
 
-// Next piece of the slice: unit (r, h), token rows [t0, t1) of prompt r,
-// whose first row starts at element p0 of k and v.
+// Next piece of the slice: unit h of prompt r (heads hp h .. hp h + hp - 1),
+// token rows [t0, t1) of prompt r, whose first row starts at element p0 of k
+// and v.
 __device__ __forceinline__ void slice_piece(const PhiKVArgs& a, SliceCursor& cur, int& h, int64_t& t0, int64_t& t1,
                                             int64_t& p0)
 {
     while (uniform_load(a.plan, cur.r + 1) <= cur.c0) ++cur.r;   // skip finished and empty prompts
     const int64_t pr = uniform_load(a.plan, cur.r);
-    const int64_t nch = (uniform_load(a.plan, cur.r + 1) - pr) / a.heads;
+    const int64_t nch = (uniform_load(a.plan, cur.r + 1) - pr) / (a.heads / a.hp);
     const int64_t local = cur.c0 - pr;
     h = (int)(local / nch);
     const int64_t k0 = local % nch;
     const int64_t k1 = (k0 + (cur.c1 - cur.c0) < nch) ? k0 + (cur.c1 - cur.c0) : nch;
     const int64_t s0 = uniform_load(a.cu, cur.r);
     const int64_t L = uniform_load(a.cu, cur.r + 1) - s0;
-    p0 = s0 * a.heads * a.d + (int64_t)h * a.d;
+    p0 = s0 * a.heads * a.d + (int64_t)h * a.hp * a.d;
     t0 = k0 * a.chunk;
     t1 = k1 * a.chunk < L ? k1 * a.chunk : L;
     cur.c0 += k1 - k0;
@@ -312,11 +323,12 @@ __device__ __forceinline__ void stage_advance(const PhiKVArgs& a, StageCursor& s
     if (s.t >= s.t1) stage_next_piece(a, s);
 }
 
-template <int D>
-__global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_bf16_mfma(PhiKVArgs a)
+template <int D, int HP>
+__global__ __launch_bounds__(PhiKVShape<D>::NW * HP * kWave, 2 / HP) void prefill_slices_bf16_mfma(PhiKVArgs a)
 {
-    using P = PhiKVTile<D>;
+    using P = PhiKVTile<D, HP>;
     constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG;
+    constexpr int WPH = P::NW / HP;            // waves per head
     __shared__ __attribute__((aligned(16))) typename P::Lds lds;
     StageCursor cp, ld;                        // compute and load cursors
     if (!slice_begin(a, cp.sl)) return;
@@ -329,6 +341,7 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_b
     const int tid = threadIdx.x;
     const int lane = tid % kWave, w = tid / kWave;
     const int l32 = lane % 32, hh = lane / 32;
+    const int hw = w / WPH, w4 = w % WPH;                // this wave's head in the group, its index there
     const int blocks_per_tensor = (T / 8) * CG;
     const int tensor = tid / blocks_per_tensor;          // 0 = K, 1 = V
     const int bidx = tid % blocks_per_tensor;
@@ -379,9 +392,9 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_b
             const int g = 2 * s + hh;
 #pragma unroll
             for (int u = 0; u < TPW; ++u) {
-                const int t = w * TPW + u, ct = t / NT, ft = t % NT;
-                const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(ct * 32 + l32, g));
-                const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(ft * 32 + l32, g));
+                const int t = w4 * TPW + u, ct = t / NT, ft = t % NT;
+                const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(hw * D + ct * 32 + l32, g));
+                const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g));
                 acc[u] = mfma32(as_bf16x8(av), as_bf16x8(relu_bf16x8(bk)), acc[u]);
             }
         }
@@ -407,8 +420,8 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_b
         mma_stage(buf);
         ++sg;
         if (cp.t + T >= cp.t1) {
-            const int64_t unit = (int64_t)cp.r * a.heads + cp.h;
-            tiles_io<D>(a.partial + ((int64_t)blockIdx.x + unit) * D * D, acc, true);
+            const int64_t unit = (int64_t)cp.r * (a.heads / HP) + cp.h;   // head group of the piece
+            tiles_io<D, WPH>(a.partial + (((int64_t)blockIdx.x + unit) * HP + hw) * D * D, acc, true, w4);
 #pragma unroll
             for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
         }
@@ -422,7 +435,8 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave, 2) void prefill_slices_b
 }
 
 // Plain fp32-arithmetic version of the slice workgroup (fp32 inputs, and bf16
-// with d = 16): one thread per state element, looping over the piece's rows.
+// with d = 16; one head per unit): one thread per state element, looping over
+// the piece's rows.
 template <typename T>
 __global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
 {
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Prefill, step 3: S[slot] = sum of the unit's partials in ascending slice
+// Prefill, step 3: S[slot] = sum of the head's partials in ascending slice
 // order (deterministic), 0 for an empty prompt.  Each thread owns four
 // consecutive floats of one (request, head) state.
 // ---------------------------------------------------------------------------
@@ -460,14 +474,15 @@ __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
     const int64_t dd = (int64_t)a.d * a.d;
     const int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e4 >= dd / 4) return;
+    const int upr = a.heads / a.hp, hu = h / a.hp, sub = h % a.hp;
     const int64_t S = a.plan[a.n_req + 1];
-    const int64_t nch = (a.plan[r + 1] - a.plan[r]) / a.heads;
+    const int64_t nch = (a.plan[r + 1] - a.plan[r]) / upr;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     if (nch > 0) {
-        const int64_t cfirst = a.plan[r] + h * nch, clast = cfirst + nch - 1;
-        const int64_t unit = (int64_t)r * a.heads + h;
+        const int64_t cfirst = a.plan[r] + hu * nch, clast = cfirst + nch - 1;
+        const int64_t unit = (int64_t)r * upr + hu;
         for (int64_t w = cfirst / S; w <= clast / S; ++w)
-            sum += reinterpret_cast<const f32x4*>(a.partial + (w + unit) * dd)[e4];
+            sum += reinterpret_cast<const f32x4*>(a.partial + ((w + unit) * a.hp + sub) * dd)[e4];
     }
     reinterpret_cast<f32x4*>(a.state + ((int64_t)slot * a.heads + h) * dd)[e4] = sum;
 }
@@ -525,9 +540,14 @@ hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream)
         const dim3 grid(a.slices);
         if (a.dtype_bf16 && a.d >= 32) {
             switch (a.d) {
-            case 32: prefill_slices_bf16_mfma<32><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a); break;
-            case 64: prefill_slices_bf16_mfma<64><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a); break;
-            default: prefill_slices_bf16_mfma<128><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a); break;
+            case 32: prefill_slices_bf16_mfma<32, 1><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a); break;
+            case 64: prefill_slices_bf16_mfma<64, 1><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a); break;
+            default:
+                if (a.hp == 2)
+                    prefill_slices_bf16_mfma<128, 2><<<grid, 2 * PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+                else
+                    prefill_slices_bf16_mfma<128, 1><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+                break;
             }
         } else if (a.dtype_bf16) {
             prefill_slices_generic<uint16_t><<<grid, 256, 0, stream>>>(a);

@@ -394,6 +394,20 @@ def test_prefill_many_ragged_requests():
     assert_parity(state_to_oracle(state), ref, torch.bfloat16, "many prompts")
 
 
+@pytest.mark.parametrize("H", [1, 3, 6])
+def test_prefill_head_groups(H):
+    """d = 128 in bf16 streams adjacent head pairs when the head count is even
+    and single heads otherwise; ragged prompts with small chunks put pieces of
+    both heads of a pair, and of several prompts, in one workgroup."""
+    rng = np.random.default_rng(78 + H)
+    lengths = [int(x) for x in rng.integers(0, 400, size=40)]
+    lengths[3] = 0
+    lengths[4] = 1
+    lengths[9] = 3000
+    state, ref, _, _ = prefill_case(lengths, H, 128, torch.bfloat16, 13200 + H, chunk=64)
+    assert_parity(state_to_oracle(state), ref, torch.bfloat16, f"{H} heads")
+
+
 def test_prefill_malformed_offsets_are_empty():
     """Offsets running backwards or past total_tokens count as empty prompts
     (S = 0) instead of reading out of bounds."""

@@ -63,6 +63,17 @@ __device__ __forceinline__ void split_hi_lo(const float* x, bf16x8& hi, bf16x8& 
     lo = as_bf16x8(l);
 }
 
+// The same split for two floats, each result packed as a bf16 pair (element 0
+// in the low half).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_hi_lo2(f32x2 x, uint32_t& hi, uint32_t& lo) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    const f32x2 hf = {__uint_as_float(h << 16), __uint_as_float(h & 0xffff0000u)};
+    hi = h;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hf, bf16x2));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }

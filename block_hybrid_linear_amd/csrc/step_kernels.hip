@@ -261,6 +261,43 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     }
 }
 
+// One 32 x 32 tile of the commit: acc holds the old state tile (value rows
+// 32 ct + 16 hh + r, features 32 ft + l32 in register r of lane (l32, hh)) and
+// gets phi(K)^T V of the block's first Br keys added by the matrix cores.  A is
+// V^T and B is ReLU(K), both through the transposing LDS read of the staged
+// rows (pitch D + 8); keys past Br are zeroed in the V^T operand.
+template <int D, int NKT>
+__device__ __forceinline__ f32x16 commit_tile(f32x16 acc, const uint16_t* sk, const uint16_t* sv, int Br, int ct,
+                                              int ft, int lane)
+{
+    constexpr int P = D + 8;
+    const int hh = lane / 32, g = lane / 16, jl = lane % 16;
+    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
+    const int kcol = 32 * ft + 16 * (g % 2) + 4 * (jl % 4);
+#pragma unroll
+    for (int jt = 0; jt < NKT; ++jt) {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+            const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+            const s16x4 k0 = lds_read_tr4(sk + row0 * P + kcol);
+            const s16x4 k1 = lds_read_tr4(sk + (row0 + 8) * P + kcol);
+            const int key0 = jt * 32 + 16 * gp + 4 * hh;    // keys key0 + e, key0 + 8 + e
+            u16x8 vop, kop;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vop[e] = key0 + e < Br ? static_cast<uint16_t>(v0[e]) : uint16_t(0);
+                vop[4 + e] = key0 + 8 + e < Br ? static_cast<uint16_t>(v1[e]) : uint16_t(0);
+                kop[e] = static_cast<uint16_t>(k0[e]);
+                kop[4 + e] = static_cast<uint16_t>(k1[e]);
+            }
+            acc = mfma32(as_bf16x8(vop), as_bf16x8(relu_bf16x8(kop)), acc);
+        }
+    }
+    return acc;
+}
+
 // ---------------------------------------------------------------------------
 // Fused step + commit (the last denoising step of a block followed by its
 // commit, worked example: block 2's output uses S_1, then
@@ -401,8 +438,6 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     if constexpr (!kCommit) return;
     // ---- the commit: S^T[c][f] += sum_j V[j][c] ReLU(K[j][f]) over j < Br
     __builtin_amdgcn_sched_barrier(0);
-    const int g = lane / 16, jl = lane % 16;
-    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
 #pragma unroll 1
     for (int ft = qt; ft < NC; ft += NKT) {
         // accumulator register rr of lane (l32, hh): row 32 ct + 16 hh + rr, feature 32 ft + l32
@@ -416,28 +451,225 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
         }
-        const int kcol = 32 * ft + 16 * (g % 2) + 4 * (jl % 4);
+        acc = commit_tile<D, NKT>(acc, sk, sv, Br, ct, ft, lane);
 #pragma unroll
-        for (int jt = 0; jt < NKT; ++jt) {
+        for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Step for blocks of 33..64 rows with D in {64, 128}, optionally followed by
+// the commit: one workgroup per (request, head) with 2 x D/32 waves; wave
+// (qt, ct) produces the outputs of query tile qt, value columns
+// [32 ct, 32 ct + 32).  Work that does not depend on ct is done once per
+// workgroup instead of once per wave:
+//  - S^T is read with whole-row coalesced loads and split into hi + lo bf16
+//    once, into LDS, where each wave reads its A operands;
+//  - each of the four 32 x 32 logit tiles (query tile qt, key tile jt) is
+//    computed by one wave, which also takes the tile's row max and row sum and
+//    writes the tile's probabilities relative to that max (hi + lo bf16, in
+//    its lane order) to LDS; waves without a logit tile do their linear part
+//    meanwhile.
+// After one barrier every wave multiplies V^T by both probability tiles of its
+// query tile into two accumulators and merges them with the two-tile softmax
+// correction: with tile maxima m_j, sums l_j and M = max_j m_j, the weights are
+// 2^(m_j - M) / sum_j l_j 2^(m_j - M).  With D = 128 the logit tiles go to
+// waves (0, 0), (0, 1), (1, 2), (1, 3), one per SIMD (wave w runs on SIMD
+// w % 4); with D = 64 every wave has one.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int D, bool kCommit>
+__global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepArgs a)
+{
+#pragma clang fp contract(off)
+    constexpr int KS = D / 16, NC = D / 32, NT = 2 * NC * kWave;
+    constexpr int R = 64, P = D + 8, CPR = D / 8;
+    constexpr int CPT = R * CPR / NT;            // 16-byte Q, K, V chunks per thread
+    constexpr int SPT = D * D / 4 / NT;          // 16-byte S^T chunks per thread
+    static_assert(NC >= 2 && CPT * NT == R * CPR && SPT * NT * 4 == D * D, "even staging split");
+    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
+    __shared__ __attribute__((aligned(16))) uint16_t shi[D * P], slo[D * P];   // S^T = hi + lo
+    __shared__ __attribute__((aligned(16))) u16x8 sp[2][2][2][2][kWave];       // [qt][jt][gp][hi, lo][lane]
+    __shared__ float smax[2][2][32], ssum[2][2][32];                            // [qt][jt][query]
+
+    const int unit = blockIdx.x;
+    const int r = unit / a.heads, h = unit % a.heads;
+    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    Br = Br > a.blk ? a.blk : Br;
+    const int slot = a.slots[r];
+    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int qt = w / NC, ct = w % NC;
+    const int l32 = lane % 32, hh = lane / 32;
+    const int g = lane / 16, jl = lane % 16;
+    const bool has_l = NC == 2 || ct / 2 == qt;               // wave-uniform
+    const int jt_l = ct % 2;                                  // its key tile
+    const int64_t rs = (int64_t)a.heads * D;
+    const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + base;
+    const uint16_t* k = static_cast<const uint16_t*>(a.k) + base;
+    const uint16_t* v = static_cast<const uint16_t*>(a.v) + base;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + base;
+    const int64_t soff = ((int64_t)slot * a.heads + h) * D * D;
+    const float* st = (kCommit ? a.state_rw : a.state) + soff;
+    const int last = Br - 1;
+    const float sl2 = a.scale * 1.4426950408889634f;
+
+    // ---- loads: Q, K, V rows (rows past B_r repeat row B_r - 1), then S^T
+    u32x4 cq[CPT], ck[CPT], cv[CPT];
 #pragma unroll
-            for (int gp = 0; gp < 2; ++gp) {
-                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-                const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
-                const s16x4 k0 = lds_read_tr4(sk + row0 * P + kcol);
-                const s16x4 k1 = lds_read_tr4(sk + (row0 + 8) * P + kcol);
-                const int key0 = jt * 32 + 16 * gp + 4 * hh;    // keys key0 + e, key0 + 8 + e
-                u16x8 vop, kop;
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        const int64_t off = (int64_t)(row < Br ? row : last) * rs + c8;
+        cq[u] = *reinterpret_cast<const u32x4*>(q + off);
+        ck[u] = *reinterpret_cast<const u32x4*>(k + off);
+        cv[u] = *reinterpret_cast<const u32x4*>(v + off);
+    }
+    f32x4 sc[SPT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vop[e] = key0 + e < Br ? static_cast<uint16_t>(v0[e]) : uint16_t(0);
-                    vop[4 + e] = key0 + 8 + e < Br ? static_cast<uint16_t>(v1[e]) : uint16_t(0);
-                    kop[e] = static_cast<uint16_t>(k0[e]);
-                    kop[4 + e] = static_cast<uint16_t>(k1[e]);
-                }
-                acc = mfma32(as_bf16x8(vop), as_bf16x8(relu_bf16x8(kop)), acc);
-            }
+    for (int u = 0; u < SPT; ++u) sc[u] = reinterpret_cast<const f32x4*>(st)[tid + u * NT];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
+        *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
+        *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int c4 = tid + u * NT, row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
+        uint32_t h0, h1, l0, l1;
+        split_hi_lo2(f32x2{sc[u][0], sc[u][1]}, h0, l0);
+        split_hi_lo2(f32x2{sc[u][2], sc[u][3]}, h1, l1);
+        *reinterpret_cast<u32x2*>(shi + row * P + col) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
+    }
+    __syncthreads();
+
+    const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;   // A row -> value column
+    const uint16_t* qrow = sq + (qt * 32 + l32) * P + 8 * hh;
+    f32x16 o = {};
+    // linear part O^T += S^T phi(Q)^T, S^T as hi + lo bf16 from LDS
+    auto linear = [&]() {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const u16x8 h8 = *reinterpret_cast<const u16x8*>(shi + cA * P + 16 * s + 8 * hh);
+            const u16x8 l8 = *reinterpret_cast<const u16x8*>(slo + cA * P + 16 * s + 8 * hh);
+            const bf16x8 pq = as_bf16x8(relu_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)));
+            o = mfma32(as_bf16x8(h8), pq, o);
+            o = mfma32(as_bf16x8(l8), pq, o);
         }
+    };
+    if (has_l) {
+        // logit tile L^T = K Q^T (keys 32 jt.., queries 32 qt..): lane (l32, hh)
+        // holds query l32 and keys 32 jt + 8 (rr / 4) + 4 hh + rr % 4
+        const int jt = jt_l;
+        f32x16 lt = {};
+        const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            lt = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
+                        as_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)), lt);
+        float m = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+            const float x = j < Br ? lt[rr] * sl2 : -INFINITY;
+            lt[rr] = x;
+            m = fmaxf(m, x);
+        }
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float mb = m == -INFINITY ? 0.f : m;   // key tile 1 has no valid key when B_r <= 32
+        float sum = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(lt[rr] - mb);
+            lt[rr] = p;
+            sum += p;
+        }
+        sum += __shfl_xor(sum, 32);
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            float pp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pp[e] = lt[8 * gp + e];
+            bf16x8 phi, plo;
+            split_hi_lo(pp, phi, plo);
+            sp[qt][jt][gp][0][lane] = __builtin_bit_cast(u16x8, phi);
+            sp[qt][jt][gp][1][lane] = __builtin_bit_cast(u16x8, plo);
+        }
+        if (hh == 0) {
+            smax[qt][jt][l32] = m;
+            ssum[qt][jt][l32] = sum;
+        }
+    } else {
+        linear();
+    }
+    __syncthreads();
+
+    // ---- O^T of each key tile = V^T P_j^T (V^T through the transposing read;
+    // the column of lane i in 16-lane group g is 32 ct + 16 (q % 2) + 8 (g % 2)
+    // + 4 (q / 2) + i % 4, q = i / 4, matching cA)
+    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
+    f32x16 opv[2] = {{}, {}};
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+            const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
+            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+            u16x8 vop;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vop[e] = static_cast<uint16_t>(v0[e]);
+                vop[4 + e] = static_cast<uint16_t>(v1[e]);
+            }
+            opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][0][lane]), opv[jt]);
+            opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][1][lane]), opv[jt]);
+        }
+    }
+    if (has_l) linear();
+    // keep the softmax statistics' LDS reads (and their wait) between the
+    // matrix-core work above and the first use of its results
+    __builtin_amdgcn_sched_barrier(0);
+    const float m0 = smax[qt][0][l32], m1 = smax[qt][1][l32];
+    const float mx = fmaxf(m0, m1);                  // finite: key 0 is valid
+    const float e0 = __builtin_amdgcn_exp2f(m0 - mx), e1 = __builtin_amdgcn_exp2f(m1 - mx);
+    const float inv = __builtin_amdgcn_rcpf(ssum[qt][0][l32] * e0 + ssum[qt][1][l32] * e1);
+    const float c0 = e0 * inv, c1 = e1 * inv;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) o[rr] = o[rr] + (opv[0][rr] * c0 + opv[1][rr] * c1);
+
+    // ---- outputs through LDS (every wave is done with sq after the barrier)
+    __syncthreads();
+    store_tile_lds<D>(sq + qt * 32 * P, o, l32, hh, ct);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        if (row < Br)
+            *reinterpret_cast<u32x4*>(out + (int64_t)row * rs + c8) = *reinterpret_cast<const u32x4*>(sq + row * P + c8);
+    }
+
+    if constexpr (!kCommit) return;
+    // ---- the commit: wave (qt, ct) owns state rows [32 ct, 32 ct + 32) and the
+    // feature tiles ft with ft % 2 == qt; the old values are re-read from
+    // global memory (an L2 hit: this workgroup streamed them above)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+    for (int ft = qt; ft < NC; ft += 2) {
+        float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
+        f32x16 acc;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
+        acc = commit_tile<D, 2>(acc, sk, sv, Br, ct, ft, lane);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
     }
@@ -625,7 +857,10 @@ template <int D>
 static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
 {
     if (a.blk <= 32) step_bf16_mfma<D, 1><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
-    else if (a.blk <= 64) step_bf16_mfma<D, 2><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
+    else if (a.blk <= 64) {
+        if constexpr (D >= 64) step_pair_bf16_mfma<D, false><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
+        else step_bf16_mfma<D, 2><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
+    }
     else step_bf16_mfma_long<D><<<units, 4 * D / 32 * kWave, 0, stream>>>(a);
 }
 
@@ -641,11 +876,11 @@ hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
             else step_commit_bf16_mfma<32, 1, true><<<units, block, 0, stream>>>(a);
             break;
         case 64:
-            if (two) step_commit_bf16_mfma<64, 2, true><<<units, block, 0, stream>>>(a);
+            if (two) step_pair_bf16_mfma<64, true><<<units, block, 0, stream>>>(a);
             else step_commit_bf16_mfma<64, 1, true><<<units, block, 0, stream>>>(a);
             break;
         default:
-            if (two) step_commit_bf16_mfma<128, 2, true><<<units, block, 0, stream>>>(a);
+            if (two) step_pair_bf16_mfma<128, true><<<units, block, 0, stream>>>(a);
             else step_commit_bf16_mfma<128, 1, true><<<units, block, 0, stream>>>(a);
             break;
         }

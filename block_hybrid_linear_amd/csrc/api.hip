@@ -1,6 +1,7 @@
 // C ABI of libhybrid_attn: host-side argument validation and kernel dispatch.
 // Every check runs before anything is enqueued, so a rejected call leaves the
 // outputs and the state store untouched.  The library allocates nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -143,7 +144,8 @@ size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads, int32_
     (void)max_len;
     if (n_req <= 0 || heads <= 0 || d <= 0 || chunk <= 0) return 0;
     return plan_bytes(n_req) +
-           ((size_t)ha::prefill_slices(d, 1) + (size_t)n_req * (size_t)heads) * (size_t)d * (size_t)d * sizeof(float);
+           ((size_t)std::max(ha::prefill_base_slices(d), (int)heads) + (size_t)n_req * (size_t)heads) * (size_t)d *
+               (size_t)d * sizeof(float);
 }
 
 ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_seqlens,
@@ -184,7 +186,8 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
     a.total_tokens = total_tokens;
     a.chunk = chunk;
     a.hp = ha::prefill_group(d, heads, dtype == HA_BF16);
-    a.slices = ha::prefill_slices(d, a.hp);
+    a.spu = ha::prefill_spu(d, a.hp, heads / a.hp);
+    a.slices = heads / a.hp * a.spu;
     a.n_req = n_req;
     a.n_slots = n_slots;
     a.heads = heads;

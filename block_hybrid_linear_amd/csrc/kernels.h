@@ -37,7 +37,8 @@ struct PhiKVArgs {
     float* partial;             // prefill workspace: [slices + n_req * heads][d][d]
     int64_t total_tokens;       // prefill
     int32_t chunk;              // prefill
-    int32_t slices;             // prefill
+    int32_t slices;             // prefill: slice workgroups, spu per unit
+    int32_t spu;                // prefill: slices per unit
     int32_t hp;                 // prefill: heads per unit (1 or 2, divides heads)
     int32_t n_req, n_slots, heads, blk, d;
     bool dtype_bf16;
@@ -47,11 +48,18 @@ struct PhiKVArgs {
 // adjacent heads per workgroup (512 contiguous bytes per token row).
 inline int prefill_group(int d, int heads, bool bf16) { return bf16 && d == 128 && heads % 2 == 0 ? 2 : 1; }
 
-// Number of prefill slice workgroups for head dim d and hp heads per unit
-// (two 4-wave or one 8-wave workgroup per compute unit of an MI355X).  Fixed
-// per (d, hp), so results do not depend on the device.  slices * hp is the
-// same for both hp, and so is the workspace.
-inline int prefill_slices(int d, int hp) { return (d == 32 ? 2048 : 512) / hp; }
+// Prefill slice workgroups per unit for head dim d, hp heads per unit and
+// upr units per request: about (d == 32 ? 2048 : 512) / hp workgroups in all
+// (two 4-wave or one 8-wave workgroup per compute unit of an MI355X), the same
+// number for every unit, at least one.  Fixed per shape, so results do not
+// depend on the device.  The workgroups' partial states, upr * spu * hp, never
+// exceed max(2048 or 512, heads).
+inline int prefill_base_slices(int d) { return d == 32 ? 2048 : 512; }
+inline int prefill_spu(int d, int hp, int upr)
+{
+    const int per = prefill_base_slices(d) / hp / upr;
+    return per > 0 ? per : 1;
+}
 
 // Exact softmax attention of the active block over [prefix; block] (the step
 // without linearisation).  The (request, head, key chunk) list is split into

@@ -202,13 +202,14 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(Ph
 
 // ---------------------------------------------------------------------------
 // Prefill, step 1 (one workgroup): the plan.  A unit is a group of hp
-// adjacent heads of one prompt (hp = 1 or 2, upr = heads / hp units per
-// request).  Prompt r is cut into nch_r = ceil(L_r / chunk) chunks per unit;
-// the (request, unit, chunk) list is laid out request by request, unit by
-// unit.  plan[r] = upr * sum over r' < r of nch_r' (exclusive prefix),
-// plan[n_req] = C (all chunks) and plan[n_req + 1] = chunks per slice
-// ceil(C / slices).  Malformed offsets (outside [0, total_tokens] or
-// decreasing) count as empty prompts.
+// adjacent heads (hp = 1 or 2, upr = heads / hp units per request).  Prompt r
+// is cut into nch_r = ceil(L_r / chunk) chunks.  The work list is laid out
+// unit by unit, and within a unit prompt by prompt: unit u's part is the
+// N = sum_r nch_r chunks of all prompts in order, the same for every unit.
+// plan[r] = sum over r' < r of nch_r' (exclusive prefix), plan[n_req] = N and
+// plan[n_req + 1] = chunks per slice ceil(N / spu) (spu slices per unit).
+// Malformed offsets (outside [0, total_tokens] or decreasing) count as empty
+// prompts.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t chunks_of(const PhiKVArgs& a, int r)
 {
@@ -234,38 +235,48 @@ __global__ __launch_bounds__(256) void prefill_plan(PhiKVArgs a)
     }
     __syncthreads();
     int64_t run = part[tid];
-    const int upr = a.heads / a.hp;
     for (int r = r0; r < r1; ++r) {
-        a.plan[r] = run * upr;
+        a.plan[r] = run;
         run += chunks_of(a, r);
     }
     if (tid == 0) {
-        const int64_t C = part[256] * upr;
-        a.plan[n] = C;
-        const int64_t S = (C + a.slices - 1) / a.slices;
+        const int64_t N = part[256];
+        a.plan[n] = N;
+        const int64_t S = (N + a.spu - 1) / a.spu;
         a.plan[n + 1] = S > 0 ? S : 1;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Prefill, step 2: slice workgroups.  Workgroup w owns the chunk range
-// [w S, (w+1) S) of the flat list -- the same number of chunks for every
-// workgroup, whatever the prompt lengths -- and writes one fp32 partial state
-// per head of each unit u its range touches, into slot w + u (hp states per
-// slot).  (Slot w + u is unique: slices and units are both consecutive
-// intervals of the same list, so a later slice never overlaps an earlier
-// unit.)
+// Prefill, step 2: slice workgroups.  Slice w = u spu + i owns chunks
+// [i S, (i+1) S) of unit u's part of the list -- the same number of chunks for
+// every workgroup, whatever the prompt lengths, and cut at the same token
+// positions for every unit, so the workgroups of the units of one prompt
+// stream the same token rows (the same DRAM pages) at the same time.  It
+// writes one fp32 partial state per head of each (unit, prompt) it touches,
+// into slot w + u n_req + r (hp states per slot).  (The slot is unique:
+// slices and (unit, prompt) pieces are both consecutive intervals of the one
+// list, so a later slice never overlaps an earlier piece.)
 // ---------------------------------------------------------------------------
 struct SliceCursor {
     int r;              // request
-    int64_t c0, c1;     // remaining chunk range of this slice
+    int u;              // unit (head group) of the slice
+    int w;              // slice index in list order, u spu + i
+    int64_t c0, c1;     // remaining chunk range of this slice within the unit's part
 };
 
 __device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur)
 {
-    const int64_t C = uniform_load(a.plan, a.n_req), S = uniform_load(a.plan, a.n_req + 1);
-    cur.c0 = (int64_t)blockIdx.x * S;
-    cur.c1 = cur.c0 + S < C ? cur.c0 + S : C;
+    const int64_t N = uniform_load(a.plan, a.n_req), S = uniform_load(a.plan, a.n_req + 1);
+    // workgroups are numbered unit-fast (consecutive workgroups, which the
+    // dispatcher deals to different XCDs, take different units of the same
+    // token range)
+    const int upr = a.heads / a.hp;
+    cur.u = (int)blockIdx.x % upr;
+    const int i = (int)blockIdx.x / upr;
+    cur.w = cur.u * a.spu + i;
+    cur.c0 = (int64_t)i * S;
+    cur.c1 = cur.c0 + S < N ? cur.c0 + S : N;
     if (cur.c0 >= cur.c1) return false;
     int lo = 0, hi = a.n_req;                 // last r with plan[r] <= c0
     while (hi - lo > 1) {
@@ -277,21 +288,19 @@ __device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur
     return true;
 }
 
-// Next piece of the slice: unit h of prompt r (heads hp h .. hp h + hp - 1),
-// token rows [t0, t1) of prompt r, whose first row starts at element p0 of k
-// and v.
+// Next piece of the slice: unit h = cur.u of prompt r (heads hp h ..
+// hp h + hp - 1), token rows [t0, t1) of prompt r, whose first row starts at
+// element p0 of k and v.
 __device__ __forceinline__ void slice_piece(const PhiKVArgs& a, SliceCursor& cur, int& h, int64_t& t0, int64_t& t1,
                                             int64_t& p0)
 {
     while (uniform_load(a.plan, cur.r + 1) <= cur.c0) ++cur.r;   // skip finished and empty prompts
-    const int64_t pr = uniform_load(a.plan, cur.r);
-    const int64_t nch = (uniform_load(a.plan, cur.r + 1) - pr) / (a.heads / a.hp);
-    const int64_t local = cur.c0 - pr;
-    h = (int)(local / nch);
-    const int64_t k0 = local % nch;
-    const int64_t k1 = (k0 + (cur.c1 - cur.c0) < nch) ? k0 + (cur.c1 - cur.c0) : nch;
+    const int64_t pr = uniform_load(a.plan, cur.r), pe = uniform_load(a.plan, cur.r + 1);
+    const int64_t k0 = cur.c0 - pr;
+    const int64_t k1 = (cur.c1 < pe ? cur.c1 : pe) - pr;
     const int64_t s0 = uniform_load(a.cu, cur.r);
     const int64_t L = uniform_load(a.cu, cur.r + 1) - s0;
+    h = cur.u;
     p0 = s0 * a.heads * a.d + (int64_t)h * a.hp * a.d;
     t0 = k0 * a.chunk;
     t1 = k1 * a.chunk < L ? k1 * a.chunk : L;
@@ -420,8 +429,8 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * HP * kWave, 2 / HP) void prefil
         mma_stage(buf);
         ++sg;
         if (cp.t + T >= cp.t1) {
-            const int64_t unit = (int64_t)cp.r * (a.heads / HP) + cp.h;   // head group of the piece
-            tiles_io<D, WPH>(a.partial + (((int64_t)blockIdx.x + unit) * HP + hw) * D * D, acc, true, w4);
+            const int64_t piece = (int64_t)cp.h * a.n_req + cp.r;        // (unit, prompt) of the piece
+            tiles_io<D, WPH>(a.partial + (((int64_t)cp.sl.w + piece) * HP + hw) * D * D, acc, true, w4);
 #pragma unroll
             for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
         }
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
         slice_piece(a, cur, h, t0, t1, p0);
         const T* kb = static_cast<const T*>(a.k) + p0 + t0 * rs;
         const T* vb = static_cast<const T*>(a.v) + p0 + t0 * rs;
-        float* dst = a.partial + ((int64_t)blockIdx.x + (int64_t)cur.r * a.heads + h) * D * D;
+        float* dst = a.partial + ((int64_t)cur.w + (int64_t)h * a.n_req + cur.r) * D * D;
         for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
             const int c = e / D, f = e % D;
             float acc = 0.f;
@@ -474,15 +483,14 @@ __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
     const int64_t dd = (int64_t)a.d * a.d;
     const int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e4 >= dd / 4) return;
-    const int upr = a.heads / a.hp, hu = h / a.hp, sub = h % a.hp;
+    const int hu = h / a.hp, sub = h % a.hp;
     const int64_t S = a.plan[a.n_req + 1];
-    const int64_t nch = (a.plan[r + 1] - a.plan[r]) / upr;
+    const int64_t cfirst = a.plan[r], cend = a.plan[r + 1];
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    if (nch > 0) {
-        const int64_t cfirst = a.plan[r] + hu * nch, clast = cfirst + nch - 1;
-        const int64_t unit = (int64_t)r * upr + hu;
-        for (int64_t w = cfirst / S; w <= clast / S; ++w)
-            sum += reinterpret_cast<const f32x4*>(a.partial + ((w + unit) * a.hp + sub) * dd)[e4];
+    if (cend > cfirst) {
+        const int64_t piece = (int64_t)hu * a.n_req + r, w0 = (int64_t)hu * a.spu;
+        for (int64_t w = w0 + cfirst / S; w <= w0 + (cend - 1) / S; ++w)
+            sum += reinterpret_cast<const f32x4*>(a.partial + ((w + piece) * a.hp + sub) * dd)[e4];
     }
     reinterpret_cast<f32x4*>(a.state + ((int64_t)slot * a.heads + h) * dd)[e4] = sum;
 }

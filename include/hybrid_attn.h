@@ -154,14 +154,15 @@ ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v,
  * total_tokens: HOST scalar, rows of k and v.
  * max_len: HOST scalar >= 0, an upper bound of the prompt lengths; the
  *   current kernels do not need it (kept for ABI stability).
- * chunk: prompts are cut into chunks of `chunk` tokens; the list of all
- *   (request, head, chunk) triples is split into a fixed number of equal
- *   ranges, one per workgroup, so the work is balanced whatever the prompt
- *   lengths.  Each workgroup writes one fp32 partial state per (request,
- *   head) its range touches into `workspace`; a second kernel sums the
- *   partials of each (request, head) in a fixed order (deterministic: the
- *   same inputs give bit-identical states).  The result does not depend on
- *   chunk beyond fp32 rounding.
+ * chunk: prompts are cut into chunks of `chunk` tokens; for every head (or
+ *   pair of adjacent heads) the chunks of all prompts form one list, which is
+ *   split into the same number of equal ranges, one per workgroup, so the
+ *   work is balanced whatever the prompt lengths and all heads are cut at
+ *   the same token positions.  Each workgroup writes one fp32 partial state
+ *   per (request, head) its range touches into `workspace`; a second kernel
+ *   sums the partials of each (request, head) in a fixed order
+ *   (deterministic: the same inputs give bit-identical states).  The result
+ *   does not depend on chunk beyond fp32 rounding.
  * workspace: device scratch of at least
  *   hybrid_state_prefill_workspace_bytes(...) bytes (non-NULL when
  *   n_req > 0); its contents on entry do not matter.  Calls sharing one
@@ -176,7 +177,10 @@ ha_status hybrid_state_prefill(const void* k, const void* v,
                                void* workspace, size_t workspace_bytes,
                                ha_dtype dtype, void* stream);
 
-/* Workspace size for hybrid_state_prefill with the same arguments (host). */
+/* Workspace size for hybrid_state_prefill with the same arguments (host):
+ * the plan ((n_req + 2) int64, padded to 256 bytes) and
+ * (max(W, heads) + n_req * heads) fp32 d x d partial states, W = 2048 for
+ * d = 32 and 512 otherwise; 0 when n_req, heads, d or chunk is <= 0. */
 size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads,
                                             int32_t d, int64_t total_tokens,
                                             int64_t max_len, int32_t chunk);

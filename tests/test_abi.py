@@ -194,13 +194,16 @@ def test_empty_batches_are_noops(lib):
 
 def test_prefill_workspace_size(lib):
     """Plan (n_req + 2 int64, padded to 256 bytes) + one fp32 d x d partial
-    per (slice, unit) slot: 512 slices (2048 for d = 32) + n_req * heads."""
+    per (slice, unit) slot: max(512 (2048 for d = 32), heads) + n_req *
+    heads."""
     f = bh.hybrid_state_prefill_workspace_bytes
     plan = lambda n: ((n + 2) * 8 + 255) // 256 * 256  # noqa: E731
     assert f(2, 4, 64, 100, 0, 256) == plan(2) + (512 + 8) * 64 * 64 * 4
     assert f(8, 32, 128, 10 ** 6, 65536, 256) == plan(8) + (512 + 256) * 128 * 128 * 4
     assert f(1, 1, 32, 0, 0, 1) == plan(1) + (2048 + 1) * 32 * 32 * 4
     assert f(40, 2, 16, 0, 0, 7) == plan(40) + (512 + 80) * 16 * 16 * 4
+    assert f(2, 600, 64, 10, 0, 256) == plan(2) + (600 + 1200) * 64 * 64 * 4
+    assert f(1, 3000, 32, 10, 0, 256) == plan(1) + (3000 + 3000) * 32 * 32 * 4
     assert f(0, 1, 16, 0, 10, 1) == 0
     assert f(3, 1, 16, 0, 10, 0) == 0
 

@@ -408,6 +408,15 @@ def test_prefill_head_groups(H):
     assert_parity(state_to_oracle(state), ref, torch.bfloat16, f"{H} heads")
 
 
+@pytest.mark.parametrize("H,d", [(600, 128), (520, 64), (2100, 32)])
+def test_prefill_more_head_groups_than_workgroups(H, d):
+    """More head groups than the usual number of slice workgroups: every head
+    group then gets one workgroup (and its own partial slot)."""
+    lengths = [70, 5, 0, 33]
+    state, ref, _, _ = prefill_case(lengths, H, d, torch.bfloat16, 13300 + d, chunk=16)
+    assert_parity(state_to_oracle(state), ref, torch.bfloat16, f"{H} heads, d = {d}")
+
+
 def test_prefill_malformed_offsets_are_empty():
     """Offsets running backwards or past total_tokens count as empty prompts
     (S = 0) instead of reading out of bounds."""

@@ -476,6 +476,13 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 // 2^(m_j - M) / sum_j l_j 2^(m_j - M).  With D = 128 the logit tiles go to
 // waves (0, 0), (0, 1), (1, 2), (1, 3), one per SIMD (wave w runs on SIMD
 // w % 4); with D = 64 every wave has one.
+// With the commit, each wave also owns the state tiles (32 ct.., 32 ft..) with
+// ft % 2 == qt: their old values are loaded in the accumulator layout right
+// after staging, and phi(K)^T V is added and the tiles written back before
+// the outputs are staged, so the state stores drain meanwhile.  The step's
+// coalesced state reads complete before the first barrier, each tile's second
+// read precedes its write in the same wave, and every element is written
+// once, by one wave.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -550,6 +557,21 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
     }
     __syncthreads();
+
+    // with the commit: this wave's old state tiles (value rows 32 ct + 16 hh + r,
+    // features 32 ft + l32 in register r; ft = qt, qt + 2, ..) re-read in the
+    // accumulator layout now (L2 hits: the rows were just streamed), so that
+    // they have arrived when the commit runs after the step
+    constexpr int NFT = kCommit ? NC / 2 : 1;
+    f32x16 old[NFT];
+    if constexpr (kCommit) {
+#pragma unroll
+        for (int f = 0; f < NFT; ++f) {
+            const float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * (qt + 2 * f) + l32;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) old[f][rr] = tile[(int64_t)rr * D];
+        }
+    }
 
     const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;   // A row -> value column
     const uint16_t* qrow = sq + (qt * 32 + l32) * P + 8 * hh;
@@ -647,6 +669,21 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) o[rr] = o[rr] + (opv[0][rr] * c0 + opv[1][rr] * c1);
 
+    // ---- the commit (before the outputs, so that the state stores drain while
+    // the outputs are staged): wave (qt, ct) owns state rows [32 ct, 32 ct + 32)
+    // and the feature tiles ft with ft % 2 == qt, starting from the old tiles
+    // loaded above; it reads only the staged K and V
+    if constexpr (kCommit) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < NFT; ++f) {
+            const int ft = qt + 2 * f;
+            float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
+            const f32x16 acc = commit_tile<D, 2>(old[f], sk, sv, Br, ct, ft, lane);
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
+        }
+    }
     // ---- outputs through LDS (every wave is done with sq after the barrier)
     __syncthreads();
     store_tile_lds<D>(sq + qt * 32 * P, o, l32, hh, ct);
@@ -658,21 +695,6 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             *reinterpret_cast<u32x4*>(out + (int64_t)row * rs + c8) = *reinterpret_cast<const u32x4*>(sq + row * P + c8);
     }
 
-    if constexpr (!kCommit) return;
-    // ---- the commit: wave (qt, ct) owns state rows [32 ct, 32 ct + 32) and the
-    // feature tiles ft with ft % 2 == qt; the old values are re-read from
-    // global memory (an L2 hit: this workgroup streamed them above)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll 1
-    for (int ft = qt; ft < NC; ft += 2) {
-        float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
-        f32x16 acc;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
-        acc = commit_tile<D, 2>(acc, sk, sv, Br, ct, ft, lane);
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
-    }
 }
 
 // ---------------------------------------------------------------------------

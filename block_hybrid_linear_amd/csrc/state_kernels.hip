@@ -3,6 +3,8 @@
 // Language Models", paper-daily summary page, section "technical details in
 // action": S_1 = phi(K_1)^T V_1, S_{1,2} = phi(K_1)^T V_1 + phi(K_2)^T V_2).
 // The state is stored transposed: state[c][f] = S[f][c].
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -50,16 +52,17 @@ template <> struct PhiKVShape<32> { static constexpr int NW = 1, T = 64; };
 // HP adjacent heads per workgroup (prefill with d = 128 takes two: their
 // columns are contiguous in a token row, so every load instruction reads two
 // whole 512-byte row segments, which HBM serves measurably faster than
-// 256-byte ones).  The LDS tiles then hold HP * D rows; wave w works on head
-// w / (NW / HP) of the group.
-template <int D, int HP = 1>
+// 256-byte ones), NW_ waves and T_-token stages.  The LDS tiles then hold
+// HP * D rows; wave w works on head w / (NW / HP) of the group.
+template <int D, int HP = 1, int NW_ = PhiKVShape<D>::NW * HP, int T_ = PhiKVShape<D>::T>
 struct PhiKVTile {
-    static constexpr int NW = PhiKVShape<D>::NW * HP, T = PhiKVShape<D>::T;
+    static constexpr int NW = NW_, T = T_;
     static constexpr int NT = D / 32;                   // tiles per dimension (per head)
     static constexpr int TPW = NT * NT * HP / NW;       // tiles per wave
     static constexpr int PITCH = T + 8;                 // LDS row pitch in bf16 (16 B pad)
     static constexpr int CG = HP * D / 8;               // 8-column groups per token row segment
-    static_assert(2 * (T / 8) * CG == NW * kWave, "one 8x8 block per thread per stage");
+    static constexpr int NLT = 2 * (T / 8) * CG;        // threads that load a stage, one 8x8 block each
+    static_assert(NLT % kWave == 0 && NLT <= NW * kWave, "whole loader waves");
     static constexpr bool kColsFast = D == 128;         // lane mapping, see above
     typedef uint16_t Lds[2][2][HP * D * PITCH];         // [buf][K^T, V^T]
     __device__ __forceinline__ static int row(int c) { return kColsFast ? (c & ~15) | ((c + (c >> 4)) & 15) : c; }
@@ -76,6 +79,7 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
 {
     using P = PhiKVTile<D>;
     constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG;
+    static_assert(P::NLT == P::NW * kWave, "every thread stages one block");
     const int tid = threadIdx.x;
     const int lane = tid % kWave, w = tid / kWave;
     const int l32 = lane % 32, hh = lane / 32;
@@ -332,12 +336,40 @@ __device__ __forceinline__ void stage_advance(const PhiKVArgs& a, StageCursor& s
     if (s.t >= s.t1) stage_next_piece(a, s);
 }
 
+// Prefill tile shapes: one head per workgroup as in the commit (4-wave
+// workgroups, two per compute unit, every wave loading its block of a stage
+// and multiplying its tiles), or a head pair with 32-token stages (80 KB of
+// LDS, one workgroup per compute unit) and the roles split: four loader waves
+// load, transpose and stage K and V, four compute waves own eight 32 x 32
+// tiles each.  Four waves issuing a compute unit's loads stream faster than
+// eight with the same bytes in flight (6.7 vs 6.4 TB/s in a load-only probe),
+// and the loaders issue each stage's loads right after the barrier instead
+// of after their share of the multiplications.
+template <int D, int HP> struct PrefillTile {
+    typedef PhiKVTile<D> type;
+    static constexpr int kLoaders = 0;         // 0: every wave loads and computes
+};
+template <> struct PrefillTile<128, 2> {
+    typedef PhiKVTile<128, 2, 4, 32> type;
+    static constexpr int kLoaders = 4;
+};
 template <int D, int HP>
-__global__ __launch_bounds__(PhiKVShape<D>::NW * HP * kWave, 2 / HP) void prefill_slices_bf16_mfma(PhiKVArgs a)
+constexpr int prefill_threads() { return (PrefillTile<D, HP>::type::NW + PrefillTile<D, HP>::kLoaders) * kWave; }
+
+// In the prefill the thread owning token group tg holds tokens tg + (T/8) e,
+// e = 0..7 (not 8 tg + e): the lanes of one load instruction then read
+// consecutive token rows, which HBM serves faster than rows 8 apart.  LDS
+// group g holds that permutation of the stage's tokens for K and V alike, so
+// the token reduction is unchanged.
+template <int D, int HP>
+__global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_slices_bf16_mfma(PhiKVArgs a)
 {
-    using P = PhiKVTile<D, HP>;
+    using P = typename PrefillTile<D, HP>::type;
+    constexpr int NLD = PrefillTile<D, HP>::kLoaders;
     constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG;
-    constexpr int WPH = P::NW / HP;            // waves per head
+    constexpr int TG = T / 8;                  // token groups per stage
+    constexpr int WPH = P::NW / HP;            // compute waves per head
+    static_assert(NLD == 0 ? P::NLT == P::NW * kWave : P::NLT == NLD * kWave, "one staging block per loader thread");
     __shared__ __attribute__((aligned(16))) typename P::Lds lds;
     StageCursor cp, ld;                        // compute and load cursors
     if (!slice_begin(a, cp.sl)) return;
@@ -348,14 +380,17 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * HP * kWave, 2 / HP) void prefil
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k);
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v);
     const int tid = threadIdx.x;
-    const int lane = tid % kWave, w = tid / kWave;
+    const int lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wc = NLD == 0 ? w : w - NLD;               // compute wave index
     const int l32 = lane % 32, hh = lane / 32;
-    const int hw = w / WPH, w4 = w % WPH;                // this wave's head in the group, its index there
-    const int blocks_per_tensor = (T / 8) * CG;
+    const int hw = wc / WPH, w4 = wc % WPH;              // the compute wave's head in the group, its index there
+    // loader threads (tid < NLT): tensor, token group and column group
+    constexpr int blocks_per_tensor = TG * CG;
     const int tensor = tid / blocks_per_tensor;          // 0 = K, 1 = V
     const int bidx = tid % blocks_per_tensor;
-    const int tg = P::kColsFast ? bidx / CG : bidx % (T / 8);
-    const int cg = P::kColsFast ? bidx % CG : bidx / (T / 8);
+    const int tg = P::kColsFast ? bidx / CG : bidx % TG;
+    const int cg = P::kColsFast ? bidx % CG : bidx / TG;
     const uint16_t* tbase = (tensor == 0 ? kbase : vbase) + cg * 8;
 
     // loads of the stage under the load cursor (rows past the piece re-read its
@@ -364,7 +399,7 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * HP * kWave, 2 / HP) void prefil
         const uint16_t* src = tbase + ld.p0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int64_t t = ld.t + tg * 8 + e;
+            const int64_t t = ld.t + tg + TG * e;
             const int64_t tc = t < ld.t1 ? t : ld.t1 - 1;
             x[e] = *reinterpret_cast<const u32x4*>(src + tc * rs);
         }
@@ -376,7 +411,7 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * HP * kWave, 2 / HP) void prefil
         if (valid < T) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (tg * 8 + e >= valid) x[e] = u32x4{0, 0, 0, 0};
+                if (tg + TG * e >= valid) x[e] = u32x4{0, 0, 0, 0};
         }
         uint16_t* dst = lds[buf][tensor];
 #pragma unroll
@@ -409,38 +444,52 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * HP * kWave, 2 / HP) void prefil
         }
     };
 
-    u32x4 x0[8], x1[8], x2[8];
-    load_stage(x0);
-    load_stage(x1);
-    load_stage(x2);
+    // One stage: the loading waves store the compute cursor's stage and issue
+    // the loads three stages ahead; the computing waves multiply and flush the
+    // unit's partial state when its piece ends.  Staging and loads run on
+    // every path (past the end they repeat the last rows), so every path
+    // around a loading wave's loop issues the three register sets' loads in
+    // the same order and each stage waits only for its own set; only the
+    // arithmetic is skipped past the end.  With split roles, loader and
+    // compute waves run separate copies of the loop with the same barriers
+    // (the cursors are workgroup-uniform), so the compute copy has no loads
+    // for the wait counters to track.
     int sg = 0;
-    // One stage: store the compute cursor's stage, issue the loads three
-    // stages ahead, multiply, and flush the unit's partial state when its
-    // piece ends.  Staging and loads run on every path (past the end they
-    // repeat the last rows), so every path around the loop issues the three
-    // register sets' loads in the same order and each stage waits only for
-    // its own set; only the arithmetic is skipped past the end.
-    auto run_stage = [&](u32x4 (&x)[8]) {
-        const int buf = sg & 1;
-        store_stage(buf, cp.t1 - cp.t, x);
-        __syncthreads();
-        load_stage(x);
-        if (!cp.live) return;                  // uniform
-        mma_stage(buf);
-        ++sg;
-        if (cp.t + T >= cp.t1) {
-            const int64_t piece = (int64_t)cp.h * a.n_req + cp.r;        // (unit, prompt) of the piece
-            tiles_io<D, WPH>(a.partial + (((int64_t)cp.sl.w + piece) * HP + hw) * D * D, acc, true, w4);
-#pragma unroll
-            for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+    auto run_all = [&](auto load_tag, auto mma_tag) {
+        constexpr bool kLoad = decltype(load_tag)::value, kMma = decltype(mma_tag)::value;
+        u32x4 x0[8], x1[8], x2[8];
+        if constexpr (kLoad) {
+            load_stage(x0);
+            load_stage(x1);
+            load_stage(x2);
         }
-        stage_advance(a, cp, T);
+        auto run_stage = [&](u32x4 (&x)[8]) {
+            const int buf = sg & 1;
+            if constexpr (kLoad) store_stage(buf, cp.t1 - cp.t, x);
+            __syncthreads();
+            if constexpr (kLoad) load_stage(x);
+            if (!cp.live) return;              // uniform
+            if constexpr (kMma) {
+                mma_stage(buf);
+                if (cp.t + T >= cp.t1) {
+                    const int64_t piece = (int64_t)cp.h * a.n_req + cp.r;    // (unit, prompt) of the piece
+                    tiles_io<D, WPH>(a.partial + (((int64_t)cp.sl.w + piece) * HP + hw) * D * D, acc, true, w4);
+#pragma unroll
+                    for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+                }
+            }
+            ++sg;
+            stage_advance(a, cp, T);
+        };
+        while (cp.live) {
+            run_stage(x0);
+            run_stage(x1);
+            run_stage(x2);
+        }
     };
-    while (cp.live) {
-        run_stage(x0);
-        run_stage(x1);
-        run_stage(x2);
-    }
+    if constexpr (NLD == 0) run_all(std::true_type{}, std::true_type{});
+    else if (w < NLD) run_all(std::true_type{}, std::false_type{});
+    else run_all(std::false_type{}, std::true_type{});
 }
 
 // Plain fp32-arithmetic version of the slice workgroup (fp32 inputs, and bf16
@@ -548,13 +597,13 @@ hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream)
         const dim3 grid(a.slices);
         if (a.dtype_bf16 && a.d >= 32) {
             switch (a.d) {
-            case 32: prefill_slices_bf16_mfma<32, 1><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a); break;
-            case 64: prefill_slices_bf16_mfma<64, 1><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a); break;
+            case 32: prefill_slices_bf16_mfma<32, 1><<<grid, prefill_threads<32, 1>(), 0, stream>>>(a); break;
+            case 64: prefill_slices_bf16_mfma<64, 1><<<grid, prefill_threads<64, 1>(), 0, stream>>>(a); break;
             default:
                 if (a.hp == 2)
-                    prefill_slices_bf16_mfma<128, 2><<<grid, 2 * PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+                    prefill_slices_bf16_mfma<128, 2><<<grid, prefill_threads<128, 2>(), 0, stream>>>(a);
                 else
-                    prefill_slices_bf16_mfma<128, 1><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+                    prefill_slices_bf16_mfma<128, 1><<<grid, prefill_threads<128, 1>(), 0, stream>>>(a);
                 break;
             }
         } else if (a.dtype_bf16) {

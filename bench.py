@@ -334,6 +334,114 @@ def exact_context(dev="cuda", rotate: int = 4) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# Layer-stack timing: one denoising step of a 20-layer stand-in stack (random
+# bf16 weights; RMSNorm, Q/K/V projections, attention, output projection,
+# SwiGLU MLP per layer) with every layer's attention exact over its KV cache
+# against the same stack with 6 of the 20 layers hybrid (the pages' LLaDA 2.1
+# model converts 6 of its 20 attention layers).  Timing only: the pages give
+# no architecture beyond the layer counts, so the widths are assumptions, and
+# the exact layers share one KV cache buffer (its 9-43 GB cannot stay in any
+# cache, so sharing it changes no traffic).
+
+STACK = {"layers": 20, "hybrid_layers": 6, "n_req": 64, "heads": 32, "head_dim": 128, "block": 32,
+         "mlp_inter": 11008, "prefix_ranges": [[1024, 16384], [16384, 65536]]}
+
+
+def _fill_normal_(x: torch.Tensor, seed: int, chunk: int = 1 << 28) -> torch.Tensor:
+    """Fills a large bf16 tensor with N(0, 1) values piece by piece (no fp32
+    copy of the whole tensor)."""
+    flat = x.view(-1)
+    g = torch.Generator(device=x.device)
+    g.manual_seed(seed)
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        flat[i:i + n].copy_(torch.randn(n, generator=g, device=x.device))
+    return x
+
+
+def layer_stack(dev="cuda", steps: int = 3) -> dict:
+    L, LH = STACK["layers"], STACK["hybrid_layers"]
+    n, H, d, B, F = STACK["n_req"], STACK["heads"], STACK["head_dim"], STACK["block"], STACK["mlp_inter"]
+    hid = H * d
+    hybrid_at = {(2 * i + 1) * L // (2 * LH) for i in range(LH)}   # spread over the stack: 1, 5, 8, 11, 15, 18
+    assert len(hybrid_at) == LH
+    base = 7_000_000
+    wsc = lambda fan_in: fan_in ** -0.5                 # noqa: E731
+    weights = []
+    for l in range(L):
+        w = [synth.normal((hid, hid), base + 100 * l + t, std=wsc(hid), device=dev) for t in range(4)]  # q k v o
+        w.append(synth.normal((hid, 2 * F), base + 100 * l + 4, std=wsc(hid), device=dev))            # gate|up
+        w.append(synth.normal((F, hid), base + 100 * l + 5, std=wsc(F), device=dev))                  # down
+        weights.append(w)
+    x0 = synth.normal((n * B, hid), base + 99_000, device=dev)
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    out = {"config": dict(STACK), "hybrid_layer_indices": sorted(hybrid_at), "results": []}
+    for lo, hi in STACK["prefix_ranges"]:
+        P = synth.uniform_int(n, lo, hi, base + 98_000 + lo)
+        cu = synth.cu_from_lengths(P)
+        total = int(cu[-1])
+        cud = cu.to(dev)
+        kc = _fill_normal_(torch.empty((total, H, d), dtype=torch.bfloat16, device=dev), base + 1)
+        vc = _fill_normal_(torch.empty((total, H, d), dtype=torch.bfloat16, device=dev), base + 2)
+        states = {l: synth.normal((n, H, d, d), base + 200 + l, dtype=torch.float32, device=dev)
+                  .mul_(torch.sqrt(P.double() / 2).float().to(dev).view(-1, 1, 1, 1)) for l in hybrid_at}
+        ws = torch.empty(bh.hybrid_exact_step_workspace_bytes(n, H, B, d), dtype=torch.uint8, device=dev)
+        attn_out = torch.empty((n, B, H, d), dtype=torch.bfloat16, device=dev)
+
+        def forward(hybrid: bool, attn_ms=None):
+            x = x0.clone()
+            for l, (wq, wk, wv, wo, wgu, wd) in enumerate(weights):
+                h = torch.nn.functional.rms_norm(x, (hid,))
+                q, k, v = ((h @ w).view(n, B, H, d) for w in (wq, wk, wv))
+                e0 = e1 = None
+                if attn_ms is not None:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                if hybrid and l in hybrid_at:
+                    bh.hybrid_attn_step(q, k, v, states[l], slots, out=attn_out)
+                else:
+                    bh.hybrid_exact_step(q, k, v, kc, vc, cud, out=attn_out, chunk=256, workspace=ws)
+                if attn_ms is not None:
+                    e1.record()
+                    attn_ms.append((l, e0, e1))
+                x = x + attn_out.view(n * B, hid) @ wo
+                h = torch.nn.functional.rms_norm(x, (hid,))
+                g, u = (h @ wgu).split(F, dim=1)
+                x = x + (torch.nn.functional.silu(g) * u) @ wd
+            return x
+
+        res = {"prefix_range": [lo, hi], "prefix_tokens": total, "kv_cache_GB": round(2 * kc.numel() * 2 / 1e9, 2)}
+        for mode in ("exact", "hybrid"):
+            hyb = mode == "hybrid"
+            for _ in range(2):
+                forward(hyb)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                forward(hyb)
+            b.record()
+            torch.cuda.synchronize()
+            step_ms = a.elapsed_time(b) / steps
+            evs = []
+            forward(hyb, evs)
+            torch.cuda.synchronize()
+            att = [(l, e0.elapsed_time(e1)) for l, e0, e1 in evs]
+            res[f"{mode}_step_ms"] = round(step_ms, 3)
+            res[f"{mode}_attention_ms"] = round(sum(t for _, t in att), 3)
+            if hyb:
+                res["hybrid_layer_attention_ms"] = round(sum(t for l, t in att if l in hybrid_at) / LH, 4)
+            res["exact_layer_attention_ms"] = round(sum(t for l, t in att if not (hyb and l in hybrid_at)) /
+                                                    (L - (LH if hyb else 0)), 4)
+            log(f"[stack] prefixes {lo}-{hi}: {mode} stack {step_ms:.2f} ms per step")
+        res["speedup"] = round(res["exact_step_ms"] / res["hybrid_step_ms"], 3)
+        out["results"].append(res)
+        del kc, vc, states, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 
 WORKLOADS = {w.name: w for w in (PREFILL_DECODE, BLOCK_LOOP, SERVING_STEP)}
 
@@ -350,6 +458,9 @@ def main():
     ap.add_argument("--no-context", action="store_true",
                     help="skip the hybrid-vs-exact step timing at the serving shapes")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle time")
+    ap.add_argument("--stack", action="store_true",
+                    help="only time the 20-layer stand-in stack, every layer exact vs 6 hybrid layers, and print "
+                         "that result as the JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times): the known-size kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters")
@@ -371,6 +482,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
     bh.load_library()
+    if args.stack:
+        res = layer_stack(steps=args.steps)
+        print(json.dumps({"metric": "decode-step time of a 20-layer stack, exact vs 6 hybrid layers", **res}))
+        return
     wl = WORKLOADS[args.workload]
     log(f"[bench] building inputs for {wl.name}")
     job = Job(wl)

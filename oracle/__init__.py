@@ -59,10 +59,15 @@ def _load():
             lib.oracle_step.argtypes = [_D, _D, _D, _D, _I32, _I32, _D] + [ctypes.c_int] * 5 + [ctypes.c_double]
             lib.oracle_commit.argtypes = [_D, _D, _D, _I32, _I32] + [ctypes.c_int] * 5
             lib.oracle_prefill.argtypes = [_D, _D, _I64, _D, _I32] + [ctypes.c_int] * 4
-            for fn in (lib.oracle_step_recompute, lib.oracle_exact_step):
+            for fn in (lib.oracle_step_recompute, lib.oracle_exact_step, lib.oracle_step_norm_recompute):
                 fn.argtypes = [_D, _D, _D, _D, _D, _I64, _I32, _D] + [ctypes.c_int] * 4 + [ctypes.c_double]
+            lib.oracle_step_norm.argtypes = [_D, _D, _D, _D, _D, _I32, _I32, _D] + [ctypes.c_int] * 5 + \
+                [ctypes.c_double]
+            lib.oracle_znorm_commit.argtypes = [_D, _D, _I32, _I32] + [ctypes.c_int] * 5
+            lib.oracle_znorm_prefill.argtypes = [_D, _I64, _D, _I32] + [ctypes.c_int] * 4
             for fn in (lib.oracle_step, lib.oracle_commit, lib.oracle_prefill,
-                       lib.oracle_step_recompute, lib.oracle_exact_step):
+                       lib.oracle_step_recompute, lib.oracle_exact_step, lib.oracle_step_norm,
+                       lib.oracle_znorm_commit, lib.oracle_znorm_prefill, lib.oracle_step_norm_recompute):
                 fn.restype = None
             _lib = lib
     return _lib
@@ -172,3 +177,62 @@ def step_recompute(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None) -> np
 def exact_step(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None) -> np.ndarray:
     """Exact softmax over [prefix; active block]: the step the method replaces."""
     return _prefix_form(_load().oracle_exact_step, q, k, v, kp, vp, cu_seqlens, blk_lens, scale)
+
+
+# ---------------------------------------------------------------------------
+# Normalised variant: the block's softmax scores and the prefix's linear scores
+# share one denominator, which needs z = sum phi(k_p) ([n_slots, H, d]) next to
+# S (a reading of the pages' LoLCATs-based retrofit; see hybrid_oracle.c).
+
+
+def step_norm(q, k, v, S, z, slots=None, blk_lens=None, scale=None) -> np.ndarray:
+    """O_i = (sum_j exp(l_ij) v_j + phi(q_i) S) / (sum_j exp(l_ij) + phi(q_i) . z)
+    per (request, head); rows at or past ``blk_lens[r]`` are zeros."""
+    q, k, v, S, z = _f64(q), _f64(k), _f64(v), _f64(S), _f64(z)
+    n_req, blk, H, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    n_slots = S.shape[0]
+    assert S.shape == (n_slots, H, d, d) and z.shape == (n_slots, H, d)
+    slots = _i32(slots if slots is not None else np.arange(n_req), n_req)
+    bl = _i32(blk_lens, n_req)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros_like(q)
+    _load().oracle_step_norm(_p(q, _D), _p(k, _D), _p(v, _D), _p(S, _D), _p(z, _D), _p(slots, _I32),
+                             _p(bl, _I32), _p(out, _D), n_req, n_slots, H, blk, d, float(scale))
+    return out
+
+
+def znorm_commit(k, z, slots=None, blk_lens=None) -> np.ndarray:
+    """Returns z + sum_j phi(k_j) over each request's valid block rows."""
+    k = _f64(k)
+    z = np.array(_f64(z), copy=True)
+    n_req, blk, H, d = k.shape
+    n_slots = z.shape[0]
+    assert z.shape == (n_slots, H, d)
+    slots = _i32(slots if slots is not None else np.arange(n_req), n_req)
+    bl = _i32(blk_lens, n_req)
+    _load().oracle_znorm_commit(_p(k, _D), _p(z, _D), _p(slots, _I32), _p(bl, _I32), n_req, n_slots, H, blk, d)
+    return z
+
+
+def znorm_prefill(k, cu_seqlens, z=None, slots=None, n_slots=None) -> np.ndarray:
+    """Returns z with each request's slot overwritten by sum_t phi(k_t) over its
+    prompt (packed [total, H, d])."""
+    k = _f64(k)
+    total, H, d = k.shape
+    cu = np.ascontiguousarray(_np(cu_seqlens), dtype=np.int64)
+    n_req = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == total and np.all(np.diff(cu) >= 0)
+    if z is None:
+        z = np.zeros((n_slots if n_slots is not None else n_req, H, d))
+    z = np.array(_f64(z), copy=True)
+    slots = _i32(slots if slots is not None else np.arange(n_req), n_req)
+    _load().oracle_znorm_prefill(_p(k, _D), _p(cu, _I64), _p(z, _D), _p(slots, _I32), n_req, z.shape[0], H, d)
+    return z
+
+
+def step_norm_recompute(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None) -> np.ndarray:
+    """The normalised output with one weight per key: exp(l_ij) for block keys
+    and phi(q_i) . phi(k_t) for the retained prefix tokens (packed [total, H, d])."""
+    return _prefix_form(_load().oracle_step_norm_recompute, q, k, v, kp, vp, cu_seqlens, blk_lens, scale)

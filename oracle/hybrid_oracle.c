@@ -35,6 +35,14 @@
  *     neither read as keys nor written as outputs;
  *   - the two terms are added with no normaliser or mixing weight.
  *
+ * A second, normalised variant ([N] below): the pages say the retrofit
+ * largely follows LoLCATs (summary page, sections "problem solving" and
+ * "method"; abstract page) but print no formula for it.  The reading taken
+ * is that method's hybrid of exact and linear attention with ONE shared
+ * denominator: the block's softmax scores exp(l_ij) and the prefix tokens'
+ * linear scores phi(q_i).phi(k_p) are normalised together, which needs a
+ * second state z = sum over prefix tokens of phi(k_p) next to S.
+ *
  * Layouts (logical, row-major, all fp64):
  *   q, k, v, out  [n_req][blk][H][d]      token-major active block
  *   S             [n_slots][H][d][d]      S[slot][h][f][c]: f = feature of
@@ -288,6 +296,152 @@ void oracle_exact_step(const double* q, const double* k, const double* v,
                 }
             }
             free(logit);
+        }
+    }
+}
+
+/*
+ * [N] Normalised step, state form:
+ *   O_i = (sum_j exp(l_ij) v_j + phi(q_i) S) / (sum_j exp(l_ij) + phi(q_i) . z)
+ * over the Br valid block keys j, l_ij = scale * <q_i, k_j>; S as in
+ * oracle_step, z[f] = sum over prefix tokens of phi(k_p[f]).  The block
+ * maximum m_i is factored out of numerator and denominator (exp(l_ij - m_i)
+ * and exp(-m_i) in place of exp(l_ij) and 1), which changes nothing
+ * mathematically.  z is [n_slots][H][d].
+ */
+void oracle_step_norm(const double* q, const double* k, const double* v, const double* S, const double* z,
+                      const int32_t* slots, const int32_t* blk_lens, double* out,
+                      int n_req, int n_slots, int H, int blk, int d, double scale)
+{
+    (void)n_slots;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int r = 0; r < n_req; ++r) {
+        for (int h = 0; h < H; ++h) {
+            const int Br = blk_lens ? blk_lens[r] : blk;
+            const double* Su = S + ((size_t)slots[r] * H + h) * d * d;
+            const double* zu = z + ((size_t)slots[r] * H + h) * d;
+            double* w = (double*)malloc(sizeof(double) * (Br > 0 ? Br : 1));
+            for (int i = 0; i < Br; ++i) {
+                const double* qi = q + tok(r, i, h, blk, H, d);
+                double* oi = out + tok(r, i, h, blk, H, d);
+                /* block scores */
+                double m = -INFINITY;
+                for (int j = 0; j < Br; ++j) {
+                    const double* kj = k + tok(r, j, h, blk, H, d);
+                    double dot = 0.0;
+                    for (int c = 0; c < d; ++c) dot += qi[c] * kj[c];
+                    w[j] = scale * dot;
+                    if (w[j] > m) m = w[j];
+                }
+                double den = 0.0;
+                for (int c = 0; c < d; ++c) oi[c] = 0.0;
+                for (int j = 0; j < Br; ++j) {
+                    const double e = exp(w[j] - m);
+                    const double* vj = v + tok(r, j, h, blk, H, d);
+                    for (int c = 0; c < d; ++c) oi[c] += e * vj[c];
+                    den += e;
+                }
+                /* prefix: phi(q_i) S over the numerator, phi(q_i) . z over the denominator */
+                const double em = exp(-m);
+                double qz = 0.0;
+                for (int f = 0; f < d; ++f) qz += phi(qi[f]) * zu[f];
+                den += em * qz;
+                for (int c = 0; c < d; ++c) {
+                    double lin = 0.0;
+                    for (int f = 0; f < d; ++f) lin += phi(qi[f]) * Su[(size_t)f * d + c];
+                    oi[c] = (oi[c] + em * lin) / den;
+                }
+            }
+            free(w);
+        }
+    }
+}
+
+/* [N] Commit of the normaliser state: z[f] += sum_{j < Br} phi(K[j][f]). */
+void oracle_znorm_commit(const double* k, double* z, const int32_t* slots, const int32_t* blk_lens,
+                         int n_req, int n_slots, int H, int blk, int d)
+{
+    (void)n_slots;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int r = 0; r < n_req; ++r) {
+        for (int h = 0; h < H; ++h) {
+            const int Br = blk_lens ? blk_lens[r] : blk;
+            double* zu = z + ((size_t)slots[r] * H + h) * d;
+            for (int f = 0; f < d; ++f) {
+                double sum = 0.0;
+                for (int j = 0; j < Br; ++j) sum += phi(k[tok(r, j, h, blk, H, d) + f]);
+                zu[f] += sum;
+            }
+        }
+    }
+}
+
+/* [N] Prefill of the normaliser state: z[f] = sum_{t < L_r} phi(K[t][f]). */
+void oracle_znorm_prefill(const double* k, const int64_t* cu, double* z, const int32_t* slots,
+                          int n_req, int n_slots, int H, int d)
+{
+    (void)n_slots;
+    const size_t stride = (size_t)H * d;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int r = 0; r < n_req; ++r) {
+        for (int h = 0; h < H; ++h) {
+            double* zu = z + ((size_t)slots[r] * H + h) * d;
+            for (int f = 0; f < d; ++f) zu[f] = 0.0;
+            for (int64_t t = cu[r]; t < cu[r + 1]; ++t) {
+                const double* kt = k + t * stride + (size_t)h * d;
+                for (int f = 0; f < d; ++f) zu[f] += phi(kt[f]);
+            }
+        }
+    }
+}
+
+/*
+ * [N] The normalised output from the retained prefix tokens: one weight per
+ * key, exp(l_ij) for the block keys and phi(q_i) . phi(k_t) for each prefix
+ * token, and O_i = sum of weight x value / sum of weights (the block maximum
+ * factored out as in oracle_step_norm).  By associativity this equals
+ * oracle_step_norm with S = sum phi(k_t)^T v_t and z = sum phi(k_t).
+ */
+void oracle_step_norm_recompute(const double* q, const double* k, const double* v,
+                                const double* kp, const double* vp, const int64_t* cu,
+                                const int32_t* blk_lens, double* out,
+                                int n_req, int H, int blk, int d, double scale)
+{
+    const size_t stride = (size_t)H * d;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int r = 0; r < n_req; ++r) {
+        for (int h = 0; h < H; ++h) {
+            const int Br = blk_lens ? blk_lens[r] : blk;
+            const int64_t P = cu[r + 1] - cu[r];
+            double* w = (double*)malloc(sizeof(double) * (Br + P > 0 ? Br + P : 1));
+            for (int i = 0; i < Br; ++i) {
+                const double* qi = q + tok(r, i, h, blk, H, d);
+                double m = -INFINITY;
+                for (int j = 0; j < Br; ++j) {
+                    const double* kj = k + tok(r, j, h, blk, H, d);
+                    double dot = 0.0;
+                    for (int c = 0; c < d; ++c) dot += qi[c] * kj[c];
+                    w[j] = scale * dot;
+                    if (w[j] > m) m = w[j];
+                }
+                for (int j = 0; j < Br; ++j) w[j] = exp(w[j] - m);
+                for (int64_t t = 0; t < P; ++t) {
+                    const double* kt = kp + (cu[r] + t) * stride + h * d;
+                    double dot = 0.0;
+                    for (int f = 0; f < d; ++f) dot += phi(qi[f]) * phi(kt[f]);
+                    w[Br + t] = exp(-m) * dot;
+                }
+                double den = 0.0;
+                for (int64_t j = 0; j < Br + P; ++j) den += w[j];
+                double* oi = out + tok(r, i, h, blk, H, d);
+                for (int c = 0; c < d; ++c) {
+                    double num = 0.0;
+                    for (int j = 0; j < Br; ++j) num += w[j] * v[tok(r, j, h, blk, H, d) + c];
+                    for (int64_t t = 0; t < P; ++t) num += w[Br + t] * vp[(cu[r] + t) * stride + h * d + c];
+                    oi[c] = num / den;
+                }
+            }
+            free(w);
         }
     }
 }

@@ -347,3 +347,122 @@ def test_worked_example_schedule():
         for h in range(W.heads):
             ref = sum(relu(kk[:, h]).T @ vv[:, h] for kk, vv in zip(kept_k, kept_v))
             np.testing.assert_allclose(S[0, h], ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Normalised variant: block softmax scores and prefix linear scores share one
+# denominator (z = sum phi(k_p) next to S)
+# --------------------------------------------------------------------------
+
+def _prefix_state(kp, vp, P):
+    cu = np.array([0, P])
+    return oracle.prefill(kp, vp, cu), oracle.znorm_prefill(kp, cu), cu
+
+
+@pytest.mark.parametrize("blk,d", [(1, 3), (4, 16), (7, 5), (32, 64)])
+def test_norm_empty_prefix_is_sdpa(blk, d):
+    """S = 0 and z = 0 (no previous block): plain softmax attention over the
+    block (torch, fp64)."""
+    n, H = 2, 3
+    q, k, v = rnd(n, blk, H, d), rnd(n, blk, H, d), rnd(n, blk, H, d)
+    o = oracle.step_norm(q, k, v, np.zeros((n, H, d, d)), np.zeros((n, H, d)), scale=0.37)
+    np.testing.assert_allclose(o, sdpa64(q, k, v, 0.37), rtol=1e-12, atol=1e-12)
+
+
+def test_norm_nonpositive_queries_is_sdpa():
+    """phi(q) = 0 when every query entry is <= 0: the prefix drops out of the
+    numerator AND the denominator, whatever S and z hold."""
+    n, blk, H, d = 2, 6, 2, 8
+    q = -np.abs(rnd(n, blk, H, d))
+    k, v = rnd(n, blk, H, d), rnd(n, blk, H, d)
+    S, z = rnd(n, H, d, d), np.abs(rnd(n, H, d)) * 50
+    o = oracle.step_norm(q, k, v, S, z, scale=0.5)
+    np.testing.assert_allclose(o, sdpa64(q, k, v, 0.5), rtol=1e-12, atol=1e-12)
+
+
+def test_norm_state_form_equals_recompute_bruteforce():
+    """The state form (S, z) equals one weight per key -- exp(l) for block
+    keys, phi(q).phi(k_t) for each retained prefix token -- over every tiny
+    size."""
+    H = 1
+    worst = 0.0
+    for blk, d, P in itertools.product(range(1, 5), (1, 2, 3, 5, 8), (0, 1, 2, 5, 12)):
+        q, k, v = rnd(1, blk, H, d), rnd(1, blk, H, d), rnd(1, blk, H, d)
+        kp, vp = rnd(P, H, d), rnd(P, H, d)
+        S, z, cu = _prefix_state(kp, vp, P)
+        a = oracle.step_norm(q, k, v, S, z)
+        b = oracle.step_norm_recompute(q, k, v, kp, vp, cu)
+        worst = max(worst, np.abs(a - b).max() / max(1.0, np.abs(b).max()))
+    assert worst <= 1e-12, worst
+
+
+def test_norm_constant_values_give_that_value():
+    """When every block value and every prefix value is the same vector u the
+    output is u for every query: the weights sum to one.  A term missing from
+    the numerator or the denominator (or exp(-m) on one side only) breaks it."""
+    blk, H, d, P = 6, 2, 7, 40
+    u = rnd(d)
+    q, k = 2 * rnd(1, blk, H, d), 2 * rnd(1, blk, H, d)
+    v = np.broadcast_to(u, (1, blk, H, d)).copy()
+    kp = rnd(P, H, d)
+    vp = np.broadcast_to(u, (P, H, d)).copy()
+    S, z, _ = _prefix_state(kp, vp, P)
+    o = oracle.step_norm(q, k, v, S, z, scale=0.8)
+    np.testing.assert_allclose(o, np.broadcast_to(u, o.shape), rtol=1e-12, atol=1e-12)
+
+
+def test_norm_output_in_convex_hull_of_values():
+    """All weights are >= 0, so each output entry lies between the smallest
+    and largest value entry over block and prefix."""
+    blk, H, d, P = 9, 2, 6, 30
+    q, k, v = rnd(1, blk, H, d), rnd(1, blk, H, d), rnd(1, blk, H, d)
+    kp, vp = rnd(P, H, d), rnd(P, H, d)
+    S, z, _ = _prefix_state(kp, vp, P)
+    o = oracle.step_norm(q, k, v, S, z)
+    for h in range(H):
+        vals = np.concatenate([v[0, :, h], vp[:, h]], 0)
+        lo, hi = vals.min(0), vals.max(0)
+        assert np.all(o[0, :, h] >= lo - 1e-12) and np.all(o[0, :, h] <= hi + 1e-12)
+
+
+def test_norm_large_logits_are_finite():
+    """Logits of several hundred: the block maximum is factored out of both
+    sides, so nothing overflows, and against such scores the prefix's linear
+    scores are negligible (softmax of the block, torch fp64)."""
+    n, blk, H, d, P = 1, 8, 1, 4, 20
+    q, k, v = 30 * rnd(n, blk, H, d), 30 * rnd(n, blk, H, d), rnd(n, blk, H, d)
+    q[..., 0] = np.abs(q[..., 0]) + 30          # a positive feature, so phi(q).z > 0
+    k[..., 0] = np.abs(k[..., 0]) + 30
+    kp, vp = rnd(P, H, d), rnd(P, H, d)
+    S, z, _ = _prefix_state(kp, vp, P)
+    o = oracle.step_norm(q, k, v, S, z, scale=1.0)
+    assert np.all(np.isfinite(o))
+    np.testing.assert_allclose(o, sdpa64(q, k, v, 1.0), rtol=1e-9, atol=1e-9)
+
+
+def test_znorm_is_sum_of_relu_keys_in_any_order():
+    """z after prefill = numpy's column sum of relu(K) per request; commits of
+    blocks in any order add up to the prefill of their concatenation."""
+    H, d, blk = 2, 5, 4
+    lens = [0, 3, 17]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    k = rnd(int(cu[-1]), H, d)
+    z = oracle.znorm_prefill(k, cu)
+    for r in range(3):
+        np.testing.assert_allclose(z[r], relu(k[cu[r]:cu[r + 1]]).sum(0), rtol=1e-13, atol=1e-13)
+    blocks = [rnd(1, blk, H, d) for _ in range(3)]
+    z0 = rnd(1, H, d)
+    res = []
+    for perm in itertools.permutations(range(3)):
+        zz = z0
+        for i in perm:
+            zz = oracle.znorm_commit(blocks[i], zz)
+        res.append(zz)
+    for zz in res[1:]:
+        np.testing.assert_allclose(zz, res[0], rtol=1e-13, atol=1e-13)
+    cat = np.concatenate([b[0] for b in blocks], 0)
+    np.testing.assert_allclose(res[0] - z0, oracle.znorm_prefill(cat, np.array([0, 3 * blk])), rtol=1e-12,
+                               atol=1e-12)
+    lens = np.array([2], dtype=np.int32)                 # ragged block: rows past B_r are not read
+    zr = oracle.znorm_commit(blocks[0], np.zeros((1, H, d)), blk_lens=lens)
+    np.testing.assert_allclose(zr[0], relu(blocks[0][0, :2]).sum(0), rtol=1e-13, atol=1e-13)

@@ -12,6 +12,12 @@ with the same names:
     hybrid_state_prefill  S = sum over a prompt of ReLU(k)^T v
     hybrid_attn_step_commit  a block's last step fused with its commit
 
+the normalised variant (block softmax scores and prefix linear scores over one
+denominator, with z = sum ReLU(k) next to S):
+
+    hybrid_attn_step_norm, hybrid_attn_step_commit_norm,
+    hybrid_state_commit_norm, hybrid_state_prefill_norm
+
 and, for comparison, the exact step the method replaces:
 
     hybrid_exact_step     softmax attention of the active block over its
@@ -19,12 +25,16 @@ and, for comparison, the exact step the method replaces:
 
 PyTorch only provides device memory and streams.
 """
-from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_attn_step_commit, hybrid_exact_step,
-                      hybrid_exact_step_workspace_bytes, hybrid_state_commit, hybrid_state_prefill,
-                      hybrid_state_prefill_workspace_bytes, load_library, prepare_commit, prepare_exact_step,
-                      prepare_prefill, prepare_step, prepare_step_commit)
+from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_attn_step_commit,
+                      hybrid_attn_step_commit_norm, hybrid_attn_step_norm, hybrid_exact_step,
+                      hybrid_exact_step_workspace_bytes, hybrid_state_commit, hybrid_state_commit_norm,
+                      hybrid_state_prefill, hybrid_state_prefill_norm, hybrid_state_prefill_workspace_bytes,
+                      load_library, prepare_commit, prepare_exact_step, prepare_prefill, prepare_prefill_norm,
+                      prepare_step, prepare_step_commit, prepare_step_commit_norm, prepare_step_norm)
 
-__all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_attn_step_commit", "hybrid_exact_step",
-           "hybrid_exact_step_workspace_bytes", "hybrid_state_commit", "hybrid_state_prefill",
-           "hybrid_state_prefill_workspace_bytes", "load_library", "prepare_commit", "prepare_exact_step",
-           "prepare_prefill", "prepare_step", "prepare_step_commit"]
+__all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_attn_step_commit",
+           "hybrid_attn_step_commit_norm", "hybrid_attn_step_norm", "hybrid_exact_step",
+           "hybrid_exact_step_workspace_bytes", "hybrid_state_commit", "hybrid_state_commit_norm",
+           "hybrid_state_prefill", "hybrid_state_prefill_norm", "hybrid_state_prefill_workspace_bytes",
+           "load_library", "prepare_commit", "prepare_exact_step", "prepare_prefill", "prepare_prefill_norm",
+           "prepare_step", "prepare_step_commit", "prepare_step_commit_norm", "prepare_step_norm"]

@@ -53,8 +53,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           ctypes.c_int, vp]
         lib.hybrid_exact_step_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.hybrid_exact_step_workspace_bytes.restype = sz
+        lib.hybrid_attn_step_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                              ctypes.c_int, vp]
+        lib.hybrid_attn_step_commit_norm.argtypes = lib.hybrid_attn_step_norm.argtypes
+        lib.hybrid_state_commit_norm.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+        lib.hybrid_state_prefill_norm.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp,
+                                                  sz, ctypes.c_int, vp]
         for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill, lib.hybrid_exact_step,
-                   lib.hybrid_attn_step_commit):
+                   lib.hybrid_attn_step_commit, lib.hybrid_attn_step_norm, lib.hybrid_attn_step_commit_norm,
+                   lib.hybrid_state_commit_norm, lib.hybrid_state_prefill_norm):
             fn.restype = ctypes.c_int
         lib.hybrid_last_error.argtypes = []
         lib.hybrid_last_error.restype = ctypes.c_char_p
@@ -310,5 +317,96 @@ def prepare_exact_step(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens=None,
         st = fn(*args)
         if st != HA_OK:
             _check("hybrid_exact_step", st)
+    run.workspace = ws
+    return run
+
+
+# ---------------------------------------------------------------------------
+# Normalised variant: one denominator for the block's softmax scores and the
+# prefix's linear scores, with z = sum phi(k) [n_slots, H, d] fp32 next to S.
+
+def _check_z(z, state):
+    n_slots, H, d = state.shape[0], state.shape[1], state.shape[2]
+    if z.dim() != 3 or tuple(z.shape) != (n_slots, H, d):
+        raise ValueError(f"z must be [{n_slots}, {H}, {d}]")
+    return _dev(z, "z", torch.float32)
+
+
+def _with_z(args, z, state, at):
+    """Inserts z's pointer into a marshalled argument tuple at position `at`."""
+    return args[:at] + (_check_z(z, state),) + args[at:]
+
+
+def hybrid_attn_step_norm(q, k, v, state, z, slots, out=None, blk_lens=None, scale=None, stream=None):
+    """out_i = (sum_j exp(l_ij) v_j + ReLU(q_i) S) / (sum_j exp(l_ij) + ReLU(q_i).z)
+    for q/k/v [n_req, blk, H, d], state [n_slots, H, d, d], z [n_slots, H, d]."""
+    if out is None:
+        out = torch.zeros_like(q)
+    args = _with_z(_step_args(q, k, v, state, slots, out, blk_lens, scale), z, state, 4)
+    _check("hybrid_attn_step_norm", load_library().hybrid_attn_step_norm(*args, _stream(stream)))
+    return out
+
+
+def prepare_step_norm(q, k, v, state, z, slots, out, blk_lens=None, scale=None, stream=None):
+    """Prepared form of hybrid_attn_step_norm (see prepare_step)."""
+    args = _with_z(_step_args(q, k, v, state, slots, out, blk_lens, scale), z, state, 4) + (_stream(stream),)
+    fn = load_library().hybrid_attn_step_norm
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_attn_step_norm", st)
+    return run
+
+
+def hybrid_attn_step_commit_norm(q, k, v, state, z, slots, out=None, blk_lens=None, scale=None, stream=None):
+    """hybrid_attn_step_norm from the current S and z, then S += ReLU(K)^T V and
+    z += sum_j ReLU(k_j) in the same call.  Requests must use distinct slots."""
+    if out is None:
+        out = torch.zeros_like(q)
+    args = _with_z(_step_args(q, k, v, state, slots, out, blk_lens, scale), z, state, 4)
+    _check("hybrid_attn_step_commit_norm", load_library().hybrid_attn_step_commit_norm(*args, _stream(stream)))
+    return out
+
+
+def prepare_step_commit_norm(q, k, v, state, z, slots, out, blk_lens=None, scale=None, stream=None):
+    """Prepared form of hybrid_attn_step_commit_norm (see prepare_step)."""
+    args = _with_z(_step_args(q, k, v, state, slots, out, blk_lens, scale), z, state, 4) + (_stream(stream),)
+    fn = load_library().hybrid_attn_step_commit_norm
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_attn_step_commit_norm", st)
+    return run
+
+
+def hybrid_state_commit_norm(k, v, state, z, slots, blk_lens=None, stream=None):
+    """state[slots] += ReLU(K)^T V and z[slots] += sum_j ReLU(k_j), in place."""
+    args = _with_z(_commit_args(k, v, state, slots, blk_lens), z, state, 3)
+    _check("hybrid_state_commit_norm", load_library().hybrid_state_commit_norm(*args, _stream(stream)))
+    return state
+
+
+def hybrid_state_prefill_norm(k, v, cu_seqlens, state, z, slots, max_len=None, chunk=256, workspace=None,
+                              stream=None):
+    """state[slots[r]] and z[slots[r]] overwritten by the sums over prompt r of
+    ReLU(k_t)^T v_t and ReLU(k_t) (see hybrid_state_prefill)."""
+    args, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    args = _with_z(args, z, state, 6)
+    _check("hybrid_state_prefill_norm", load_library().hybrid_state_prefill_norm(*args, _stream(stream)))
+    return state
+
+
+def prepare_prefill_norm(k, v, cu_seqlens, state, z, slots, max_len=None, chunk=256, workspace=None, stream=None):
+    """Prepared form of hybrid_state_prefill_norm; keeps its workspace alive."""
+    args, ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    args = _with_z(args, z, state, 6) + (_stream(stream),)
+    fn = load_library().hybrid_state_prefill_norm
+
+    def run():
+        st = fn(*args)
+        if st != HA_OK:
+            _check("hybrid_state_prefill_norm", st)
     run.workspace = ws
     return run

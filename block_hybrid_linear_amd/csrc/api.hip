@@ -75,53 +75,57 @@ const char* hybrid_last_error(void) { return g_last_error.c_str(); }
 
 int32_t hybrid_abi_version(void) { return HYBRID_ATTN_ABI_VERSION; }
 
-ha_status hybrid_attn_step(const void* q, const void* k, const void* v, const float* state,
-                           const int32_t* slots, void* out, const int32_t* blk_lens,
-                           int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
-                           float scale, ha_dtype dtype, void* stream)
+}  // extern "C"
+
+namespace {
+
+// The step, the fused step + commit, the commit and the prefill, with z =
+// NULL for the plain sum and z non-NULL for the normalised variant.
+ha_status step_impl(const char* fn, const void* q, const void* k, const void* v, const float* state, float* z,
+                    const int32_t* slots, void* out, const int32_t* blk_lens, int32_t n_req, int32_t n_slots,
+                    int32_t heads, int32_t blk, int32_t d, float scale, ha_dtype dtype, void* stream, bool norm)
 {
-    static const char* fn = "hybrid_attn_step";
     ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
     if (st != HA_OK) return st;
     if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
     if (n_req == 0) return HA_OK;
-    if (!q || !k || !v || !state || !slots || !out)
-        return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state, slots and out must be non-NULL", fn);
-    if ((st = check_aligned(fn, {q, k, v, state, out}, nullptr)) != HA_OK) return st;
-    ha::StepArgs a{q, k, v, state, nullptr, slots, out, blk_lens, n_req, n_slots, heads, blk, d, scale,
+    if (!q || !k || !v || !state || !slots || !out || (norm && !z))
+        return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state%s, slots and out must be non-NULL", fn,
+                    norm ? ", z" : "");
+    if ((st = check_aligned(fn, {q, k, v, state, out, z}, nullptr)) != HA_OK) return st;
+    ha::StepArgs a{q, k, v, state, nullptr, slots, out, blk_lens, z, n_req, n_slots, heads, blk, d, scale,
                    dtype == HA_BF16};
     return hip_status(ha::launch_step(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v, float* state,
-                                  const int32_t* slots, void* out, const int32_t* blk_lens,
-                                  int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
-                                  float scale, ha_dtype dtype, void* stream)
+ha_status step_commit_impl(const char* fn, const void* q, const void* k, const void* v, float* state, float* z,
+                           const int32_t* slots, void* out, const int32_t* blk_lens, int32_t n_req,
+                           int32_t n_slots, int32_t heads, int32_t blk, int32_t d, float scale, ha_dtype dtype,
+                           void* stream, bool norm)
 {
-    static const char* fn = "hybrid_attn_step_commit";
     ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
     if (st != HA_OK) return st;
     if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
     if (n_req == 0) return HA_OK;
-    if (!q || !k || !v || !state || !slots || !out)
-        return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state, slots and out must be non-NULL", fn);
-    if ((st = check_aligned(fn, {q, k, v, state, out}, nullptr)) != HA_OK) return st;
-    ha::StepArgs a{q, k, v, state, state, slots, out, blk_lens, n_req, n_slots, heads, blk, d, scale,
+    if (!q || !k || !v || !state || !slots || !out || (norm && !z))
+        return fail(HA_ERR_INVALID_ARG, "%s: q, k, v, state%s, slots and out must be non-NULL", fn,
+                    norm ? ", z" : "");
+    if ((st = check_aligned(fn, {q, k, v, state, out, z}, nullptr)) != HA_OK) return st;
+    ha::StepArgs a{q, k, v, state, state, slots, out, blk_lens, z, n_req, n_slots, heads, blk, d, scale,
                    dtype == HA_BF16};
     return hip_status(ha::launch_step_commit(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-ha_status hybrid_state_commit(const void* k, const void* v, float* state, const int32_t* slots,
-                              const int32_t* blk_lens, int32_t n_req, int32_t n_slots,
-                              int32_t heads, int32_t blk, int32_t d, ha_dtype dtype, void* stream)
+ha_status commit_impl(const char* fn, const void* k, const void* v, float* state, float* z, const int32_t* slots,
+                      const int32_t* blk_lens, int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk,
+                      int32_t d, ha_dtype dtype, void* stream, bool norm)
 {
-    static const char* fn = "hybrid_state_commit";
     ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
     if (st != HA_OK) return st;
     if (n_req == 0) return HA_OK;
-    if (!k || !v || !state || !slots)
-        return fail(HA_ERR_INVALID_ARG, "%s: k, v, state and slots must be non-NULL", fn);
-    if ((st = check_aligned(fn, {k, v, state}, nullptr)) != HA_OK) return st;
+    if (!k || !v || !state || !slots || (norm && !z))
+        return fail(HA_ERR_INVALID_ARG, "%s: k, v, state%s and slots must be non-NULL", fn, norm ? ", z" : "");
+    if ((st = check_aligned(fn, {k, v, state, z}, nullptr)) != HA_OK) return st;
     ha::PhiKVArgs a{};
     a.k = k;
     a.v = v;
@@ -134,27 +138,25 @@ ha_status hybrid_state_commit(const void* k, const void* v, float* state, const 
     a.blk = blk;
     a.d = d;
     a.dtype_bf16 = dtype == HA_BF16;
-    return hip_status(ha::launch_commit(a, static_cast<hipStream_t>(stream)), fn);
+    hipError_t e = ha::launch_commit(a, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && norm) {
+        ha::StepArgs zc{nullptr, k, v, nullptr, nullptr, slots, nullptr, blk_lens, z, n_req, n_slots, heads, blk,
+                        d, 0.f, dtype == HA_BF16};
+        e = ha::launch_znorm_commit(zc, static_cast<hipStream_t>(stream));
+    }
+    return hip_status(e, fn);
 }
 
-size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads, int32_t d,
-                                            int64_t total_tokens, int64_t max_len, int32_t chunk)
+size_t prefill_slots(int32_t n_req, int32_t heads, int32_t d)
 {
-    (void)total_tokens;
-    (void)max_len;
-    if (n_req <= 0 || heads <= 0 || d <= 0 || chunk <= 0) return 0;
-    return plan_bytes(n_req) +
-           ((size_t)std::max(ha::prefill_base_slices(d), (int)heads) + (size_t)n_req * (size_t)heads) * (size_t)d *
-               (size_t)d * sizeof(float);
+    return (size_t)std::max(ha::prefill_base_slices(d), (int)heads) + (size_t)n_req * (size_t)heads;
 }
 
-ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_seqlens,
-                               int64_t total_tokens, int64_t max_len, float* state,
-                               const int32_t* slots, int32_t n_req, int32_t n_slots,
-                               int32_t heads, int32_t d, int32_t chunk, void* workspace,
-                               size_t workspace_bytes, ha_dtype dtype, void* stream)
+ha_status prefill_impl(const char* fn, const void* k, const void* v, const int64_t* cu_seqlens,
+                       int64_t total_tokens, int64_t max_len, float* state, float* z, const int32_t* slots,
+                       int32_t n_req, int32_t n_slots, int32_t heads, int32_t d, int32_t chunk, void* workspace,
+                       size_t workspace_bytes, ha_dtype dtype, void* stream, bool norm)
 {
-    static const char* fn = "hybrid_state_prefill";
     if (n_req < 0) return fail(HA_ERR_INVALID_ARG, "%s: n_req must be >= 0 (got %d)", fn, n_req);
     if (n_slots <= 0) return fail(HA_ERR_INVALID_ARG, "%s: n_slots must be > 0 (got %d)", fn, n_slots);
     if (heads <= 0) return fail(HA_ERR_INVALID_ARG, "%s: heads must be > 0 (got %d)", fn, heads);
@@ -166,26 +168,29 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
     if (n_req > 65535 || heads > 65535)
         return fail(HA_ERR_INVALID_ARG, "%s: n_req and heads must be <= 65535", fn);
     if (n_req == 0) return HA_OK;
-    if (!cu_seqlens || !state || !slots)
-        return fail(HA_ERR_INVALID_ARG, "%s: cu_seqlens, state and slots must be non-NULL", fn);
+    if (!cu_seqlens || !state || !slots || (norm && !z))
+        return fail(HA_ERR_INVALID_ARG, "%s: cu_seqlens, state%s and slots must be non-NULL", fn,
+                    norm ? ", z" : "");
     if (total_tokens > 0 && (!k || !v))
         return fail(HA_ERR_INVALID_ARG, "%s: k and v must be non-NULL when total_tokens > 0", fn);
     const size_t need = hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk);
     if (workspace_bytes < need || !workspace)
         return fail(HA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
                     workspace_bytes, workspace ? "" : ", NULL");
-    if (ha_status st = check_aligned(fn, {k, v, state}, workspace); st != HA_OK) return st;
+    if (ha_status st = check_aligned(fn, {k, v, state, z}, workspace); st != HA_OK) return st;
     ha::PhiKVArgs a{};
     a.k = k;
     a.v = v;
     a.state = state;
+    a.z = z;
     a.slots = slots;
     a.cu = cu_seqlens;
     a.plan = static_cast<int64_t*>(workspace);
     a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan_bytes(n_req));
+    a.zpartial = a.partial + prefill_slots(n_req, heads, d) * (size_t)d * (size_t)d;
     a.total_tokens = total_tokens;
     a.chunk = chunk;
-    a.hp = ha::prefill_group(d, heads, dtype == HA_BF16);
+    a.hp = norm ? 1 : ha::prefill_group(d, heads, dtype == HA_BF16);
     a.spu = ha::prefill_spu(d, a.hp, heads / a.hp);
     a.slices = heads / a.hp * a.spu;
     a.n_req = n_req;
@@ -194,6 +199,93 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
     a.d = d;
     a.dtype_bf16 = dtype == HA_BF16;
     return hip_status(ha::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+ha_status hybrid_attn_step(const void* q, const void* k, const void* v, const float* state,
+                           const int32_t* slots, void* out, const int32_t* blk_lens,
+                           int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
+                           float scale, ha_dtype dtype, void* stream)
+{
+    return step_impl("hybrid_attn_step", q, k, v, state, nullptr, slots, out, blk_lens, n_req, n_slots, heads, blk,
+                     d, scale, dtype, stream, false);
+}
+
+ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v, float* state,
+                                  const int32_t* slots, void* out, const int32_t* blk_lens,
+                                  int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
+                                  float scale, ha_dtype dtype, void* stream)
+{
+    return step_commit_impl("hybrid_attn_step_commit", q, k, v, state, nullptr, slots, out, blk_lens, n_req,
+                            n_slots, heads, blk, d, scale, dtype, stream, false);
+}
+
+ha_status hybrid_state_commit(const void* k, const void* v, float* state, const int32_t* slots,
+                              const int32_t* blk_lens, int32_t n_req, int32_t n_slots,
+                              int32_t heads, int32_t blk, int32_t d, ha_dtype dtype, void* stream)
+{
+    return commit_impl("hybrid_state_commit", k, v, state, nullptr, slots, blk_lens, n_req, n_slots, heads, blk, d,
+                       dtype, stream, false);
+}
+
+size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads, int32_t d,
+                                            int64_t total_tokens, int64_t max_len, int32_t chunk)
+{
+    (void)total_tokens;
+    (void)max_len;
+    if (n_req <= 0 || heads <= 0 || d <= 0 || chunk <= 0) return 0;
+    return plan_bytes(n_req) + prefill_slots(n_req, heads, d) * ((size_t)d * (size_t)d + (size_t)d) * sizeof(float);
+}
+
+ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_seqlens,
+                               int64_t total_tokens, int64_t max_len, float* state,
+                               const int32_t* slots, int32_t n_req, int32_t n_slots,
+                               int32_t heads, int32_t d, int32_t chunk, void* workspace,
+                               size_t workspace_bytes, ha_dtype dtype, void* stream)
+{
+    return prefill_impl("hybrid_state_prefill", k, v, cu_seqlens, total_tokens, max_len, state, nullptr, slots,
+                        n_req, n_slots, heads, d, chunk, workspace, workspace_bytes, dtype, stream, false);
+}
+
+ha_status hybrid_attn_step_norm(const void* q, const void* k, const void* v, const float* state, const float* z,
+                                const int32_t* slots, void* out, const int32_t* blk_lens,
+                                int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
+                                float scale, ha_dtype dtype, void* stream)
+{
+    // the step only reads z; the argument block carries it as a writable
+    // pointer because the fused commit updates it
+    return step_impl("hybrid_attn_step_norm", q, k, v, state, const_cast<float*>(z), slots, out, blk_lens, n_req,
+                     n_slots, heads, blk, d, scale, dtype, stream, true);
+}
+
+ha_status hybrid_attn_step_commit_norm(const void* q, const void* k, const void* v, float* state, float* z,
+                                       const int32_t* slots, void* out, const int32_t* blk_lens,
+                                       int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk, int32_t d,
+                                       float scale, ha_dtype dtype, void* stream)
+{
+    return step_commit_impl("hybrid_attn_step_commit_norm", q, k, v, state, z, slots, out, blk_lens, n_req,
+                            n_slots, heads, blk, d, scale, dtype, stream, true);
+}
+
+ha_status hybrid_state_commit_norm(const void* k, const void* v, float* state, float* z, const int32_t* slots,
+                                   const int32_t* blk_lens, int32_t n_req, int32_t n_slots,
+                                   int32_t heads, int32_t blk, int32_t d, ha_dtype dtype, void* stream)
+{
+    return commit_impl("hybrid_state_commit_norm", k, v, state, z, slots, blk_lens, n_req, n_slots, heads, blk, d,
+                       dtype, stream, true);
+}
+
+ha_status hybrid_state_prefill_norm(const void* k, const void* v, const int64_t* cu_seqlens,
+                                    int64_t total_tokens, int64_t max_len, float* state, float* z,
+                                    const int32_t* slots, int32_t n_req, int32_t n_slots,
+                                    int32_t heads, int32_t d, int32_t chunk, void* workspace,
+                                    size_t workspace_bytes, ha_dtype dtype, void* stream)
+{
+    return prefill_impl("hybrid_state_prefill_norm", k, v, cu_seqlens, total_tokens, max_len, state, z, slots,
+                        n_req, n_slots, heads, d, chunk, workspace, workspace_bytes, dtype, stream, true);
 }
 
 size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads, int32_t blk, int32_t d)

@@ -15,6 +15,8 @@ struct StepArgs {
     const int32_t* slots;
     void* out;
     const int32_t* blk_lens;
+    float* z;                   // normalised variant: z = sum phi(k) [n_slots][heads][d]
+                                // (read by the step, updated by the fused commit); NULL: plain sum
     int32_t n_req, n_slots, heads, blk, d;
     float scale;
     bool dtype_bf16;
@@ -35,6 +37,9 @@ struct PhiKVArgs {
     const int64_t* cu;          // prefill: [n_req + 1]
     int64_t* plan;              // prefill workspace: [n_req + 2]
     float* partial;             // prefill workspace: [slices + n_req * heads][d][d]
+    float* z;                   // normalised variant: z = sum phi(k) [n_slots][heads][d] (prefill: overwritten);
+                                // NULL: plain
+    float* zpartial;            // prefill workspace, normalised variant: [slices + n_req * heads][d]
     int64_t total_tokens;       // prefill
     int32_t chunk;              // prefill
     int32_t slices;             // prefill: slice workgroups, spu per unit
@@ -107,6 +112,7 @@ inline int exact_slot_floats(int blk, int d) { return exact_slot_rows(blk) * (d 
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream);
+hipError_t launch_znorm_commit(const StepArgs& a, hipStream_t stream);
 hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream);
 hipError_t launch_exact(const ExactArgs& a, hipStream_t stream);

@@ -361,7 +361,7 @@ constexpr int prefill_threads() { return (PrefillTile<D, HP>::type::NW + Prefill
 // consecutive token rows, which HBM serves faster than rows 8 apart.  LDS
 // group g holds that permutation of the stage's tokens for K and V alike, so
 // the token reduction is unchanged.
-template <int D, int HP>
+template <int D, int HP, bool kNorm>
 __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_slices_bf16_mfma(PhiKVArgs a)
 {
     using P = typename PrefillTile<D, HP>::type;
@@ -428,6 +428,16 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
     f32x16 acc[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+    // normalised variant: z = sum phi(k) per feature, from the ReLU(K) operands
+    // the wave already reads.  The wave's first NZ tiles share one value-row
+    // tile and cover NZ distinct feature tiles; in the waves whose first tile
+    // is in value row 0 (the ones that write z), lane (l32, hh) sums in fp32
+    // its half of each k-step's tokens of feature 32 ft + l32.
+    constexpr int NZ = TPW < NT ? TPW : NT;
+    const bool zwriter = (w4 * TPW) / NT == 0;           // wave-uniform
+    float zacc[kNorm ? NZ : 1];
+#pragma unroll
+    for (int u = 0; u < (kNorm ? NZ : 1); ++u) zacc[u] = 0.f;
     auto mma_stage = [&](int buf) {
         const uint16_t* kt = lds[buf][0];
         const uint16_t* vt = lds[buf][1];
@@ -440,6 +450,25 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
                 const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(hw * D + ct * 32 + l32, g));
                 const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g));
                 acc[u] = mfma32(as_bf16x8(av), as_bf16x8(relu_bf16x8(bk)), acc[u]);
+            }
+        }
+    };
+    // normalised variant, writer waves: the stage's sums of phi(k), re-reading
+    // the K^T operands of the first NZ tiles after the multiplications
+    auto z_stage = [&](int buf) {
+        const uint16_t* kt = lds[buf][0];
+#pragma unroll
+        for (int s = 0; s < T / 16; ++s) {
+            const int g = 2 * s + hh;
+#pragma unroll
+            for (int u = 0; u < NZ; ++u) {
+                const int ft = (w4 * TPW + u) % NT;
+                const u32x4 w = __builtin_bit_cast(
+                    u32x4, relu_bf16x8(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g))));
+                float s8 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
+                zacc[u] += s8;
             }
         }
     };
@@ -471,11 +500,23 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
             if (!cp.live) return;              // uniform
             if constexpr (kMma) {
                 mma_stage(buf);
+                if constexpr (kNorm) {
+                    if (zwriter) z_stage(buf);
+                }
                 if (cp.t + T >= cp.t1) {
                     const int64_t piece = (int64_t)cp.h * a.n_req + cp.r;    // (unit, prompt) of the piece
                     tiles_io<D, WPH>(a.partial + (((int64_t)cp.sl.w + piece) * HP + hw) * D * D, acc, true, w4);
 #pragma unroll
                     for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+                    if constexpr (kNorm) {
+                        float* zp = a.zpartial + (((int64_t)cp.sl.w + piece) * HP + hw) * D;
+#pragma unroll
+                        for (int u = 0; u < NZ; ++u) {
+                            const float zs = zacc[u] + __shfl_xor(zacc[u], 32);
+                            if (zwriter && hh == 0) zp[((w4 * TPW + u) % NT) * 32 + l32] = zs;
+                            zacc[u] = 0.f;
+                        }
+                    }
                 }
             }
             ++sg;
@@ -508,13 +549,21 @@ __global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
         slice_piece(a, cur, h, t0, t1, p0);
         const T* kb = static_cast<const T*>(a.k) + p0 + t0 * rs;
         const T* vb = static_cast<const T*>(a.v) + p0 + t0 * rs;
-        float* dst = a.partial + ((int64_t)cur.w + (int64_t)h * a.n_req + cur.r) * D * D;
+        const int64_t piece = (int64_t)cur.w + (int64_t)h * a.n_req + cur.r;
+        float* dst = a.partial + piece * D * D;
         for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
             const int c = e / D, f = e % D;
             float acc = 0.f;
             for (int64_t t = 0; t < t1 - t0; ++t)
                 acc = fmaf(Elem<T>::load(vb, t * rs + c), relu(Elem<T>::load(kb, t * rs + f)), acc);
             dst[e] = acc;
+        }
+        if (a.z) {                                       // normalised variant: sum phi(k) of the piece
+            for (int f = threadIdx.x; f < D; f += blockDim.x) {
+                float acc = 0.f;
+                for (int64_t t = 0; t < t1 - t0; ++t) acc += relu(Elem<T>::load(kb, t * rs + f));
+                a.zpartial[piece * D + f] = acc;
+            }
         }
     }
 }
@@ -535,13 +584,21 @@ __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
     const int hu = h / a.hp, sub = h % a.hp;
     const int64_t S = a.plan[a.n_req + 1];
     const int64_t cfirst = a.plan[r], cend = a.plan[r + 1];
+    const int64_t piece = (int64_t)hu * a.n_req + r, w0 = (int64_t)hu * a.spu;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     if (cend > cfirst) {
-        const int64_t piece = (int64_t)hu * a.n_req + r, w0 = (int64_t)hu * a.spu;
         for (int64_t w = w0 + cfirst / S; w <= w0 + (cend - 1) / S; ++w)
             sum += reinterpret_cast<const f32x4*>(a.partial + ((w + piece) * a.hp + sub) * dd)[e4];
     }
     reinterpret_cast<f32x4*>(a.state + ((int64_t)slot * a.heads + h) * dd)[e4] = sum;
+    if (a.z && e4 < a.d / 4) {                           // normalised variant: z, the same way
+        f32x4 zs = {0.f, 0.f, 0.f, 0.f};
+        if (cend > cfirst) {
+            for (int64_t w = w0 + cfirst / S; w <= w0 + (cend - 1) / S; ++w)
+                zs += reinterpret_cast<const f32x4*>(a.zpartial + ((w + piece) * a.hp + sub) * a.d)[e4];
+        }
+        reinterpret_cast<f32x4*>(a.z + ((int64_t)slot * a.heads + h) * a.d)[e4] = zs;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -588,6 +645,26 @@ hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <bool kNorm>
+static void launch_prefill_slices(const PhiKVArgs& a, dim3 grid, hipStream_t stream)
+{
+    switch (a.d) {
+    case 32: prefill_slices_bf16_mfma<32, 1, kNorm><<<grid, prefill_threads<32, 1>(), 0, stream>>>(a); break;
+    case 64: prefill_slices_bf16_mfma<64, 1, kNorm><<<grid, prefill_threads<64, 1>(), 0, stream>>>(a); break;
+    default:
+        // (the normalised variant runs one head per workgroup: its z sums do
+        // not fit next to the head pair's 128 accumulator registers per wave)
+        if constexpr (!kNorm) {
+            if (a.hp == 2) {
+                prefill_slices_bf16_mfma<128, 2, false><<<grid, prefill_threads<128, 2>(), 0, stream>>>(a);
+                break;
+            }
+        }
+        prefill_slices_bf16_mfma<128, 1, kNorm><<<grid, prefill_threads<128, 1>(), 0, stream>>>(a);
+        break;
+    }
+}
+
 hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream)
 {
     prefill_plan<<<1, 256, 0, stream>>>(a);
@@ -596,16 +673,8 @@ hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream)
     if (a.total_tokens > 0) {
         const dim3 grid(a.slices);
         if (a.dtype_bf16 && a.d >= 32) {
-            switch (a.d) {
-            case 32: prefill_slices_bf16_mfma<32, 1><<<grid, prefill_threads<32, 1>(), 0, stream>>>(a); break;
-            case 64: prefill_slices_bf16_mfma<64, 1><<<grid, prefill_threads<64, 1>(), 0, stream>>>(a); break;
-            default:
-                if (a.hp == 2)
-                    prefill_slices_bf16_mfma<128, 2><<<grid, prefill_threads<128, 2>(), 0, stream>>>(a);
-                else
-                    prefill_slices_bf16_mfma<128, 1><<<grid, prefill_threads<128, 1>(), 0, stream>>>(a);
-                break;
-            }
+            if (a.z) launch_prefill_slices<true>(a, grid, stream);
+            else launch_prefill_slices<false>(a, grid, stream);
         } else if (a.dtype_bf16) {
             prefill_slices_generic<uint16_t><<<grid, 256, 0, stream>>>(a);
         } else {

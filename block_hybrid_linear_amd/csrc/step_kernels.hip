@@ -58,15 +58,76 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// Normalised variant (one denominator for the block's softmax scores and the
+// prefix's linear scores, z = sum phi(k) next to S): the output of a query is
+//   (sum_j 2^(l_j) v_j + phi(q) S) / (sum_j 2^(l_j) + phi(q).z)
+// with l_j its logits in log2 units.  Both sides are divided by 2^c,
+// c = max(m, log2(phi(q).z)), m the logits' maximum, so that the larger part
+// of the denominator is one and nothing overflows; given m, the block's sum
+// A = sum_j 2^(l_j - m) and qz = phi(q).z, alpha scales the probabilities
+// 2^(l_j - m) and beta the linear term phi(q) S.  (c is kept above -100, so
+// 2^-c stays finite; below that both parts would underflow anyway.)
+__device__ __forceinline__ void norm_weights(float m, float A, float qz, float& alpha, float& beta)
+{
+    float c = m;
+    if (qz > 0.f) c = fmaxf(c, __builtin_amdgcn_logf(qz));   // log2
+    c = fmaxf(c, -100.f);
+    const float ws = __builtin_amdgcn_exp2f(m - c), wl = __builtin_amdgcn_exp2f(-c);
+    const float inv = __builtin_amdgcn_rcpf(fmaf(ws, A, wl * qz));
+    alpha = ws * inv;
+    beta = wl * inv;
+}
+
+// phi(q).z for the query whose staged row starts at qrow (pitch D + 8 bf16)
+// against z staged in LDS: lane half hh sums features [hh D/2, hh D/2 + D/2),
+// then the halves are added (every lane returns its query's full sum).
+template <int D>
+__device__ __forceinline__ float query_dot_z(const uint16_t* qrow, const float* zl, int hh)
+{
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        const int f0 = hh * (D / 2) + 8 * c;
+        const u16x8 qv = relu_bf16x8(*reinterpret_cast<const u16x8*>(qrow + f0));
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zl + f0), z1 = *reinterpret_cast<const f32x4*>(zl + f0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(bf16_bits_to_f32(qv[e]), z0[e], acc);
+            acc = fmaf(bf16_bits_to_f32(qv[4 + e]), z1[e], acc);
+        }
+    }
+    return acc + __shfl_xor(acc, 32);
+}
+
+// Stages the unit's z (D floats) in LDS; threads 0 .. D/4 - 1 each copy 16 bytes.
+template <int D>
+__device__ __forceinline__ void stage_z(float* zl, const float* zg, int tid)
+{
+    if (tid < D / 4) reinterpret_cast<f32x4*>(zl)[tid] = reinterpret_cast<const f32x4*>(zg)[tid];
+}
+
+// z += sum over the block's first Br staged key rows (pitch D + 8 bf16, row
+// major) of phi(k): thread f < D owns feature f.
+template <int D>
+__device__ __forceinline__ void commit_z(float* zg, const uint16_t* sk, int Br, int tid)
+{
+    if (tid < D) {
+        float acc = 0.f;
+        for (int j = 0; j < Br; ++j) acc += relu(bf16_bits_to_f32(sk[j * (D + 8) + tid]));
+        zg[tid] += acc;
+    }
+}
+
 // Softmax part of one 32-query tile whose rows start at qtile in LDS:
 // L^T = K Q^T over the key tiles, row softmax over the Br valid keys (one
 // query per lane pair), O^T = V^T P^T with P as hi + lo bf16.  Returns the
 // wave's accumulator (value columns of tile ct, transposed).  Contraction of
 // the scaling and the max subtraction into one fma is switched off so that
 // every kernel that inlines this computes bit-identical probabilities.
-template <int D, int NKT>
+template <int D, int NKT, bool kNorm = false>
 __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint16_t* sk, const uint16_t* sv,
-                                               int Br, float sl2, int ct, int lane)
+                                               int Br, float sl2, int ct, int lane, float qz = 0.f,
+                                               float* beta = nullptr)
 {
 #pragma clang fp contract(off)
     constexpr int KS = D / 16, P = D + 8;
@@ -109,7 +170,9 @@ __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint
         }
     }
     sum += __shfl_xor(sum, 32);
-    const float inv = __builtin_amdgcn_rcpf(sum);
+    float inv;
+    if constexpr (kNorm) norm_weights(m, sum, qz, inv, *beta);   // probabilities over the shared denominator
+    else inv = __builtin_amdgcn_rcpf(sum);
     // V^T operand of k-step (jt, gp): keys jt*32 + 16gp + 4hh + {0..3} and the
     // same + 8, matching registers 8gp .. 8gp+7 of L^T; the column of lane i in
     // 16-lane group g is 32ct + 16(q%2) + 8(g%2) + 4(q/2) + i%4, q = i/4 (= cA).
@@ -157,7 +220,7 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* tile, const f32x16& o, 
 // Workgroups per XCD group: the NKT query tiles of 8 consecutive units.
 __host__ __device__ inline int step_grid(int units, int nkt) { return (units + 7) / 8 * 8 * nkt; }
 
-template <int D, int NKT>
+template <int D, int NKT, bool kNorm>
 __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;              // k-steps over the head dimension
@@ -170,6 +233,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     constexpr int CK = RK * CPR / NT;       // K (and V) chunks per thread
     static_assert(CQ * NT == 32 * CPR && CK * NT == RK * CPR, "even staging split");
     __shared__ __attribute__((aligned(16))) uint16_t sq[32 * P], sk[RK * P], sv[RK * P];
+    __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];   // normalised variant: the unit's z
 
     // workgroup -> (unit, query tile): the NKT tiles of a unit share b % 8
     const int b = blockIdx.x;
@@ -227,10 +291,14 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
         *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
         *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
     }
+    if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
     __syncthreads();
 
     // ---- softmax part (overlaps the S stream)
-    f32x16 o = softmax_tile<D, NKT>(sq, sk, sv, Br, sl2, ct, lane);
+    float qz = 0.f, beta = 1.f;
+    if constexpr (kNorm) qz = query_dot_z<D>(sq + l32 * P, sz, hh);
+    f32x16 o = softmax_tile<D, NKT, kNorm>(sq, sk, sv, Br, sl2, ct, lane, qz, &beta);
+    f32x16 olin = {};                                   // normalised variant: the linear part apart
     // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16 (fenced so its
     // phi(Q) operand reads are not hoisted into the softmax part, where the
     // logits already occupy the registers)
@@ -243,8 +311,17 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
         split_hi_lo(sv8, shi, slo);
         const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + l32 * P + 16 * s + 8 * hh);
         const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-        o = mfma32(shi, pq, o);
-        o = mfma32(slo, pq, o);
+        if constexpr (kNorm) {
+            olin = mfma32(shi, pq, olin);
+            olin = mfma32(slo, pq, olin);
+        } else {
+            o = mfma32(shi, pq, o);
+            o = mfma32(slo, pq, o);
+        }
+    }
+    if constexpr (kNorm) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) o[rr] = fmaf(beta, olin[rr], o[rr]);
     }
     // ---- store through LDS: lane holds query qt*32 + l32, columns
     // 32 ct + 16 hh + 0..15; the tile is written back row-major so that each
@@ -317,7 +394,7 @@ __device__ __forceinline__ f32x16 commit_tile(f32x16 acc, const uint16_t* sk, co
 // barrier and written once after it, by one wave; a unit's state is touched
 // by one workgroup, so requests only need distinct slots.
 // ---------------------------------------------------------------------------
-template <int D, int NKT, bool kCommit>
+template <int D, int NKT, bool kCommit, bool kNorm>
 __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;
@@ -337,6 +414,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     static_assert(CPT * NT == R * CPR && SPT * NT * 4 == D * D, "even staging split");
     __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
     __shared__ __attribute__((aligned(16))) float ss[kStageS ? D * PS : 4];   // the unit's S^T
+    __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];          // normalised variant: the unit's z
 
     const int unit = blockIdx.x;
     const int r = unit / a.heads, h = unit % a.heads;
@@ -401,10 +479,14 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
             *reinterpret_cast<f32x4*>(ss + row * PS + col) = sc[u];
         }
     }
+    if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
     __syncthreads();
 
     // ---- the step, from the old state
-    f32x16 o = softmax_tile<D, NKT>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane);
+    float qz = 0.f, beta = 1.f;
+    if constexpr (kNorm) qz = query_dot_z<D>(sq + (qt * 32 + l32) * P, sz, hh);
+    f32x16 o = softmax_tile<D, NKT, kNorm>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane, qz, &beta);
+    f32x16 olin = {};                                   // normalised variant: the linear part apart
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -421,8 +503,17 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
         split_hi_lo(sv8, shi, slo);
         const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
         const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-        o = mfma32(shi, pq, o);
-        o = mfma32(slo, pq, o);
+        if constexpr (kNorm) {
+            olin = mfma32(shi, pq, olin);
+            olin = mfma32(slo, pq, olin);
+        } else {
+            o = mfma32(shi, pq, o);
+            o = mfma32(slo, pq, o);
+        }
+    }
+    if constexpr (kNorm) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) o[rr] = fmaf(beta, olin[rr], o[rr]);
     }
     // outputs through LDS (sq is free now; the commit below still reads sk, sv)
     __syncthreads();
@@ -455,6 +546,9 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
     }
+    // normalised variant: z += sum phi(k) over the block (z was staged before
+    // the first barrier, so the step above used the old value)
+    if constexpr (kNorm) commit_z<D>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,7 +580,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int D, bool kCommit>
+template <int D, bool kCommit, bool kNorm>
 __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepArgs a)
 {
 #pragma clang fp contract(off)
@@ -499,6 +593,8 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     __shared__ __attribute__((aligned(16))) uint16_t shi[D * P], slo[D * P];   // S^T = hi + lo
     __shared__ __attribute__((aligned(16))) u16x8 sp[2][2][2][2][kWave];       // [qt][jt][gp][hi, lo][lane]
     __shared__ float smax[2][2][32], ssum[2][2][32];                            // [qt][jt][query]
+    __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];           // normalised variant: z
+    __shared__ float sqz[kNorm ? 2 : 1][32];                                    // and phi(q).z per query
 
     const int unit = blockIdx.x;
     const int r = unit / a.heads, h = unit % a.heads;
@@ -556,6 +652,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         *reinterpret_cast<u32x2*>(shi + row * P + col) = u32x2{h0, h1};
         *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
     }
+    if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
     __syncthreads();
 
     // with the commit: this wave's old state tiles (value rows 32 ct + 16 hh + r,
@@ -629,6 +726,12 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             smax[qt][jt][l32] = m;
             ssum[qt][jt][l32] = sum;
         }
+        if constexpr (kNorm) {
+            if (jt == 0) {                                // one wave per query tile publishes phi(q).z
+                const float qz = query_dot_z<D>(qrow - 8 * hh, sz, hh);
+                if (hh == 0) sqz[qt][l32] = qz;
+            }
+        }
     } else {
         linear();
     }
@@ -662,12 +765,28 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     __builtin_amdgcn_sched_barrier(0);
     const float m0 = smax[qt][0][l32], m1 = smax[qt][1][l32];
     const float mx = fmaxf(m0, m1);                  // finite: key 0 is valid
-    const float e0 = __builtin_amdgcn_exp2f(m0 - mx), e1 = __builtin_amdgcn_exp2f(m1 - mx);
-    const float inv = __builtin_amdgcn_rcpf(ssum[qt][0][l32] * e0 + ssum[qt][1][l32] * e1);
-    const float c0 = e0 * inv, c1 = e1 * inv;
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kNorm) {
+        // one denominator for both key tiles and the prefix: divide by 2^c,
+        // c = max(mx, log2(phi(q).z)) (as norm_weights does for one tile)
+        const float qz = sqz[qt][l32];
+        float c = mx;
+        if (qz > 0.f) c = fmaxf(c, __builtin_amdgcn_logf(qz));
+        c = fmaxf(c, -100.f);
+        const float e0 = __builtin_amdgcn_exp2f(m0 - c), e1 = __builtin_amdgcn_exp2f(m1 - c);
+        const float wl = __builtin_amdgcn_exp2f(-c);
+        const float inv = __builtin_amdgcn_rcpf(ssum[qt][0][l32] * e0 + ssum[qt][1][l32] * e1 + wl * qz);
+        const float c0 = e0 * inv, c1 = e1 * inv, beta = wl * inv;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) o[rr] = o[rr] + (opv[0][rr] * c0 + opv[1][rr] * c1);
+        for (int rr = 0; rr < 16; ++rr) o[rr] = o[rr] * beta + (opv[0][rr] * c0 + opv[1][rr] * c1);
+    } else {
+        const float e0 = __builtin_amdgcn_exp2f(m0 - mx), e1 = __builtin_amdgcn_exp2f(m1 - mx);
+        const float inv = __builtin_amdgcn_rcpf(ssum[qt][0][l32] * e0 + ssum[qt][1][l32] * e1);
+        const float c0 = e0 * inv, c1 = e1 * inv;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) o[rr] = o[rr] + (opv[0][rr] * c0 + opv[1][rr] * c1);
+    }
 
     // ---- the commit (before the outputs, so that the state stores drain while
     // the outputs are staged): wave (qt, ct) owns state rows [32 ct, 32 ct + 32)
@@ -683,6 +802,9 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
         }
+        // normalised variant: z += sum phi(k) over the block (the step used the
+        // copy staged before the first barrier)
+        if constexpr (kNorm) commit_z<D>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
     }
     // ---- outputs through LDS (every wave is done with sq after the barrier)
     __syncthreads();
@@ -829,7 +951,7 @@ __global__ __launch_bounds__(4 * D / 32 * kWave) void step_bf16_mfma_long(StepAr
 template <typename T>
 __global__ __launch_bounds__(256) void step_generic(StepArgs a)
 {
-    extern __shared__ float P[];                  // [Br][Br]
+    extern __shared__ float P[];                  // [Br][Br], then the linear term's weight per row
     const int D = a.d;
     const int unit = blockIdx.x;
     const int r = unit / a.heads, h = unit % a.heads;
@@ -852,6 +974,8 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
         P[idx] = a.scale * dot;
     }
     __syncthreads();
+    float* wlin = P + Br * Br;
+    const float* zg = a.z ? a.z + ((int64_t)slot * a.heads + h) * D : nullptr;
     for (int i = threadIdx.x; i < Br; i += blockDim.x) {
         float m = -INFINITY;
         for (int j = 0; j < Br; ++j) m = fmaxf(m, P[i * Br + j]);
@@ -861,15 +985,35 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
             P[i * Br + j] = p;
             sum += p;
         }
-        const float inv = 1.f / sum;
+        float inv = 1.f / sum, beta = 1.f;
+        if (zg) {
+            // normalised variant: one denominator, both sides divided by e^c,
+            // c = max(m, ln(phi(q).z)) (kept above -69, where e^-c stays finite)
+            float qz = 0.f;
+            for (int f = 0; f < D; ++f) qz = fmaf(relu(Elem<T>::load(q, i * rs + f)), zg[f], qz);
+            float c = m;
+            if (qz > 0.f) c = fmaxf(c, logf(qz));
+            c = fmaxf(c, -69.f);
+            const float ws = expf(m - c), wl = expf(-c);
+            const float den = fmaf(ws, sum, wl * qz);
+            inv = ws / den;
+            beta = wl / den;
+        }
         for (int j = 0; j < Br; ++j) P[i * Br + j] *= inv;
+        wlin[i] = beta;
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < Br * D; idx += blockDim.x) {
         const int i = idx / D, c = idx % D;
         float acc = 0.f;
         for (int j = 0; j < Br; ++j) acc = fmaf(P[i * Br + j], Elem<T>::load(v, j * rs + c), acc);
-        for (int f = 0; f < D; ++f) acc = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], acc);
+        if (zg) {
+            float lin = 0.f;
+            for (int f = 0; f < D; ++f) lin = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], lin);
+            acc = fmaf(wlin[i], lin, acc);
+        } else {
+            for (int f = 0; f < D; ++f) acc = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], acc);
+        }
         Elem<T>::store(out, i * rs + c, acc);
     }
 }
@@ -878,38 +1022,98 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
 template <int D>
 static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
 {
-    if (a.blk <= 32) step_bf16_mfma<D, 1><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
+    if (a.blk <= 32) step_bf16_mfma<D, 1, false><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
     else if (a.blk <= 64) {
-        if constexpr (D >= 64) step_pair_bf16_mfma<D, false><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
-        else step_bf16_mfma<D, 2><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
+        if constexpr (D >= 64) step_pair_bf16_mfma<D, false, false><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
+        else step_bf16_mfma<D, 2, false><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
     }
     else step_bf16_mfma_long<D><<<units, 4 * D / 32 * kWave, 0, stream>>>(a);
+}
+
+// Normalised variant on the matrix cores: blocks of up to 32 rows (d >= 32)
+// and 33..64 rows (d = 64, 128); returns false for the shapes that take the
+// fp32 kernel.
+template <int D>
+static bool launch_step_norm_d(const StepArgs& a, int units, hipStream_t stream)
+{
+    if (a.blk <= 32) {
+        step_bf16_mfma<D, 1, true><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
+        return true;
+    }
+    if constexpr (D >= 64) {
+        if (a.blk <= 64) {
+            step_pair_bf16_mfma<D, false, true><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
+            return true;
+        }
+    }
+    return false;
+}
+
+// z += sum over the block's first B_r rows of phi(k), one workgroup per
+// (request, head), thread f < d owning feature f (the normaliser state of the
+// normalised variant; the commit of S runs separately).
+template <typename T>
+__global__ __launch_bounds__(128) void znorm_commit(StepArgs a)
+{
+    const int D = a.d;
+    const int r = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
+    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    Br = Br > a.blk ? a.blk : Br;
+    const int slot = a.slots[r];
+    const int f = threadIdx.x;
+    if (Br <= 0 || slot < 0 || slot >= a.n_slots || f >= D) return;
+    const int64_t rs = (int64_t)a.heads * D;
+    const T* kb = static_cast<const T*>(a.k) + ((int64_t)r * a.blk * a.heads + h) * D + f;
+    float acc = 0.f;
+    for (int j = 0; j < Br; ++j) acc += relu(Elem<T>::load(kb, j * rs));
+    a.z[((int64_t)slot * a.heads + h) * D + f] += acc;
+}
+
+hipError_t launch_znorm_commit(const StepArgs& a, hipStream_t stream)
+{
+    const int units = a.n_req * a.heads;
+    if (a.dtype_bf16) znorm_commit<uint16_t><<<units, 128, 0, stream>>>(a);
+    else znorm_commit<float><<<units, 128, 0, stream>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
 {
     const int units = a.n_req * a.heads;
-    if (a.dtype_bf16 && a.d >= 32 && a.blk <= 64) {
+    const bool norm = a.z != nullptr;
+    if (a.dtype_bf16 && a.d >= 32 && a.blk <= 64 && !(norm && a.d == 32 && a.blk > 32)) {
         const bool two = a.blk > 32;
         const dim3 block((two ? 2 : 1) * a.d / 32 * kWave);
         switch (a.d) {
         case 32:
-            if (two) step_commit_bf16_mfma<32, 2, true><<<units, block, 0, stream>>>(a);
-            else step_commit_bf16_mfma<32, 1, true><<<units, block, 0, stream>>>(a);
+            if (norm) step_commit_bf16_mfma<32, 1, true, true><<<units, block, 0, stream>>>(a);
+            else if (two) step_commit_bf16_mfma<32, 2, true, false><<<units, block, 0, stream>>>(a);
+            else step_commit_bf16_mfma<32, 1, true, false><<<units, block, 0, stream>>>(a);
             break;
         case 64:
-            if (two) step_pair_bf16_mfma<64, true><<<units, block, 0, stream>>>(a);
-            else step_commit_bf16_mfma<64, 1, true><<<units, block, 0, stream>>>(a);
+            if (two) {
+                if (norm) step_pair_bf16_mfma<64, true, true><<<units, block, 0, stream>>>(a);
+                else step_pair_bf16_mfma<64, true, false><<<units, block, 0, stream>>>(a);
+            } else {
+                if (norm) step_commit_bf16_mfma<64, 1, true, true><<<units, block, 0, stream>>>(a);
+                else step_commit_bf16_mfma<64, 1, true, false><<<units, block, 0, stream>>>(a);
+            }
             break;
         default:
-            if (two) step_pair_bf16_mfma<128, true><<<units, block, 0, stream>>>(a);
-            else step_commit_bf16_mfma<128, 1, true><<<units, block, 0, stream>>>(a);
+            if (two) {
+                if (norm) step_pair_bf16_mfma<128, true, true><<<units, block, 0, stream>>>(a);
+                else step_pair_bf16_mfma<128, true, false><<<units, block, 0, stream>>>(a);
+            } else {
+                if (norm) step_commit_bf16_mfma<128, 1, true, true><<<units, block, 0, stream>>>(a);
+                else step_commit_bf16_mfma<128, 1, true, false><<<units, block, 0, stream>>>(a);
+            }
             break;
         }
         return hipGetLastError();
     }
-    // other shapes: the step, then the commit, on the same stream
-    const hipError_t e = launch_step(a, stream);
+    // other shapes: the step, then the commit (and the normaliser's), on the
+    // same stream
+    hipError_t e = launch_step(a, stream);
     if (e != hipSuccess) return e;
     PhiKVArgs c{};
     c.k = a.k;
@@ -923,20 +1127,33 @@ hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
     c.blk = a.blk;
     c.d = a.d;
     c.dtype_bf16 = a.dtype_bf16;
-    return launch_commit(c, stream);
+    e = launch_commit(c, stream);
+    if (e != hipSuccess || !norm) return e;
+    return launch_znorm_commit(a, stream);
 }
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream)
 {
     const int units = a.n_req * a.heads;
+    bool done = false;
     if (a.dtype_bf16 && a.d >= 32) {
-        switch (a.d) {
-        case 32: launch_step_d<32>(a, units, stream); break;
-        case 64: launch_step_d<64>(a, units, stream); break;
-        default: launch_step_d<128>(a, units, stream); break;
+        done = true;
+        if (a.z) {
+            switch (a.d) {
+            case 32: done = launch_step_norm_d<32>(a, units, stream); break;
+            case 64: done = launch_step_norm_d<64>(a, units, stream); break;
+            default: done = launch_step_norm_d<128>(a, units, stream); break;
+            }
+        } else {
+            switch (a.d) {
+            case 32: launch_step_d<32>(a, units, stream); break;
+            case 64: launch_step_d<64>(a, units, stream); break;
+            default: launch_step_d<128>(a, units, stream); break;
+            }
         }
-    } else {
-        const size_t lds = sizeof(float) * (size_t)a.blk * a.blk;
+    }
+    if (!done) {
+        const size_t lds = sizeof(float) * ((size_t)a.blk * a.blk + a.blk);
         if (a.dtype_bf16) step_generic<uint16_t><<<units, 256, lds, stream>>>(a);
         else step_generic<float><<<units, 256, lds, stream>>>(a);
     }

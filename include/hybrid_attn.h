@@ -177,13 +177,76 @@ ha_status hybrid_state_prefill(const void* k, const void* v,
                                void* workspace, size_t workspace_bytes,
                                ha_dtype dtype, void* stream);
 
-/* Workspace size for hybrid_state_prefill with the same arguments (host):
- * the plan ((n_req + 2) int64, padded to 256 bytes) and
- * (max(W, heads) + n_req * heads) fp32 d x d partial states, W = 2048 for
- * d = 32 and 512 otherwise; 0 when n_req, heads, d or chunk is <= 0. */
+/* Workspace size for hybrid_state_prefill and hybrid_state_prefill_norm with
+ * the same arguments (host): the plan ((n_req + 2) int64, padded to 256
+ * bytes) and (max(W, heads) + n_req * heads) fp32 partial states of d x d + d
+ * floats (S and z), W = 2048 for d = 32 and 512 otherwise; 0 when n_req,
+ * heads, d or chunk is <= 0. */
 size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads,
                                             int32_t d, int64_t total_tokens,
                                             int64_t max_len, int32_t chunk);
+
+/*
+ * Normalised variant.  The pages say the retrofit largely follows LoLCATs
+ * (summary page, sections "problem solving" and "method"; abstract page) and
+ * print no formula for a normaliser; the reading implemented here is that
+ * method's hybrid attention with one shared denominator: for query i of the
+ * active block,
+ *
+ *   O_i = (sum_j exp(l_ij) v_j + phi(q_i) S) / (sum_j exp(l_ij) + phi(q_i) . z)
+ *
+ * over the B_r valid block keys j (l_ij = scale <q_i, k_j>), with a second
+ * per-(slot, head) state z = sum over committed / prompt tokens of phi(k)
+ * next to S.  With S = 0 and z = 0 (no previous block) it is plain softmax
+ * attention over the block.
+ *
+ * z: device fp32 [n_slots][heads][d], 16-byte aligned.  The calls below take
+ * the arguments of their plain counterparts plus z and keep their
+ * conventions (slots, blk_lens, alignment, errors); z is required (NULL is
+ * HA_ERR_INVALID_ARG).  Per query, both sides are divided by
+ * exp(max(m_i, ln(phi(q_i) . z))) (m_i the block's largest logit), so the
+ * denominator's larger part is one; results are undefined only when both
+ * parts underflow fp32.
+ *
+ * hybrid_attn_step_norm: the output above; reads S and z.
+ * hybrid_attn_step_commit_norm: the same output from the old S and z, then
+ *   S += phi(K)^T V and z += sum_j phi(k_j) over the block's valid rows.
+ * hybrid_state_commit_norm: S += phi(K)^T V and z += sum_j phi(k_j).
+ * hybrid_state_prefill_norm: S and z of each request's slot overwritten by
+ *   the sums over its prompt (an empty prompt gives S = 0, z = 0); the
+ *   workspace is hybrid_state_prefill_workspace_bytes(...).
+ */
+ha_status hybrid_attn_step_norm(const void* q, const void* k, const void* v,
+                                const float* state, const float* z,
+                                const int32_t* slots, void* out,
+                                const int32_t* blk_lens, int32_t n_req,
+                                int32_t n_slots, int32_t heads, int32_t blk,
+                                int32_t d, float scale, ha_dtype dtype,
+                                void* stream);
+
+ha_status hybrid_attn_step_commit_norm(const void* q, const void* k,
+                                       const void* v, float* state, float* z,
+                                       const int32_t* slots, void* out,
+                                       const int32_t* blk_lens, int32_t n_req,
+                                       int32_t n_slots, int32_t heads,
+                                       int32_t blk, int32_t d, float scale,
+                                       ha_dtype dtype, void* stream);
+
+ha_status hybrid_state_commit_norm(const void* k, const void* v, float* state,
+                                   float* z, const int32_t* slots,
+                                   const int32_t* blk_lens, int32_t n_req,
+                                   int32_t n_slots, int32_t heads, int32_t blk,
+                                   int32_t d, ha_dtype dtype, void* stream);
+
+ha_status hybrid_state_prefill_norm(const void* k, const void* v,
+                                    const int64_t* cu_seqlens,
+                                    int64_t total_tokens, int64_t max_len,
+                                    float* state, float* z,
+                                    const int32_t* slots, int32_t n_req,
+                                    int32_t n_slots, int32_t heads, int32_t d,
+                                    int32_t chunk, void* workspace,
+                                    size_t workspace_bytes, ha_dtype dtype,
+                                    void* stream);
 
 /*
  * The exact step that block-hybrid attention replaces (paper abstract: without

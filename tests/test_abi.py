@@ -32,7 +32,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("hybrid_attn_step", "hybrid_attn_step_commit", "hybrid_state_commit", "hybrid_state_prefill",
               "hybrid_state_prefill_workspace_bytes", "hybrid_exact_step", "hybrid_exact_step_workspace_bytes",
-              "hybrid_last_error", "hybrid_abi_version"):
+              "hybrid_attn_step_norm", "hybrid_attn_step_commit_norm", "hybrid_state_commit_norm",
+              "hybrid_state_prefill_norm", "hybrid_last_error", "hybrid_abi_version"):
         assert n in names
 
 
@@ -74,6 +75,29 @@ def exact(lib, q=1, k=1, v=1, kc=1, vc=1, cu=1, total=100, out=1, n_req=2, heads
           chunk=256, ws=1, ws_bytes=1 << 40, dtype=binding.HA_BF16):
     return lib.hybrid_exact_step(q, k, v, kc, vc, cu, total, out, None, n_req, heads, blk, d, scale, chunk, ws,
                                  ws_bytes, dtype, None)
+
+
+def step_norm(lib, q=1, k=1, v=1, state=1, z=1, slots=1, out=1, n_req=2, n_slots=2, heads=4, blk=32, d=64,
+              scale=0.125, dtype=binding.HA_BF16):
+    return lib.hybrid_attn_step_norm(q, k, v, state, z, slots, out, None, n_req, n_slots, heads, blk, d, scale,
+                                     dtype, None)
+
+
+def step_commit_norm(lib, q=1, k=1, v=1, state=1, z=1, slots=1, out=1, n_req=2, n_slots=2, heads=4, blk=32, d=64,
+                     scale=0.125, dtype=binding.HA_BF16):
+    return lib.hybrid_attn_step_commit_norm(q, k, v, state, z, slots, out, None, n_req, n_slots, heads, blk, d,
+                                            scale, dtype, None)
+
+
+def commit_norm(lib, k=1, v=1, state=1, z=1, slots=1, n_req=2, n_slots=2, heads=4, blk=32, d=64,
+                dtype=binding.HA_BF16):
+    return lib.hybrid_state_commit_norm(k, v, state, z, slots, None, n_req, n_slots, heads, blk, d, dtype, None)
+
+
+def prefill_norm(lib, k=1, v=1, cu=1, total=100, max_len=60, state=1, z=1, slots=1, n_req=2, n_slots=2, heads=4,
+                 d=64, chunk=256, ws=1, ws_bytes=1 << 40, dtype=binding.HA_BF16):
+    return lib.hybrid_state_prefill_norm(k, v, cu, total, max_len, state, z, slots, n_req, n_slots, heads, d, chunk,
+                                         ws, ws_bytes, dtype, None)
 
 
 def last(lib):
@@ -155,6 +179,28 @@ def test_exact_rejects(lib, kw, status, msg):
     assert msg in last(lib) and "hybrid_exact_step" in last(lib)
 
 
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=100), binding.HA_ERR_UNSUPPORTED, "head dim"),
+    (dict(blk=129), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(scale=float("nan")), binding.HA_ERR_INVALID_ARG, "scale"),
+    (dict(z=None), binding.HA_ERR_INVALID_ARG, "z"),
+    (dict(state=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),
+])
+def test_norm_calls_reject(lib, kw, status, msg):
+    """The normalised calls keep their plain counterparts' checks and require z."""
+    for fn, name in ((step_norm, "hybrid_attn_step_norm"), (step_commit_norm, "hybrid_attn_step_commit_norm")):
+        assert fn(lib, **kw) == status
+        assert msg in last(lib) and name in last(lib)
+    ckw = {key: val for key, val in kw.items() if key != "scale"}
+    if ckw:
+        assert commit_norm(lib, **ckw) == status
+        assert msg in last(lib) and "hybrid_state_commit_norm" in last(lib)
+    pkw = {key: val for key, val in kw.items() if key not in ("scale", "blk")}
+    if pkw:
+        assert prefill_norm(lib, **pkw) == status
+        assert msg in last(lib) and "hybrid_state_prefill_norm" in last(lib)
+
+
 A = 1 << 12   # a fake, suitably aligned device address (never dereferenced: the calls fail validation)
 
 
@@ -168,14 +214,21 @@ A = 1 << 12   # a fake, suitably aligned device address (never dereferenced: the
     ("exact", dict(vc=A + 2), "16-byte"),
     ("exact", dict(out=A + 8), "16-byte"),
     ("exact", dict(ws=A + 128), "256-byte"),
+    ("step_norm", dict(z=A + 4), "16-byte"),
+    ("commit_norm", dict(z=A + 8), "16-byte"),
+    ("prefill_norm", dict(z=A + 12), "16-byte"),
 ])
 def test_misaligned_pointers_rejected(lib, call, kw, msg):
-    fn = {"step": step, "step_commit": step_commit, "commit": commit, "prefill": prefill, "exact": exact}[call]
+    fn = {"step": step, "step_commit": step_commit, "commit": commit, "prefill": prefill, "exact": exact,
+          "step_norm": step_norm, "commit_norm": commit_norm, "prefill_norm": prefill_norm}[call]
     base = {"step": dict(q=A, k=A, v=A, state=A, slots=A, out=A),
             "step_commit": dict(q=A, k=A, v=A, state=A, slots=A, out=A),
             "commit": dict(k=A, v=A, state=A, slots=A),
             "prefill": dict(k=A, v=A, cu=A, state=A, slots=A, ws=A),
-            "exact": dict(q=A, k=A, v=A, kc=A, vc=A, cu=A, out=A, ws=A)}[call]
+            "exact": dict(q=A, k=A, v=A, kc=A, vc=A, cu=A, out=A, ws=A),
+            "step_norm": dict(q=A, k=A, v=A, state=A, slots=A, out=A),
+            "commit_norm": dict(k=A, v=A, state=A, slots=A),
+            "prefill_norm": dict(k=A, v=A, cu=A, state=A, slots=A, ws=A)}[call]
     base.update(kw)
     assert fn(lib, **base) == binding.HA_ERR_INVALID_ARG
     assert msg in last(lib)
@@ -190,20 +243,25 @@ def test_empty_batches_are_noops(lib):
                    n_req=0) == binding.HA_OK
     assert exact(lib, q=None, k=None, v=None, kc=None, vc=None, cu=None, out=None, ws=None, ws_bytes=0,
                  n_req=0) == binding.HA_OK
+    assert step_norm(lib, q=None, k=None, v=None, state=None, z=None, slots=None, out=None,
+                     n_req=0) == binding.HA_OK
+    assert commit_norm(lib, k=None, v=None, state=None, z=None, slots=None, n_req=0) == binding.HA_OK
+    assert prefill_norm(lib, k=None, v=None, cu=None, state=None, z=None, slots=None, ws=None, ws_bytes=0,
+                        n_req=0) == binding.HA_OK
 
 
 def test_prefill_workspace_size(lib):
-    """Plan (n_req + 2 int64, padded to 256 bytes) + one fp32 d x d partial
-    per (slice, unit) slot: max(512 (2048 for d = 32), heads) + n_req *
-    heads."""
+    """Plan (n_req + 2 int64, padded to 256 bytes) + one fp32 partial of
+    d x d + d floats (S and the normalised variant's z) per (slice, unit)
+    slot: max(512 (2048 for d = 32), heads) + n_req * heads slots."""
     f = bh.hybrid_state_prefill_workspace_bytes
     plan = lambda n: ((n + 2) * 8 + 255) // 256 * 256  # noqa: E731
-    assert f(2, 4, 64, 100, 0, 256) == plan(2) + (512 + 8) * 64 * 64 * 4
-    assert f(8, 32, 128, 10 ** 6, 65536, 256) == plan(8) + (512 + 256) * 128 * 128 * 4
-    assert f(1, 1, 32, 0, 0, 1) == plan(1) + (2048 + 1) * 32 * 32 * 4
-    assert f(40, 2, 16, 0, 0, 7) == plan(40) + (512 + 80) * 16 * 16 * 4
-    assert f(2, 600, 64, 10, 0, 256) == plan(2) + (600 + 1200) * 64 * 64 * 4
-    assert f(1, 3000, 32, 10, 0, 256) == plan(1) + (3000 + 3000) * 32 * 32 * 4
+    assert f(2, 4, 64, 100, 0, 256) == plan(2) + (512 + 8) * (64 * 64 + 64) * 4
+    assert f(8, 32, 128, 10 ** 6, 65536, 256) == plan(8) + (512 + 256) * (128 * 128 + 128) * 4
+    assert f(1, 1, 32, 0, 0, 1) == plan(1) + (2048 + 1) * (32 * 32 + 32) * 4
+    assert f(40, 2, 16, 0, 0, 7) == plan(40) + (512 + 80) * (16 * 16 + 16) * 4
+    assert f(2, 600, 64, 10, 0, 256) == plan(2) + (600 + 1200) * (64 * 64 + 64) * 4
+    assert f(1, 3000, 32, 10, 0, 256) == plan(1) + (3000 + 3000) * (32 * 32 + 32) * 4
     assert f(0, 1, 16, 0, 10, 1) == 0
     assert f(3, 1, 16, 0, 10, 0) == 0
 

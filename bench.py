@@ -333,6 +333,62 @@ def exact_context(dev="cuda", rotate: int = 4) -> dict:
     return res
 
 
+def norm_context(dev="cuda", rotate: int = 4) -> dict:
+    """The normalised variant (one denominator for block softmax and prefix
+    linear scores, z = sum phi(k) next to S) beside the plain calls: the step
+    at the serving shapes (rotating input sets, as in exact_context), the step
+    and fused step + commit at the prefill + decode workload's block shape,
+    and its prefill (one head per workgroup) against the plain prefill."""
+    res = {}
+    W = SERVING_STEP
+    n, H, d, B = W.n_req, W.heads, W.d, W.blk
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    sets = []
+    for i in range(rotate):
+        S = synth.normal((n, H, d, d), synth.seed_of(W.index, i, 0, synth.TENSOR_S), dtype=torch.float32, device=dev)
+        z = synth.normal((n, H, d), synth.seed_of(W.index, i, 1, synth.TENSOR_S), dtype=torch.float32,
+                         device=dev).abs_().mul_(1000.0)
+        q, k, v = (synth.normal((n, B, H, d), synth.seed_of(W.index, i, 0, t), device=dev) for t in range(3))
+        sets.append((q, k, v, S, z, torch.empty_like(q)))
+    plain = [bh.prepare_step(q, k, v, S, slots, out, scale=W.scale) for q, k, v, S, z, out in sets]
+    norm = [bh.prepare_step_norm(q, k, v, S, z, slots, out, scale=W.scale) for q, k, v, S, z, out in sets]
+    it = iter(range(1 << 30))
+    t_p = time_call(lambda: plain[next(it) % rotate](), 48)
+    t_n = time_call(lambda: norm[next(it) % rotate](), 48)
+    hb, _ = step_cost(n * H, B, d)
+    res["serving_step"] = {"workload": W.name, "plain_us": round(t_p * 1e3, 2), "norm_us": round(t_n * 1e3, 2),
+                           "norm_GBps": round((hb + n * H * d * 4) / (t_n * 1e-3) / 1e9, 1)}
+    del sets, plain, norm
+    W = PREFILL_DECODE
+    n, H, d, B = W.n_req, W.heads, W.d, W.blk
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    S = torch.zeros((n, H, d, d), dtype=torch.float32, device=dev)
+    z = torch.zeros((n, H, d), dtype=torch.float32, device=dev)
+    q, k, v = (synth.normal((n, B, H, d), synth.seed_of(W.index, 0, 0, t), device=dev) for t in range(3))
+    out = torch.empty_like(q)
+    calls = {"step": (bh.prepare_step(q, k, v, S, slots, out), bh.prepare_step_norm(q, k, v, S, z, slots, out)),
+             "step_commit": (bh.prepare_step_commit(q, k, v, S, slots, out),
+                             bh.prepare_step_commit_norm(q, k, v, S, z, slots, out))}
+    for name, (fp, fn) in calls.items():
+        res[f"decode_{name}"] = {"plain_us": round(time_call(fp, 48) * 1e3, 2),
+                                 "norm_us": round(time_call(fn, 48) * 1e3, 2)}
+    lens = synth.uniform_int(n, *W.prompt_range, synth.seed_of(W.index, tensor=synth.TENSOR_LEN))
+    cu = synth.cu_from_lengths(lens)
+    total = int(cu[-1])
+    kp = synth.normal((total, H, d), synth.seed_of(W.index, PROMPT_BLOCK, 0, synth.TENSOR_K), device=dev)
+    vp = synth.normal((total, H, d), synth.seed_of(W.index, PROMPT_BLOCK, 0, synth.TENSOR_V), device=dev)
+    cud = cu.to(dev)
+    fp = bh.prepare_prefill(kp, vp, cud, S, slots, chunk=W.chunk)
+    fn = bh.prepare_prefill_norm(kp, vp, cud, S, z, slots, chunk=W.chunk)
+    t_p, t_n = time_call(fp, 5), time_call(fn, 5)
+    pb, _ = prefill_cost(total * H, n * H, d)
+    res["prefill"] = {"workload": W.name, "plain_us": round(t_p * 1e3, 1), "norm_us": round(t_n * 1e3, 1),
+                      "norm_GBps": round(pb / (t_n * 1e-3) / 1e9, 1)}
+    del kp, vp
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------
 # Layer-stack timing: one denoising step of a 20-layer stand-in stack (random
 # bf16 weights; RMSNorm, Q/K/V projections, attention, output projection,
@@ -585,6 +641,8 @@ def main():
     if not args.no_context:
         log("[bench] context: hybrid step vs exact full-prefix step at the serving shapes")
         result["context"] = exact_context()
+        log("[bench] context: the normalised variant beside the plain calls")
+        result["context"]["norm"] = norm_context()
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(job, args.cpu_budget)

@@ -86,6 +86,21 @@ template <> struct Elem<uint16_t> {
 
 __device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }
 
+// Max and sum of x over lane pairs (i, i + 32), returned in both lanes.  The
+// permlane32 swap hands every lane the value of lanes 0-31 and of lanes 32-63
+// in one VALU op (no LDS round trip); both halves add the two operands in the
+// same order, so the result is the same in the pair.
+__device__ __forceinline__ float half_pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Read of a small per-request array (offsets, plans, lengths) at an index that
 // is the same in every lane, through the scalar cache.  The data is written
 // by the host or by an earlier kernel, never by the reading kernel, and a

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(D / 32 * kWave) __attribute__((amdgpu_waves_per_eu(
                 lt[rr] = xv;
                 mt = fmaxf(mt, xv);
             }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = half_pair_max(mt);
             const float mo = sm[qt][l32];
             const float mn = fmaxf(mo, mt);
             const float corr = __builtin_amdgcn_exp2f(mo - mn);     // 0 on the piece's first stage
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(D / 32 * kWave) __attribute__((amdgpu_waves_per_eu(
                 lt[rr] = p;
                 ls += p;
             }
-            ls += __shfl_xor(ls, 32);
+            ls = half_pair_sum(ls);
             const float ln = sl[qt][l32] * corr + ls;
 #pragma unroll
             for (int gp = 0; gp < 2; ++gp) {

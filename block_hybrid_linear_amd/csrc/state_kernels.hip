@@ -512,7 +512,7 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
                         float* zp = a.zpartial + (((int64_t)cp.sl.w + piece) * HP + hw) * D;
 #pragma unroll
                         for (int u = 0; u < NZ; ++u) {
-                            const float zs = zacc[u] + __shfl_xor(zacc[u], 32);
+                            const float zs = half_pair_sum(zacc[u]);
                             if (zwriter && hh == 0) zp[((w4 * TPW + u) % NT) * 32 + l32] = zs;
                             zacc[u] = 0.f;
                         }

@@ -96,7 +96,7 @@ __device__ __forceinline__ float query_dot_z(const uint16_t* qrow, const float* 
             acc = fmaf(bf16_bits_to_f32(qv[4 + e]), z1[e], acc);
         }
     }
-    return acc + __shfl_xor(acc, 32);
+    return half_pair_sum(acc);
 }
 
 // Stages the unit's z (D floats) in LDS; threads 0 .. D/4 - 1 each copy 16 bytes.
@@ -158,7 +158,7 @@ __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint
             m = fmaxf(m, x);
         }
     }
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = half_pair_max(m);
     float sum = 0.f;
 #pragma unroll
     for (int jt = 0; jt < NKT; ++jt) {
@@ -169,7 +169,7 @@ __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint
             sum += p;
         }
     }
-    sum += __shfl_xor(sum, 32);
+    sum = half_pair_sum(sum);
     float inv;
     if constexpr (kNorm) norm_weights(m, sum, qz, inv, *beta);   // probabilities over the shared denominator
     else inv = __builtin_amdgcn_rcpf(sum);
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             lt[rr] = x;
             m = fmaxf(m, x);
         }
-        m = fmaxf(m, __shfl_xor(m, 32));
+        m = half_pair_max(m);
         const float mb = m == -INFINITY ? 0.f : m;   // key tile 1 has no valid key when B_r <= 32
         float sum = 0.f;
 #pragma unroll
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             lt[rr] = p;
             sum += p;
         }
-        sum += __shfl_xor(sum, 32);
+        sum = half_pair_sum(sum);
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
             float pp[8];
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(4 * D / 32 * kWave) void step_bf16_mfma_long(StepAr
             lt[rr] = x;
             mt = fmaxf(mt, x);
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = half_pair_max(mt);
         const float mn = fmaxf(m, mt);
         const float corr = __builtin_amdgcn_exp2f(m - mn);     // 0 on the first tile
         float ls = 0.f;
@@ -899,7 +899,7 @@ __global__ __launch_bounds__(4 * D / 32 * kWave) void step_bf16_mfma_long(StepAr
             lt[rr] = p;
             ls += p;
         }
-        ls += __shfl_xor(ls, 32);
+        ls = half_pair_sum(ls);
         l = l * corr + ls;
         m = mn;
 #pragma unroll

@@ -562,9 +562,12 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 //  - each of the four 32 x 32 logit tiles (query tile qt, key tile jt) is
 //    computed by one wave, which also takes the tile's row max and row sum and
 //    writes the tile's probabilities relative to that max (hi + lo bf16, in
-//    its lane order) to LDS; waves without a logit tile do their linear part
-//    meanwhile.
-// After one barrier every wave multiplies V^T by both probability tiles of its
+//    its lane order) to LDS.
+// The state loads are issued right after the Q/K/V loads, but only Q, K and V
+// are staged before the first barrier: the logit waves run their softmax while
+// the state (the larger part of the bytes, which arrives last) is still in
+// flight, and every wave stages its share of S^T after that.
+// After the second barrier every wave multiplies V^T by both probability tiles of its
 // query tile into two accumulators and merges them with the two-tile softmax
 // correction: with tile maxima m_j, sums l_j and M = max_j m_j, the weights are
 // 2^(m_j - M) / sum_j l_j 2^(m_j - M).  With D = 128 the logit tiles go to
@@ -643,21 +646,12 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
         *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
     }
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-        const int c4 = tid + u * NT, row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
-        uint32_t h0, h1, l0, l1;
-        split_hi_lo2(f32x2{sc[u][0], sc[u][1]}, h0, l0);
-        split_hi_lo2(f32x2{sc[u][2], sc[u][3]}, h1, l1);
-        *reinterpret_cast<u32x2*>(shi + row * P + col) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
-    }
     if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
     __syncthreads();
 
     // with the commit: this wave's old state tiles (value rows 32 ct + 16 hh + r,
     // features 32 ft + l32 in register r; ft = qt, qt + 2, ..) re-read in the
-    // accumulator layout now (L2 hits: the rows were just streamed), so that
+    // accumulator layout now (cache hits: the same rows are in flight), so that
     // they have arrived when the commit runs after the step
     constexpr int NFT = kCommit ? NC / 2 : 1;
     f32x16 old[NFT];
@@ -732,8 +726,17 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
                 if (hh == 0) sqz[qt][l32] = qz;
             }
         }
-    } else {
-        linear();
+    }
+    // S^T into LDS as hi + lo bf16 (waits for this thread's state loads)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int c4 = tid + u * NT, row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
+        uint32_t h0, h1, l0, l1;
+        split_hi_lo2(f32x2{sc[u][0], sc[u][1]}, h0, l0);
+        split_hi_lo2(f32x2{sc[u][2], sc[u][3]}, h1, l1);
+        *reinterpret_cast<u32x2*>(shi + row * P + col) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
     }
     __syncthreads();
 
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][1][lane]), opv[jt]);
         }
     }
-    if (has_l) linear();
+    linear();
     // keep the softmax statistics' LDS reads (and their wait) between the
     // matrix-core work above and the first use of its results
     __builtin_amdgcn_sched_barrier(0);

@@ -217,6 +217,23 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* tile, const f32x16& o, 
     op[1] = o1;
 }
 
+// Writes a wave's output accumulator (query l32, columns 32 ct + 16 hh + r)
+// as bf16 straight to its output row (two 16-byte stores per lane; the four
+// waves of a query tile fill the row's 256 bytes between them).
+template <int D>
+__device__ __forceinline__ void store_tile_global(uint16_t* orow, const f32x16& o, int hh, int ct)
+{
+    u16x8 o0, o1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        o0[e] = f32_to_bf16_bits(o[e]);
+        o1[e] = f32_to_bf16_bits(o[8 + e]);
+    }
+    u16x8* op = reinterpret_cast<u16x8*>(orow + 32 * ct + 16 * hh);
+    op[0] = o0;
+    op[1] = o1;
+}
+
 // Workgroups per XCD group: the NKT query tiles of 8 consecutive units.
 __host__ __device__ inline int step_grid(int units, int nkt) { return (units + 7) / 8 * 8 * nkt; }
 
@@ -575,11 +592,13 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 // w % 4); with D = 64 every wave has one.
 // With the commit, each wave also owns the state tiles (32 ct.., 32 ft..) with
 // ft % 2 == qt: their old values are loaded in the accumulator layout right
-// after staging, and phi(K)^T V is added and the tiles written back before
-// the outputs are staged, so the state stores drain meanwhile.  The step's
-// coalesced state reads complete before the first barrier, each tile's second
-// read precedes its write in the same wave, and every element is written
-// once, by one wave.
+// after the first barrier; once its outputs are stored, the wave adds
+// phi(K)^T V to them and writes the tiles back.  The step's coalesced state
+// reads complete before the second barrier and every state write follows it,
+// each tile's second read precedes its write in the same wave, and every
+// element is written once, by one wave.
+// Each lane stores its outputs straight from the accumulator: it holds 16
+// consecutive value columns of one query row.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -791,10 +810,13 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         for (int rr = 0; rr < 16; ++rr) o[rr] = o[rr] + (opv[0][rr] * c0 + opv[1][rr] * c1);
     }
 
-    // ---- the commit (before the outputs, so that the state stores drain while
-    // the outputs are staged): wave (qt, ct) owns state rows [32 ct, 32 ct + 32)
-    // and the feature tiles ft with ft % 2 == qt, starting from the old tiles
-    // loaded above; it reads only the staged K and V
+    // ---- outputs straight from the accumulator (rows past B_r are not written);
+    // with the commit they drain while the state tiles are updated
+    if (qt * 32 + l32 < Br) store_tile_global<D>(out + (int64_t)(qt * 32 + l32) * rs, o, hh, ct);
+
+    // ---- the commit: wave (qt, ct) owns state rows [32 ct, 32 ct + 32) and the
+    // feature tiles ft with ft % 2 == qt, starting from the old tiles loaded
+    // above; it reads only the staged K and V
     if constexpr (kCommit) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -809,17 +831,6 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         // copy staged before the first barrier)
         if constexpr (kNorm) commit_z<D>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
     }
-    // ---- outputs through LDS (every wave is done with sq after the barrier)
-    __syncthreads();
-    store_tile_lds<D>(sq + qt * 32 * P, o, l32, hh, ct);
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
-        if (row < Br)
-            *reinterpret_cast<u32x4*>(out + (int64_t)row * rs + c8) = *reinterpret_cast<const u32x4*>(sq + row * P + c8);
-    }
-
 }
 
 // ---------------------------------------------------------------------------

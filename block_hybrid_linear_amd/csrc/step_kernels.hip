@@ -580,10 +580,12 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 //    computed by one wave, which also takes the tile's row max and row sum and
 //    writes the tile's probabilities relative to that max (hi + lo bf16, in
 //    its lane order) to LDS.
-// The state loads are issued right after the Q/K/V loads, but only Q, K and V
-// are staged before the first barrier: the logit waves run their softmax while
-// the state (the larger part of the bytes, which arrives last) is still in
-// flight, and every wave stages its share of S^T after that.
+// Without the commit the state loads are issued right after the Q/K/V loads,
+// but only Q, K and V are staged before the first barrier: the logit waves run
+// their softmax while the state is still in flight, and every wave stages its
+// share of S^T after that.  With the commit S^T is staged before the first
+// barrier and the waves without a logit tile do their linear part while the
+// others run the softmax.
 // After the second barrier every wave multiplies V^T by both probability tiles of its
 // query tile into two accumulators and merges them with the two-tile softmax
 // correction: with tile maxima m_j, sums l_j and M = max_j m_j, the weights are
@@ -611,6 +613,10 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     constexpr int CPT = R * CPR / NT;            // 16-byte Q, K, V chunks per thread
     constexpr int SPT = D * D / 4 / NT;          // 16-byte S^T chunks per thread
     static_assert(NC >= 2 && CPT * NT == R * CPR && SPT * NT * 4 == D * D, "even staging split");
+    // the step stages S^T after the softmax (the state loads are still in
+    // flight meanwhile); with the commit, whose old-tile reads follow the
+    // first barrier, staging it before that barrier measured faster
+    constexpr bool kDeferS = !kCommit;
     __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
     __shared__ __attribute__((aligned(16))) uint16_t shi[D * P], slo[D * P];   // S^T = hi + lo
     __shared__ __attribute__((aligned(16))) u16x8 sp[2][2][2][2][kWave];       // [qt][jt][gp][hi, lo][lane]
@@ -665,6 +671,20 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
         *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
     }
+    // S^T into LDS as hi + lo bf16 (waits for this thread's state loads)
+    auto stage_s = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int c4 = tid + u * NT, row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
+            uint32_t h0, h1, l0, l1;
+            split_hi_lo2(f32x2{sc[u][0], sc[u][1]}, h0, l0);
+            split_hi_lo2(f32x2{sc[u][2], sc[u][3]}, h1, l1);
+            *reinterpret_cast<u32x2*>(shi + row * P + col) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
+        }
+    };
+    if constexpr (!kDeferS) stage_s();
     if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
     __syncthreads();
 
@@ -745,18 +765,10 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
                 if (hh == 0) sqz[qt][l32] = qz;
             }
         }
+    } else if constexpr (!kDeferS) {
+        linear();                                 // S^T is staged: waves without a logit tile start
     }
-    // S^T into LDS as hi + lo bf16 (waits for this thread's state loads)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-        const int c4 = tid + u * NT, row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
-        uint32_t h0, h1, l0, l1;
-        split_hi_lo2(f32x2{sc[u][0], sc[u][1]}, h0, l0);
-        split_hi_lo2(f32x2{sc[u][2], sc[u][3]}, h1, l1);
-        *reinterpret_cast<u32x2*>(shi + row * P + col) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
-    }
+    if constexpr (kDeferS) stage_s();
     __syncthreads();
 
     // ---- O^T of each key tile = V^T P_j^T (V^T through the transposing read;
@@ -781,7 +793,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][1][lane]), opv[jt]);
         }
     }
-    linear();
+    if (kDeferS || has_l) linear();
     // keep the softmax statistics' LDS reads (and their wait) between the
     // matrix-core work above and the first use of its results
     __builtin_amdgcn_sched_barrier(0);

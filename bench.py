@@ -338,7 +338,7 @@ def norm_context(dev="cuda", rotate: int = 4) -> dict:
     linear scores, z = sum phi(k) next to S) beside the plain calls: the step
     at the serving shapes (rotating input sets, as in exact_context), the step
     and fused step + commit at the prefill + decode workload's block shape,
-    and its prefill (one head per workgroup) against the plain prefill."""
+    and its prefill against the plain prefill."""
     res = {}
     W = SERVING_STEP
     n, H, d, B = W.n_req, W.heads, W.d, W.blk

@@ -190,7 +190,7 @@ ha_status prefill_impl(const char* fn, const void* k, const void* v, const int64
     a.zpartial = a.partial + prefill_slots(n_req, heads, d) * (size_t)d * (size_t)d;
     a.total_tokens = total_tokens;
     a.chunk = chunk;
-    a.hp = norm ? 1 : ha::prefill_group(d, heads, dtype == HA_BF16);
+    a.hp = ha::prefill_group(d, heads, dtype == HA_BF16);
     a.spu = ha::prefill_spu(d, a.hp, heads / a.hp);
     a.slices = heads / a.hp * a.spu;
     a.n_req = n_req;

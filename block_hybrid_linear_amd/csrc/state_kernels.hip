@@ -448,8 +448,21 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
             for (int u = 0; u < TPW; ++u) {
                 const int t = w4 * TPW + u, ct = t / NT, ft = t % NT;
                 const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(hw * D + ct * 32 + l32, g));
-                const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g));
-                acc[u] = mfma32(as_bf16x8(av), as_bf16x8(relu_bf16x8(bk)), acc[u]);
+                const u16x8 bk = relu_bf16x8(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g)));
+                acc[u] = mfma32(as_bf16x8(av), as_bf16x8(bk), acc[u]);
+                if constexpr (kNorm && HP == 2) {
+                    // head pairs: the z sums from the operand in hand (a second
+                    // read as below does not fit in the registers); every wave
+                    // sums, only the writer waves' sums are stored
+                    if (u < NZ) {
+                        const u32x4 w = __builtin_bit_cast(u32x4, bk);
+                        float s8 = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
+                        zacc[u] += s8;
+                    }
+                }
             }
         }
     };
@@ -500,7 +513,7 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
             if (!cp.live) return;              // uniform
             if constexpr (kMma) {
                 mma_stage(buf);
-                if constexpr (kNorm) {
+                if constexpr (kNorm && HP == 1) {
                     if (zwriter) z_stage(buf);
                 }
                 if (cp.t + T >= cp.t1) {
@@ -652,13 +665,9 @@ static void launch_prefill_slices(const PhiKVArgs& a, dim3 grid, hipStream_t str
     case 32: prefill_slices_bf16_mfma<32, 1, kNorm><<<grid, prefill_threads<32, 1>(), 0, stream>>>(a); break;
     case 64: prefill_slices_bf16_mfma<64, 1, kNorm><<<grid, prefill_threads<64, 1>(), 0, stream>>>(a); break;
     default:
-        // (the normalised variant runs one head per workgroup: its z sums do
-        // not fit next to the head pair's 128 accumulator registers per wave)
-        if constexpr (!kNorm) {
-            if (a.hp == 2) {
-                prefill_slices_bf16_mfma<128, 2, false><<<grid, prefill_threads<128, 2>(), 0, stream>>>(a);
-                break;
-            }
+        if (a.hp == 2) {
+            prefill_slices_bf16_mfma<128, 2, kNorm><<<grid, prefill_threads<128, 2>(), 0, stream>>>(a);
+            break;
         }
         prefill_slices_bf16_mfma<128, 1, kNorm><<<grid, prefill_threads<128, 1>(), 0, stream>>>(a);
         break;

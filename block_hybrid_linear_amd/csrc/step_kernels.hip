@@ -2,7 +2,6 @@
 // (request, head) ("Retrofitting Linear Attention into Diffusion Language
 // Models", paper-daily summary page, section "core formula"; the worked
 // example's "block output = softmax result + phi(Q_2) S_1").
-#include <type_traits>
 #include "device_common.h"
 #include "kernels.h"
 
@@ -681,12 +680,11 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
         *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
     }
-    // S^T chunks [u0, u1) into LDS as hi + lo bf16 (waits for those loads)
-    auto stage_s = [&](auto u0c, auto u1c) {
-        constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
+    // this thread's S^T chunks into LDS as hi + lo bf16 (waits for their loads)
+    auto stage_s = [&]() {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = u0; u < u1; ++u) {
+        for (int u = 0; u < SPT; ++u) {
             const int c4 = s_chunk(u), row = c4 / (D / 4), col = (c4 % (D / 4)) * 4;
             uint32_t h0, h1, l0, l1;
             split_hi_lo2(f32x2{sc[u][0], sc[u][1]}, h0, l0);
@@ -695,15 +693,13 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             *reinterpret_cast<u32x2*>(slo + row * P + col) = u32x2{l0, l1};
         }
     };
-    using I0 = std::integral_constant<int, 0>;
-    using IS = std::integral_constant<int, SPT>;
-    if constexpr (!kDeferS) stage_s(I0{}, IS{});
+    if constexpr (!kDeferS) stage_s();
     if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
     __syncthreads();
 
     // with the commit: this wave's old state tiles (value rows 32 ct + 16 hh + r,
     // features 32 ft + l32 in register r; ft = qt, qt + 2, ..) re-read in the
-    // accumulator layout now (cache hits: the same rows are in flight), so that
+    // accumulator layout now (cache hits: the rows were just read), so that
     // they have arrived when the commit runs after the step
     constexpr int NFT = kCommit ? NC / 2 : 1;
     f32x16 old[NFT];
@@ -719,12 +715,10 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;   // A row -> value column
     const uint16_t* qrow = sq + (qt * 32 + l32) * P + 8 * hh;
     f32x16 o = {};
-    // linear part O^T += S^T phi(Q)^T over k-steps [s0, s1), S^T as hi + lo
-    // bf16 from LDS
-    auto linear = [&](auto s0c, auto s1c) {
-        constexpr int s0 = decltype(s0c)::value, s1 = decltype(s1c)::value;
+    // linear part O^T += S^T phi(Q)^T, S^T as hi + lo bf16 from LDS
+    auto linear = [&]() {
 #pragma unroll
-        for (int s = s0; s < s1; ++s) {
+        for (int s = 0; s < KS; ++s) {
             const u16x8 h8 = *reinterpret_cast<const u16x8*>(shi + cA * P + 16 * s + 8 * hh);
             const u16x8 l8 = *reinterpret_cast<const u16x8*>(slo + cA * P + 16 * s + 8 * hh);
             const bf16x8 pq = as_bf16x8(relu_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)));
@@ -781,9 +775,9 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             }
         }
     } else if constexpr (!kDeferS) {
-        linear(I0{}, std::integral_constant<int, KS>{});   // S^T is staged: waves without a logit tile start
+        linear();                                 // S^T is staged: waves without a logit tile start
     }
-    if constexpr (kDeferS) stage_s(I0{}, IS{});
+    if constexpr (kDeferS) stage_s();
     __syncthreads();
 
     // ---- O^T of each key tile = V^T P_j^T (V^T through the transposing read;
@@ -808,7 +802,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][1][lane]), opv[jt]);
         }
     }
-    if (kDeferS || has_l) linear(I0{}, std::integral_constant<int, KS>{});
+    if (kDeferS || has_l) linear();
     // keep the softmax statistics' LDS reads (and their wait) between the
     // matrix-core work above and the first use of its results
     __builtin_amdgcn_sched_barrier(0);

@@ -64,10 +64,23 @@ struct PhiKVTile {
     static constexpr int NLT = 2 * (T / 8) * CG;        // threads that load a stage, one 8x8 block each
     static_assert(NLT % kWave == 0 && NLT <= NW * kWave, "whole loader waves");
     static constexpr bool kColsFast = D == 128;         // lane mapping, see above
-    typedef uint16_t Lds[2][2][HP * D * PITCH];         // [buf][K^T, V^T]
+    // 32-token stages (four 16-byte token groups per row): rows c and c ^ 4
+    // share a 128-byte line, each in the half that bit 2 of
+    // h = ((c >> 3) ^ c) & 7 selects, with the token group at chunk g ^ h.
+    // Measured with the LDS bank-conflict counter on gfx950, that is
+    // conflict-free both for the staging writes (8 consecutive lanes write
+    // rows 8 apart) and for the operand reads (32 consecutive rows, two token
+    // groups), where the padded, rotated layout below is 2-way conflicted for
+    // each; it also needs no padding.
+    static constexpr bool kPacked = T == 32;
+    typedef uint16_t Lds[2][2][kPacked ? HP * D * T : HP * D * PITCH];   // [buf][K^T, V^T]
     __device__ __forceinline__ static int row(int c) { return kColsFast ? (c & ~15) | ((c + (c >> 4)) & 15) : c; }
     // element offset of token group g (8 tokens) of logical LDS row c
-    __device__ __forceinline__ static int slot(int c, int g) { return row(c) * PITCH + 8 * g; }
+    __device__ __forceinline__ static int slot(int c, int g)
+    {
+        if constexpr (kPacked) return (((c >> 3) << 2) | (c & 3)) * 64 + 8 * (g ^ (((c >> 3) ^ c) & 7));
+        else return row(c) * PITCH + 8 * g;
+    }
 };
 
 // Adds ReLU(K)^T V over rows [0, nrows) of (kb, vb) (rows rs elements apart)
@@ -338,7 +351,7 @@ __device__ __forceinline__ void stage_advance(const PhiKVArgs& a, StageCursor& s
 
 // Prefill tile shapes: one head per workgroup as in the commit (4-wave
 // workgroups, two per compute unit, every wave loading its block of a stage
-// and multiplying its tiles), or a head pair with 32-token stages (80 KB of
+// and multiplying its tiles), or a head pair with 32-token stages (64 KB of
 // LDS, one workgroup per compute unit) and the roles split: four loader waves
 // load, transpose and stage K and V, four compute waves own eight 32 x 32
 // tiles each.  Four waves issuing a compute unit's loads stream faster than

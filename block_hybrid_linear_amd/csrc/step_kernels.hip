@@ -106,14 +106,14 @@ __device__ __forceinline__ void stage_z(float* zl, const float* zg, int tid)
     if (tid < D / 4) reinterpret_cast<f32x4*>(zl)[tid] = reinterpret_cast<const f32x4*>(zg)[tid];
 }
 
-// z += sum over the block's first Br staged key rows (pitch D + 8 bf16, row
+// z += sum over the block's first Br staged key rows (pitch PK bf16, row
 // major) of phi(k): thread f < D owns feature f.
-template <int D>
+template <int D, int PK = D + 8>
 __device__ __forceinline__ void commit_z(float* zg, const uint16_t* sk, int Br, int tid)
 {
     if (tid < D) {
         float acc = 0.f;
-        for (int j = 0; j < Br; ++j) acc += relu(bf16_bits_to_f32(sk[j * (D + 8) + tid]));
+        for (int j = 0; j < Br; ++j) acc += relu(bf16_bits_to_f32(sk[j * PK + tid]));
         zg[tid] += acc;
     }
 }
@@ -359,12 +359,11 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 // 32 ct + 16 hh + r, features 32 ft + l32 in register r of lane (l32, hh)) and
 // gets phi(K)^T V of the block's first Br keys added by the matrix cores.  A is
 // V^T and B is ReLU(K), both through the transposing LDS read of the staged
-// rows (pitch D + 8); keys past Br are zeroed in the V^T operand.
-template <int D, int NKT>
+// rows (pitches PK and PV); keys past Br are zeroed in the V^T operand.
+template <int D, int NKT, int PK = D + 8, int PV = D + 8>
 __device__ __forceinline__ f32x16 commit_tile(f32x16 acc, const uint16_t* sk, const uint16_t* sv, int Br, int ct,
                                               int ft, int lane)
 {
-    constexpr int P = D + 8;
     const int hh = lane / 32, g = lane / 16, jl = lane % 16;
     const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
     const int kcol = 32 * ft + 16 * (g % 2) + 4 * (jl % 4);
@@ -373,10 +372,10 @@ __device__ __forceinline__ f32x16 commit_tile(f32x16 acc, const uint16_t* sk, co
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
             const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-            const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
-            const s16x4 k0 = lds_read_tr4(sk + row0 * P + kcol);
-            const s16x4 k1 = lds_read_tr4(sk + (row0 + 8) * P + kcol);
+            const s16x4 v0 = lds_read_tr4(sv + row0 * PV + vcol);
+            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * PV + vcol);
+            const s16x4 k0 = lds_read_tr4(sk + row0 * PK + kcol);
+            const s16x4 k1 = lds_read_tr4(sk + (row0 + 8) * PK + kcol);
             const int key0 = jt * 32 + 16 * gp + 4 * hh;    // keys key0 + e, key0 + 8 + e
             u16x8 vop, kop;
 #pragma unroll
@@ -610,6 +609,12 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
 #pragma clang fp contract(off)
     constexpr int KS = D / 16, NC = D / 32, NT = 2 * NC * kWave;
     constexpr int R = 64, P = D + 8, CPR = D / 8;
+    // row pitches (bf16) of the staged K and V at D = 128: the transposing
+    // reads of V (and of K in the commit) are bank-conflict-free at D + 32 and
+    // 2-way at D + 24, which keeps the 16-byte row reads of K conflict-free
+    // (D + 8: 4-way for the transposing reads; measured on gfx950 with the LDS
+    // bank-conflict counter)
+    constexpr int PK = D == 128 ? D + 24 : P, PV = D == 128 ? D + 32 : P;
     constexpr int CPT = R * CPR / NT;            // 16-byte Q, K, V chunks per thread
     constexpr int SPT = D * D / 4 / NT;          // 16-byte S^T chunks per thread
     static_assert(NC >= 2 && CPT * NT == R * CPR && SPT * NT * 4 == D * D, "even staging split");
@@ -617,7 +622,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     // flight meanwhile); with the commit, whose old-tile reads follow the
     // first barrier, staging it before that barrier measured faster
     constexpr bool kDeferS = !kCommit;
-    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
+    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * PK], sv[R * PV];
     __shared__ __attribute__((aligned(16))) uint16_t shi[D * P], slo[D * P];   // S^T = hi + lo
     __shared__ __attribute__((aligned(16))) u16x8 sp[2][2][2][2][kWave];       // [qt][jt][gp][hi, lo][lane]
     __shared__ float smax[2][2][32], ssum[2][2][32];                            // [qt][jt][query]
@@ -677,8 +682,8 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     for (int u = 0; u < CPT; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
         *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
-        *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
-        *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
+        *reinterpret_cast<u32x4*>(sk + row * PK + c8) = ck[u];
+        *reinterpret_cast<u32x4*>(sv + row * PV + c8) = cv[u];
     }
     // this thread's S^T chunks into LDS as hi + lo bf16 (waits for their loads)
     auto stage_s = [&]() {
@@ -731,7 +736,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         // holds query l32 and keys 32 jt + 8 (rr / 4) + 4 hh + rr % 4
         const int jt = jt_l;
         f32x16 lt = {};
-        const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
+        const uint16_t* kr = sk + (jt * 32 + l32) * PK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             lt = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
@@ -790,8 +795,8 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
             const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-            const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+            const s16x4 v0 = lds_read_tr4(sv + row0 * PV + vcol);
+            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * PV + vcol);
             u16x8 vop;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -844,13 +849,13 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         for (int f = 0; f < NFT; ++f) {
             const int ft = qt + 2 * f;
             float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
-            const f32x16 acc = commit_tile<D, 2>(old[f], sk, sv, Br, ct, ft, lane);
+            const f32x16 acc = commit_tile<D, 2, PK, PV>(old[f], sk, sv, Br, ct, ft, lane);
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
         }
         // normalised variant: z += sum phi(k) over the block (the step used the
         // copy staged before the first barrier)
-        if constexpr (kNorm) commit_z<D>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
+        if constexpr (kNorm) commit_z<D, PK>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
     }
 }
 

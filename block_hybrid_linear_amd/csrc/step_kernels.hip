@@ -124,7 +124,7 @@ __device__ __forceinline__ void commit_z(float* zg, const uint16_t* sk, int Br, 
 // wave's accumulator (value columns of tile ct, transposed).  Contraction of
 // the scaling and the max subtraction into one fma is switched off so that
 // every kernel that inlines this computes bit-identical probabilities.
-template <int D, int NKT, bool kNorm = false>
+template <int D, int NKT, bool kNorm = false, int PK = D + 8, int PV = D + 8>
 __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint16_t* sk, const uint16_t* sv,
                                                int Br, float sl2, int ct, int lane, float qz = 0.f,
                                                float* beta = nullptr)
@@ -140,7 +140,7 @@ __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint
 #pragma unroll
     for (int jt = 0; jt < NKT; ++jt) {
         f32x16 acc = {};
-        const uint16_t* kr = sk + (jt * 32 + l32) * P + 8 * hh;
+        const uint16_t* kr = sk + (jt * 32 + l32) * PK + 8 * hh;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             acc = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
@@ -181,8 +181,8 @@ __device__ __forceinline__ f32x16 softmax_tile(const uint16_t* qtile, const uint
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
             const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-            const s16x4 v0 = lds_read_tr4(sv + row0 * P + vcol);
-            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * P + vcol);
+            const s16x4 v0 = lds_read_tr4(sv + row0 * PV + vcol);
+            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * PV + vcol);
             u16x8 vop;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -245,11 +245,13 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     constexpr int NT = NC * kWave;          // threads
     constexpr int RK = NKT * 32;            // staged key / value rows
     constexpr int P = D + 8;                // LDS row pitch (bf16)
+    // K and V row pitches at D = 128 (see the head-pair step kernel)
+    constexpr int PK = D == 128 ? D + 24 : P, PV = D == 128 ? D + 32 : P;
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int CQ = 32 * CPR / NT;       // Q chunks per thread
     constexpr int CK = RK * CPR / NT;       // K (and V) chunks per thread
     static_assert(CQ * NT == 32 * CPR && CK * NT == RK * CPR, "even staging split");
-    __shared__ __attribute__((aligned(16))) uint16_t sq[32 * P], sk[RK * P], sv[RK * P];
+    __shared__ __attribute__((aligned(16))) uint16_t sq[32 * P], sk[RK * PK], sv[RK * PV];
     __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];   // normalised variant: the unit's z
 
     // workgroup -> (unit, query tile): the NKT tiles of a unit share b % 8
@@ -305,8 +307,8 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     for (int u = 0; u < CK; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
         if (u < CQ) *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
-        *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
-        *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
+        *reinterpret_cast<u32x4*>(sk + row * PK + c8) = ck[u];
+        *reinterpret_cast<u32x4*>(sv + row * PV + c8) = cv[u];
     }
     if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
     __syncthreads();
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     // ---- softmax part (overlaps the S stream)
     float qz = 0.f, beta = 1.f;
     if constexpr (kNorm) qz = query_dot_z<D>(sq + l32 * P, sz, hh);
-    f32x16 o = softmax_tile<D, NKT, kNorm>(sq, sk, sv, Br, sl2, ct, lane, qz, &beta);
+    f32x16 o = softmax_tile<D, NKT, kNorm, PK, PV>(sq, sk, sv, Br, sl2, ct, lane, qz, &beta);
     f32x16 olin = {};                                   // normalised variant: the linear part apart
     // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16 (fenced so its
     // phi(Q) operand reads are not hoisted into the softmax part, where the
@@ -418,6 +420,8 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     constexpr int NT = NKT * NC * kWave;
     constexpr int R = NKT * 32;             // staged rows of Q, K and V
     constexpr int P = D + 8;
+    // K and V row pitches at D = 128 (see the head-pair step kernel)
+    constexpr int PK = D == 128 ? D + 24 : P, PV = D == 128 ? D + 32 : P;
     constexpr int CPR = D / 8;
     constexpr int CPT = R * CPR / NT;
     // Two query tiles: S^T is staged in LDS (one workgroup per compute unit
@@ -428,7 +432,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     constexpr int PS = D + 4;               // LDS row pitch of the state tile (fp32)
     constexpr int SPT = D * D / 4 / NT;     // 16-byte state chunks per thread
     static_assert(CPT * NT == R * CPR && SPT * NT * 4 == D * D, "even staging split");
-    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * P], sv[R * P];
+    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * PK], sv[R * PV];
     __shared__ __attribute__((aligned(16))) float ss[kStageS ? D * PS : 4];   // the unit's S^T
     __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];          // normalised variant: the unit's z
 
@@ -485,8 +489,8 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     for (int u = 0; u < CPT; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
         *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
-        *reinterpret_cast<u32x4*>(sk + row * P + c8) = ck[u];
-        *reinterpret_cast<u32x4*>(sv + row * P + c8) = cv[u];
+        *reinterpret_cast<u32x4*>(sk + row * PK + c8) = ck[u];
+        *reinterpret_cast<u32x4*>(sv + row * PV + c8) = cv[u];
     }
     if constexpr (kStageS) {
 #pragma unroll
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     // ---- the step, from the old state
     float qz = 0.f, beta = 1.f;
     if constexpr (kNorm) qz = query_dot_z<D>(sq + (qt * 32 + l32) * P, sz, hh);
-    f32x16 o = softmax_tile<D, NKT, kNorm>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane, qz, &beta);
+    f32x16 o = softmax_tile<D, NKT, kNorm, PK, PV>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane, qz, &beta);
     f32x16 olin = {};                                   // normalised variant: the linear part apart
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -558,13 +562,13 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
         }
-        acc = commit_tile<D, NKT>(acc, sk, sv, Br, ct, ft, lane);
+        acc = commit_tile<D, NKT, PK, PV>(acc, sk, sv, Br, ct, ft, lane);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
     }
     // normalised variant: z += sum phi(k) over the block (z was staged before
     // the first barrier, so the step above used the old value)
-    if constexpr (kNorm) commit_z<D>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
+    if constexpr (kNorm) commit_z<D, PK>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
 }
 
 // ---------------------------------------------------------------------------

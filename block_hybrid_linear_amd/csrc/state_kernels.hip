@@ -611,20 +611,30 @@ __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
     const int64_t S = a.plan[a.n_req + 1];
     const int64_t cfirst = a.plan[r], cend = a.plan[r + 1];
     const int64_t piece = (int64_t)hu * a.n_req + r, w0 = (int64_t)hu * a.spu;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    if (cend > cfirst) {
-        for (int64_t w = w0 + cfirst / S; w <= w0 + (cend - 1) / S; ++w)
-            sum += reinterpret_cast<const f32x4*>(a.partial + ((w + piece) * a.hp + sub) * dd)[e4];
-    }
-    reinterpret_cast<f32x4*>(a.state + ((int64_t)slot * a.heads + h) * dd)[e4] = sum;
-    if (a.z && e4 < a.d / 4) {                           // normalised variant: z, the same way
-        f32x4 zs = {0.f, 0.f, 0.f, 0.f};
-        if (cend > cfirst) {
-            for (int64_t w = w0 + cfirst / S; w <= w0 + (cend - 1) / S; ++w)
-                zs += reinterpret_cast<const f32x4*>(a.zpartial + ((w + piece) * a.hp + sub) * a.d)[e4];
+    // slices w0 + cfirst / S .. w0 + (cend - 1) / S hold the head's partials
+    const int64_t wfirst = w0 + (cend > cfirst ? cfirst / S : 0);
+    const int64_t nw = cend > cfirst ? (cend - 1) / S - cfirst / S + 1 : 0;
+    // sum of the n partials at base + (wfirst + i + piece) hp stride, i < n, in
+    // ascending order; loaded four at a time (indices clamped to the last one,
+    // so every load is valid) so that their latencies overlap
+    auto sum_partials = [&](const float* base, int64_t stride) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t i0 = 0; i0 < nw; i0 += 4) {
+            f32x4 p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t w = wfirst + (i0 + j < nw ? i0 + j : nw - 1);
+                p[j] = reinterpret_cast<const f32x4*>(base + ((w + piece) * a.hp + sub) * stride)[e4];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (i0 + j < nw) acc += p[j];
         }
-        reinterpret_cast<f32x4*>(a.z + ((int64_t)slot * a.heads + h) * a.d)[e4] = zs;
-    }
+        return acc;
+    };
+    reinterpret_cast<f32x4*>(a.state + ((int64_t)slot * a.heads + h) * dd)[e4] = sum_partials(a.partial, dd);
+    if (a.z && e4 < a.d / 4)                             // normalised variant: z, the same way
+        reinterpret_cast<f32x4*>(a.z + ((int64_t)slot * a.heads + h) * a.d)[e4] = sum_partials(a.zpartial, a.d);
 }
 
 // ---------------------------------------------------------------------------

@@ -219,7 +219,9 @@ __device__ __forceinline__ void store_tile_lds(uint16_t* tile, const f32x16& o, 
 
 // Writes a wave's output accumulator (query l32, columns 32 ct + 16 hh + r)
 // as bf16 straight to its output row (two 16-byte stores per lane; the four
-// waves of a query tile fill the row's 256 bytes between them).
+// waves of a query tile fill the row's 256 bytes between them).  Non-temporal
+// stores: the workgroup never reads them back, and a step measured 1.6 %
+// faster with them than with ordinary stores.
 template <int D>
 __device__ __forceinline__ void store_tile_global(uint16_t* orow, const f32x16& o, int hh, int ct)
 {
@@ -230,8 +232,8 @@ __device__ __forceinline__ void store_tile_global(uint16_t* orow, const f32x16& 
         o1[e] = f32_to_bf16_bits(o[8 + e]);
     }
     u16x8* op = reinterpret_cast<u16x8*>(orow + 32 * ct + 16 * hh);
-    op[0] = o0;
-    op[1] = o1;
+    __builtin_nontemporal_store(o0, op);
+    __builtin_nontemporal_store(o1, op + 1);
 }
 
 // Workgroups per XCD group: the NKT query tiles of 8 consecutive units.
@@ -855,7 +857,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
             float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
             const f32x16 acc = commit_tile<D, 2, PK, PV>(old[f], sk, sv, Br, ct, ft, lane);
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
+            for (int rr = 0; rr < 16; ++rr) __builtin_nontemporal_store(acc[rr], tile + (int64_t)rr * D);   // not read again here
         }
         // normalised variant: z += sum phi(k) over the block (the step used the
         // copy staged before the first barrier)

@@ -110,7 +110,7 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
         for (int e = 0; e < 8; ++e) {
             const int64_t t = t0 + tg * 8 + e;
             const int64_t tc = t < nrows ? t : nrows - 1;   // unconditional load; zeroed at store
-            x[e] = *reinterpret_cast<const u32x4*>(src + tc * rs);
+            x[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + tc * rs));   // read once
         }
     };
     // zero rows past the range, transpose the 8x8 bf16 block, write 8 rows

@@ -173,7 +173,9 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
 }
 
 // Writes (store = true) or reads (store = false) the tiles of a d x d state
-// that wave w of the WPH waves working on it holds.
+// that wave w of the WPH waves working on it holds.  The writes are
+// non-temporal (the kernel never reads them back; for the prefill's partial
+// states that measured 2.9 % faster, with the reduce's non-temporal reads).
 template <int D, int WPH = PhiKVShape<D>::NW>
 __device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (D / 32) / WPH], bool store, int w)
 {
@@ -187,7 +189,7 @@ __device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (
         for (int rr = 0; rr < 16; ++rr) {
             const int c = ct * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
             float* p = base + (int64_t)c * D + ft * 32 + l32;
-            if (store) *p = acc[u][rr];
+            if (store) __builtin_nontemporal_store(acc[u][rr], p);
             else acc[u][rr] = *p;
         }
     }
@@ -618,7 +620,8 @@ __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
     const int64_t nw = cend > cfirst ? (cend - 1) / S - cfirst / S + 1 : 0;
     // sum of the n partials at base + (wfirst + i + piece) hp stride, i < n, in
     // ascending order; loaded four at a time (indices clamped to the last one,
-    // so every load is valid) so that their latencies overlap
+    // so every load is valid) so that their latencies overlap, non-temporal
+    // (each partial is read once)
     auto sum_partials = [&](const float* base, int64_t stride) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int64_t i0 = 0; i0 < nw; i0 += 4) {
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t w = wfirst + (i0 + j < nw ? i0 + j : nw - 1);
-                p[j] = reinterpret_cast<const f32x4*>(base + ((w + piece) * a.hp + sub) * stride)[e4];
+                p[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + ((w + piece) * a.hp + sub) * stride) + e4);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)

@@ -242,7 +242,6 @@ __host__ __device__ inline int step_grid(int units, int nkt) { return (units + 7
 template <int D, int NKT, bool kNorm>
 __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 {
-    constexpr int KS = D / 16;              // k-steps over the head dimension
     constexpr int NC = D / 32;              // value-column tiles = waves
     constexpr int NT = NC * kWave;          // threads
     constexpr int RK = NKT * 32;            // staged key / value rows
@@ -253,7 +252,14 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     constexpr int CQ = 32 * CPR / NT;       // Q chunks per thread
     constexpr int CK = RK * CPR / NT;       // K (and V) chunks per thread
     static_assert(CQ * NT == 32 * CPR && CK * NT == RK * CPR, "even staging split");
-    __shared__ __attribute__((aligned(16))) uint16_t sq[32 * P], sk[RK * PK], sv[RK * PV];
+    __shared__ __attribute__((aligned(16))) uint16_t sq[32 * P], skv[RK * PK + RK * PV];
+    uint16_t* sk = skv;
+    uint16_t* sv = skv + RK * PK;
+    // after the softmax part, K and V are dead and each wave stages its S^T
+    // tile there, a 32-feature quarter (32 rows x 128 bytes) at a time, at a
+    // row pitch of SQP floats
+    constexpr int SQP = 36, NQ = D / 32;
+    static_assert(NC * 32 * SQP * 4 <= (RK * PK + RK * PV) * 2, "S^T quarters fit in the K/V staging");
     __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];   // normalised variant: the unit's z
 
     // workgroup -> (unit, query tile): the NKT tiles of a unit share b % 8
@@ -283,8 +289,10 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     const float sl2 = a.scale * 1.4426950408889634f;         // logits in log2 units
 
     // ---- global loads: this thread's Q/K/V chunks (read once: non-temporal),
-    // then the wave's S^T tile (ordinary loads: its 32-byte pieces of each
-    // row are served by the caches to the wave's later loads)
+    // then the wave's S^T tile in 128-byte row pieces: load i of quarter qq
+    // gives lane l features 32 qq + 4 (l % 8) .. + 3 of tile row 8 i + l / 8
+    // (coalesced; the operand layout needs 32 bytes of each of 32 rows per
+    // instruction, which the caches served poorly)
     u32x4 cq[CQ], ck[CK], cv[CK];
 #pragma unroll
     for (int u = 0; u < CK; ++u) {
@@ -297,13 +305,13 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
         ck[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
         cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
     }
-    f32x4 sraw[KS][2];
-    const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
+    f32x4 sraw[NQ][4];
+    const float* stile = st + (int64_t)(32 * ct + lane / 8) * D + 4 * (lane % 8);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        sraw[s][0] = srow[4 * s];
-        sraw[s][1] = srow[4 * s + 1];
-    }
+    for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sraw[qq][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(stile + (int64_t)8 * i * D + 32 * qq));
     // keep the scheduler from sinking these loads next to their uses: the
     // whole wave's bytes must be in flight before the first wait
     __builtin_amdgcn_sched_barrier(0);
@@ -322,24 +330,36 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     if constexpr (kNorm) qz = query_dot_z<D>(sq + l32 * P, sz, hh);
     f32x16 o = softmax_tile<D, NKT, kNorm, PK, PV>(sq, sk, sv, Br, sl2, ct, lane, qz, &beta);
     f32x16 olin = {};                                   // normalised variant: the linear part apart
-    // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16 (fenced so its
-    // phi(Q) operand reads are not hoisted into the softmax part, where the
-    // logits already occupy the registers)
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16.  Every wave is
+    // done with K and V after this barrier; then each wave writes a quarter of
+    // its S^T tile to its own part of their LDS and reads its A operands back
+    // (row cA - 32 ct, features 16 s + 8 hh .. + 7): LDS accesses of one wave
+    // complete in order, so no further barrier is needed
+    __syncthreads();
+    float* sbuf = reinterpret_cast<float*>(skv) + ct * 32 * SQP;
+    const int arow = cA - 32 * ct;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const float sv8[8] = {sraw[s][0][0], sraw[s][0][1], sraw[s][0][2], sraw[s][0][3],
-                              sraw[s][1][0], sraw[s][1][1], sraw[s][1][2], sraw[s][1][3]};
-        bf16x8 shi, slo;
-        split_hi_lo(sv8, shi, slo);
-        const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + l32 * P + 16 * s + 8 * hh);
-        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-        if constexpr (kNorm) {
-            olin = mfma32(shi, pq, olin);
-            olin = mfma32(slo, pq, olin);
-        } else {
-            o = mfma32(shi, pq, o);
-            o = mfma32(slo, pq, o);
+    for (int qq = 0; qq < NQ; ++qq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4*>(sbuf + (8 * i + lane / 8) * SQP + 4 * (lane % 8)) = sraw[qq][i];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * qq + s2;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(sbuf + arow * SQP + 16 * s2 + 8 * hh);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(sbuf + arow * SQP + 16 * s2 + 8 * hh + 4);
+            const float sv8[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            bf16x8 shi, slo;
+            split_hi_lo(sv8, shi, slo);
+            const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + l32 * P + 16 * s + 8 * hh);
+            const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
+            if constexpr (kNorm) {
+                olin = mfma32(shi, pq, olin);
+                olin = mfma32(slo, pq, olin);
+            } else {
+                o = mfma32(shi, pq, o);
+                o = mfma32(slo, pq, o);
+            }
         }
     }
     if constexpr (kNorm) {

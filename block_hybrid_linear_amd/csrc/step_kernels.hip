@@ -288,8 +288,10 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     const int last = Br - 1;
     const float sl2 = a.scale * 1.4426950408889634f;         // logits in log2 units
 
-    // ---- global loads: this thread's Q/K/V chunks (read once: non-temporal),
-    // then the wave's S^T tile in 128-byte row pieces: load i of quarter qq
+    // ---- global loads: this thread's Q/K/V chunks, then the wave's S^T tile,
+    // non-temporal where this workgroup is their only reader (with two query
+    // tiles the unit's other workgroup reads K, V and S again, on the same
+    // XCD, from its L2); the S^T tile in 128-byte row pieces: load i of quarter qq
     // gives lane l features 32 qq + 4 (l % 8) .. + 3 of tile row 8 i + l / 8
     // (coalesced; the operand layout needs 32 bytes of each of 32 rows per
     // instruction, which the caches served poorly)
@@ -302,16 +304,20 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
             cq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + (int64_t)(rq < Br ? rq : last) * rs + c8));
         }
         const int64_t off = (int64_t)(row < Br ? row : last) * rs + c8;
-        ck[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
-        cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+        const u32x4* kp = reinterpret_cast<const u32x4*>(k + off);
+        const u32x4* vp = reinterpret_cast<const u32x4*>(v + off);
+        ck[u] = NKT == 1 ? __builtin_nontemporal_load(kp) : *kp;
+        cv[u] = NKT == 1 ? __builtin_nontemporal_load(vp) : *vp;
     }
     f32x4 sraw[NQ][4];
     const float* stile = st + (int64_t)(32 * ct + lane / 8) * D + 4 * (lane % 8);
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sraw[qq][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(stile + (int64_t)8 * i * D + 32 * qq));
+        for (int i = 0; i < 4; ++i) {
+            const f32x4* sp4 = reinterpret_cast<const f32x4*>(stile + (int64_t)8 * i * D + 32 * qq);
+            sraw[qq][i] = NKT == 1 ? __builtin_nontemporal_load(sp4) : *sp4;
+        }
     // keep the scheduler from sinking these loads next to their uses: the
     // whole wave's bytes must be in flight before the first wait
     __builtin_amdgcn_sched_barrier(0);

@@ -382,8 +382,8 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
     for (int u = 0; u < CQ; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
         if (qt * 32 + row < Br)
-            *reinterpret_cast<u32x4*>(out + (int64_t)(qt * 32 + row) * rs + c8) =
-                *reinterpret_cast<const u32x4*>(sq + row * P + c8);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sq + row * P + c8),   // not read here again
+                                        reinterpret_cast<u32x4*>(out + (int64_t)(qt * 32 + row) * rs + c8));
     }
 }
 
@@ -573,7 +573,8 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
     for (int u = 0; u < CPT; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
         if (row < Br)
-            *reinterpret_cast<u32x4*>(out + (int64_t)row * rs + c8) = *reinterpret_cast<const u32x4*>(sq + row * P + c8);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sq + row * P + c8),
+                                        reinterpret_cast<u32x4*>(out + (int64_t)row * rs + c8));
     }
 
     if constexpr (!kCommit) return;

@@ -531,8 +531,9 @@ def main():
         log("[bench] copy calibration: 5 copies of 1 GiB")
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU only "
-              "(every (request, head) unit is independent, see the sharding notes)", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark runs on one GPU "
+              "(every (request, head) unit is independent, so the work shards across GPUs with no "
+              "exchange; only the one-GPU share is measured)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)

@@ -86,6 +86,23 @@ template <> struct Elem<uint16_t> {
 
 __device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }
 
+// In-place prefix sum over part[1..256] by a workgroup of 256 threads, thread
+// t owning part[t + 1] (already written by it): afterwards part[0] = 0 and
+// part[i] is the sum of the first i elements.  Log-step (8 rounds of read,
+// barrier, add) instead of one thread walking the array, whose 256 dependent
+// LDS round trips were most of a plan kernel's time.
+__device__ __forceinline__ void scan256(int64_t* part, int tid)
+{
+    if (tid == 0) part[0] = 0;
+    for (int off = 1; off < 256; off <<= 1) {
+        __syncthreads();
+        const int64_t v = tid >= off ? part[tid + 1 - off] : 0;
+        __syncthreads();
+        part[tid + 1] += v;
+    }
+    __syncthreads();
+}
+
 // Max and sum of x over lane pairs (i, i + 32), returned in both lanes.  The
 // permlane32 swap hands every lane the value of lanes 0-31 and of lanes 32-63
 // in one VALU op (no LDS round trip); both halves add the two operands in the

@@ -247,12 +247,7 @@ __global__ __launch_bounds__(256) void prefill_plan(PhiKVArgs a)
     int64_t s = 0;
     for (int r = r0; r < r1; ++r) s += chunks_of(a, r);
     part[tid + 1] = s;
-    __syncthreads();
-    if (tid == 0) {
-        part[0] = 0;
-        for (int i = 1; i <= 256; ++i) part[i] += part[i - 1];
-    }
-    __syncthreads();
+    scan256(part, tid);
     int64_t run = part[tid];
     for (int r = r0; r < r1; ++r) {
         a.plan[r] = run;

@@ -6,9 +6,9 @@ block length (1..128, the range of every step kernel), ragged valid lengths
 (zero included), an injective slot map into a larger store, the dtype, the
 scale, the prompt lengths (empty ones included) and the prefill chunk.  The
 step, the fused step + commit, the commit and the prefill, plain and
-normalised, are compared with the oracle under the tolerance rule of the
-other parity tests; rows past a request's valid length and slots no request
-names must be left untouched.
+normalised, and the exact comparator are compared with the oracle under the
+tolerance rule of the other parity tests; rows past a request's valid length
+and slots no request names must be left untouched.
 """
 import numpy as np
 import pytest
@@ -174,3 +174,28 @@ def test_random_normalised_calls(case):
     assert np.array_equal(gz[unnamed(c)], z0[unnamed(c)]), "normalised commit touched an unnamed z"
     assert_parity(state_to_oracle(state), S2, c["dtype"], "state after the normalised commit")
     assert_parity(gz, z2, c["dtype"], "z after the normalised commit")
+
+
+@pytest.mark.parametrize("case", CASES[:12])
+def test_random_exact_step(case):
+    """The exact comparator on the same random shapes, over random prefix
+    lengths (empty ones included) and key chunks."""
+    c = draw(case)
+    rng = np.random.default_rng(93000 + case)
+    prefixes = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(1, 2500, size=c["n_req"])]
+    chunk = int(rng.choice([1, 32, 100, 256, 3000]))
+    print(f"case {case}: d={c['d']} H={c['H']} blk={c['blk']} lens={c['lens']} prefixes={prefixes} "
+          f"chunk={chunk} dtype={c['dtype']}", flush=True)
+    q, k, v = block_inputs(c, 60)
+    cu = synth.cu_from_lengths(prefixes)
+    kc, vc = (synth.normal((int(cu[-1]), c["H"], c["d"]), c["seed"] + 70 + t, dtype=c["dtype"]).to(DEV)
+              for t in range(2))
+    lens = torch.tensor(c["lens"], dtype=torch.int32, device=DEV)
+    out = torch.full_like(q, SENTINEL)
+    bh.hybrid_exact_step(q, k, v, kc, vc, cu.to(DEV), out=out, blk_lens=lens, scale=c["scale"], chunk=chunk)
+    torch.cuda.synchronize()
+    ref = oracle.exact_step(q, k, v, kc, vc, cu, blk_lens=c["lens"], scale=c["scale"])
+    mask = rows_mask(lens, c["n_req"], c["blk"])
+    o = to64(out)
+    assert np.all(o[~mask] == SENTINEL), "exact step: rows past B_r were written"
+    assert_parity(o[mask], ref[mask], c["dtype"], "exact step")

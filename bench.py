@@ -194,6 +194,39 @@ class Job:
         return graphs
 
 
+def graph_call_us(job: Job, reps: int = 3) -> dict:
+    """Per-call microseconds of each kind of call as the timed region runs it:
+    the kind's calls of one step (input set 0, in step order) captured as one
+    HIP graph, replayed `reps` times back to back after one warm replay."""
+    side = torch.cuda.Stream()
+    calls = job.prepare(side, 0)
+    res = {}
+    for kind in dict.fromkeys(k for k, _ in calls):
+        fns = [fn for k, fn in calls if k == kind]
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for fn in fns:
+                fn()                                    # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for fn in fns:
+                fn()
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[kind] = a.elapsed_time(b) * 1e3 / (reps * len(fns))
+        del g
+    job.reset()
+    return res
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload's units
 # ---------------------------------------------------------------------------
@@ -616,6 +649,15 @@ def main():
                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOPs": round(tfs, 2),
                          "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 5),
                          "share_of_step": round(avg_ms * len(ts) / args.steps / eager_ms_per_step, 4)}
+    # the same calls as they run in the timed region: each kind's calls of one
+    # step (input set 0, step order) captured as a HIP graph and replayed back
+    # to back; per call = replay time / calls
+    for kind, us in graph_call_us(job, reps=3).items():
+        if kind in kernels:
+            byts = job.cost[kind][0]
+            gbs = byts / (us * 1e-6) / 1e9
+            kernels[kind].update({"graph_us": round(us, 2), "graph_GBps": round(gbs, 1),
+                                  "graph_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
     dom = max(kernels, key=lambda k: kernels[k]["share_of_step"])
     kd = kernels[dom]
     traffic = measured_traffic(dom, wl.name)
@@ -636,7 +678,8 @@ def main():
                    "source_digest": source_digest()},
         "roofline": roofline,
         "timing": {"mode": mode, "eager_ms_per_step": round(eager_ms_per_step, 4),
-                   "kernels_from": "HIP events around each call of the eager steps"},
+                   "kernels_from": "HIP events around each call of the eager steps; graph_* from each "
+                                   "kind's calls of one step replayed back to back in a HIP graph"},
         "kernels": kernels,
     }
     if not args.no_context:

@@ -298,3 +298,16 @@ def test_missing_library_fails_loudly(tmp_path):
             binding.load_library(str(tmp_path / "nope.so"))
         finally:
             binding._lib = binding._lib_saved
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/hybrid_attn.h compiles as C11 (gcc, -Wall -Wextra -Werror) in
+    a program that links libhybrid_attn.so and libamdhip64 with no C++ or
+    torch; the GPU test runs the same program."""
+    import importlib.util
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("c_consumer_build", os.path.join(here, "c_consumer", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    exe = mod.build_consumer(str(tmp_path / "abi_consumer"))
+    assert os.path.getsize(exe) > 0

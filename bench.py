@@ -327,6 +327,41 @@ def time_call(fn, iters: int, warm: int = 2) -> float:
     return a.elapsed_time(b) / iters
 
 
+def commit_context(dev="cuda", rotate: int = 4) -> dict:
+    """hybrid_state_commit alone at the block-loop shapes (32 requests x 32
+    heads, d = 128, B = 32): the calls cycle through `rotate` input sets (K/V
+    and S, ~143 MB each, so not served from the last-level cache), captured
+    as one HIP graph of 40 calls and replayed."""
+    W = BLOCK_LOOP
+    n, H, d, B = W.n_req, W.heads, W.d, W.blk
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    sets = []
+    for r in range(rotate):
+        k, v = (synth.normal((n, B, H, d), synth.seed_of(W.index, 0, 0, t) + 700_000 * r, std=W.std, device=dev)
+                for t in (1, 2))
+        sets.append((k, v, torch.zeros(n, H, d, d, device=dev)))
+    side = torch.cuda.Stream()
+    runs = [bh.prepare_commit(k, v, st, slots, stream=side) for k, v, st in sets]
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in runs:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(40):
+            runs[i % rotate]()
+    ms = time_call(g.replay, iters=5, warm=1) / 40
+    byts, flops = commit_cost(n * H, B, d)
+    del g
+    return {"workload": W.name, "call": "hybrid_state_commit", "n_req": n, "heads": H, "head_dim": d, "block": B,
+            "us": round(ms * 1e3, 2), "alg_bytes": byts, "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}
+
+
 def exact_context(dev="cuda", rotate: int = 4) -> dict:
     """The hybrid step cycles through `rotate` distinct input sets (Q/K/V and
     S, ~201 MB each) so that its inputs come from HBM rather than from the
@@ -687,6 +722,8 @@ def main():
         result["context"] = exact_context()
         log("[bench] context: the normalised variant beside the plain calls")
         result["context"]["norm"] = norm_context()
+        log("[bench] context: the commit alone at the block-loop shapes")
+        result["context"]["commit"] = commit_context()
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(job, args.cpu_budget)

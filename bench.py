@@ -701,7 +701,7 @@ def main():
 
     value = job.tokens * args.steps / (total_ms * 1e-3)
     result = {
-        "metric": "hybrid-attn denoising throughput (tokens/s) + % HBM peak; commit/prefill % MFMA",
+        "metric": "hybrid-attn denoising steps/s (tokens/s) + % HBM peak; commit/prefill % MFMA",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",

@@ -18,6 +18,11 @@ denominator, with z = sum ReLU(k) next to S):
     hybrid_attn_step_norm, hybrid_attn_step_commit_norm,
     hybrid_state_commit_norm, hybrid_state_prefill_norm
 
+the prefill for callers that cannot allocate (its workspace is the library's
+own device scratch):
+
+    hybrid_state_prefill_noalloc
+
 and, for comparison, the exact step the method replaces:
 
     hybrid_exact_step     softmax attention of the active block over its
@@ -28,13 +33,15 @@ PyTorch only provides device memory and streams.
 from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_attn_step_commit,
                       hybrid_attn_step_commit_norm, hybrid_attn_step_norm, hybrid_exact_step,
                       hybrid_exact_step_workspace_bytes, hybrid_state_commit, hybrid_state_commit_norm,
-                      hybrid_state_prefill, hybrid_state_prefill_norm, hybrid_state_prefill_workspace_bytes,
+                      hybrid_state_prefill, hybrid_state_prefill_noalloc, hybrid_state_prefill_norm,
+                      hybrid_state_prefill_workspace_bytes,
                       load_library, prepare_commit, prepare_exact_step, prepare_prefill, prepare_prefill_norm,
                       prepare_step, prepare_step_commit, prepare_step_commit_norm, prepare_step_norm)
 
 __all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_attn_step_commit",
            "hybrid_attn_step_commit_norm", "hybrid_attn_step_norm", "hybrid_exact_step",
            "hybrid_exact_step_workspace_bytes", "hybrid_state_commit", "hybrid_state_commit_norm",
-           "hybrid_state_prefill", "hybrid_state_prefill_norm", "hybrid_state_prefill_workspace_bytes",
+           "hybrid_state_prefill", "hybrid_state_prefill_noalloc", "hybrid_state_prefill_norm",
+           "hybrid_state_prefill_workspace_bytes",
            "load_library", "prepare_commit", "prepare_exact_step", "prepare_prefill", "prepare_prefill_norm",
            "prepare_step", "prepare_step_commit", "prepare_step_commit_norm", "prepare_step_norm"]

@@ -47,6 +47,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 ctypes.c_int, vp]
         lib.hybrid_state_prefill.argtypes = [vp, vp, vp, i64, i64, vp, vp, i32, i32, i32, i32, i32, vp, sz,
                                              ctypes.c_int, vp]
+        lib.hybrid_state_prefill_noalloc.argtypes = [vp, vp, vp, i64, i64, vp, vp, i32, i32, i32, i32, i32,
+                                                     ctypes.c_int, vp]
         lib.hybrid_state_prefill_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32]
         lib.hybrid_state_prefill_workspace_bytes.restype = sz
         lib.hybrid_exact_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, i32, i32, i32, i32, f32, i32, vp, sz,
@@ -61,7 +63,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                   sz, ctypes.c_int, vp]
         for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill, lib.hybrid_exact_step,
                    lib.hybrid_attn_step_commit, lib.hybrid_attn_step_norm, lib.hybrid_attn_step_commit_norm,
-                   lib.hybrid_state_commit_norm, lib.hybrid_state_prefill_norm):
+                   lib.hybrid_state_commit_norm, lib.hybrid_state_prefill_norm, lib.hybrid_state_prefill_noalloc):
             fn.restype = ctypes.c_int
         lib.hybrid_last_error.argtypes = []
         lib.hybrid_last_error.restype = ctypes.c_char_p
@@ -259,6 +261,29 @@ def prepare_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, wor
             _check("hybrid_state_prefill", st)
     run.workspace = ws
     return run
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def hybrid_state_prefill_noalloc(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, stream=None):
+    """hybrid_state_prefill with the library's own device scratch as the
+    workspace: nothing is allocated by the call (for graph capture and
+    callers that cannot allocate).  Calls that overlap on one GPU race on
+    that scratch."""
+    total, H, d = k.shape
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k, v must share shape and dtype")
+    n_req = cu_seqlens.shape[0] - 1
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, d, d):
+        raise ValueError(f"state must be [n_slots, {H}, {d}, {d}]")
+    if slots.shape != (n_req,):
+        raise ValueError("slots must be [n_req]")
+    args = (_dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens, "cu_seqlens", torch.int64), total,
+            0 if max_len is None else max_len, _dev(state, "state", torch.float32), _dev(slots, "slots", torch.int32),
+            n_req, state.shape[0], H, d, chunk, _dtype_code(k))
+    _check("hybrid_state_prefill_noalloc", load_library().hybrid_state_prefill_noalloc(*args, _stream(stream)))
+    return state
 
 
 def hybrid_exact_step_workspace_bytes(n_req, heads, blk, d) -> int:

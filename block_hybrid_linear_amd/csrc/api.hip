@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "../../include/hybrid_attn.h"
@@ -152,10 +153,11 @@ size_t prefill_slots(int32_t n_req, int32_t heads, int32_t d)
     return (size_t)std::max(ha::prefill_base_slices(d), (int)heads) + (size_t)n_req * (size_t)heads;
 }
 
-ha_status prefill_impl(const char* fn, const void* k, const void* v, const int64_t* cu_seqlens,
-                       int64_t total_tokens, int64_t max_len, float* state, float* z, const int32_t* slots,
-                       int32_t n_req, int32_t n_slots, int32_t heads, int32_t d, int32_t chunk, void* workspace,
-                       size_t workspace_bytes, ha_dtype dtype, void* stream, bool norm)
+// Argument checks of the prefill calls that do not involve the workspace.
+ha_status prefill_check(const char* fn, const void* k, const void* v, const int64_t* cu_seqlens,
+                        int64_t total_tokens, int64_t max_len, float* state, float* z, const int32_t* slots,
+                        int32_t n_req, int32_t n_slots, int32_t heads, int32_t d, int32_t chunk, ha_dtype dtype,
+                        bool norm)
 {
     if (n_req < 0) return fail(HA_ERR_INVALID_ARG, "%s: n_req must be >= 0 (got %d)", fn, n_req);
     if (n_slots <= 0) return fail(HA_ERR_INVALID_ARG, "%s: n_slots must be > 0 (got %d)", fn, n_slots);
@@ -173,6 +175,18 @@ ha_status prefill_impl(const char* fn, const void* k, const void* v, const int64
                     norm ? ", z" : "");
     if (total_tokens > 0 && (!k || !v))
         return fail(HA_ERR_INVALID_ARG, "%s: k and v must be non-NULL when total_tokens > 0", fn);
+    return HA_OK;
+}
+
+ha_status prefill_impl(const char* fn, const void* k, const void* v, const int64_t* cu_seqlens,
+                       int64_t total_tokens, int64_t max_len, float* state, float* z, const int32_t* slots,
+                       int32_t n_req, int32_t n_slots, int32_t heads, int32_t d, int32_t chunk, void* workspace,
+                       size_t workspace_bytes, ha_dtype dtype, void* stream, bool norm)
+{
+    if (ha_status st = prefill_check(fn, k, v, cu_seqlens, total_tokens, max_len, state, z, slots, n_req, n_slots,
+                                     heads, d, chunk, dtype, norm);
+        st != HA_OK || n_req == 0)
+        return st;
     const size_t need = hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk);
     if (workspace_bytes < need || !workspace)
         return fail(HA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
@@ -248,6 +262,71 @@ ha_status hybrid_state_prefill(const void* k, const void* v, const int64_t* cu_s
 {
     return prefill_impl("hybrid_state_prefill", k, v, cu_seqlens, total_tokens, max_len, state, nullptr, slots,
                         n_req, n_slots, heads, d, chunk, workspace, workspace_bytes, dtype, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device scratch of the prefill entry point that allocates nothing: one copy
+// of this array per GPU the library runs on, held until the process ends.
+// Host code never uses the array's name as an address (on the host it is only
+// a stand-in); the device address is looked up once per device and kept in
+// g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[HYBRID_ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the device that runs `stream`.
+ha_status scratch_address(const char* fn, void* stream, void** out)
+{
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(HA_ERR_HIP, "%s: cannot find the stream's device: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(HA_ERR_HIP, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return fail(HA_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(HA_ERR_HIP, "%s: hipSetDevice(%d) failed: %s", fn, dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return fail(HA_ERR_HIP, "%s: scratch address on device %d: %s", fn, dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return HA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ha_status hybrid_state_prefill_noalloc(const void* k, const void* v, const int64_t* cu_seqlens,
+                                       int64_t total_tokens, int64_t max_len, float* state,
+                                       const int32_t* slots, int32_t n_req, int32_t n_slots,
+                                       int32_t heads, int32_t d, int32_t chunk, ha_dtype dtype, void* stream)
+{
+    static const char* fn = "hybrid_state_prefill_noalloc";
+    if (ha_status st = prefill_check(fn, k, v, cu_seqlens, total_tokens, max_len, state, nullptr, slots, n_req,
+                                     n_slots, heads, d, chunk, dtype, false);
+        st != HA_OK || n_req == 0)
+        return st;
+    const size_t need = hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk);
+    if (need > HYBRID_ATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(HA_ERR_INVALID_ARG, "%s: needs %zu bytes of scratch, more than the %zu available", fn, need,
+                    (size_t)HYBRID_ATTN_NOALLOC_SCRATCH_BYTES);
+    if (ha_status st = check_aligned(fn, {k, v, state}, nullptr); st != HA_OK) return st;
+    void* ws = nullptr;
+    if (ha_status st = scratch_address(fn, stream, &ws); st != HA_OK) return st;
+    return prefill_impl(fn, k, v, cu_seqlens, total_tokens, max_len, state, nullptr, slots, n_req, n_slots, heads,
+                        d, chunk, ws, HYBRID_ATTN_NOALLOC_SCRATCH_BYTES, dtype, stream, false);
 }
 
 ha_status hybrid_attn_step_norm(const void* q, const void* k, const void* v, const float* state, const float* z,

@@ -187,6 +187,36 @@ size_t hybrid_state_prefill_workspace_bytes(int32_t n_req, int32_t heads,
                                             int64_t max_len, int32_t chunk);
 
 /*
+ * hybrid_state_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call, the same kernels and the same results, but the
+ * workspace is the library's own scratch array instead of an argument.  The
+ * array is a fixed HYBRID_ATTN_NOALLOC_SCRATCH_BYTES (128 MiB) of device
+ * memory, one copy per GPU the library runs on, held until the process ends;
+ * its address on a device is looked up once, on the first call on that
+ * device (the device of `stream`; NULL = the current device).  The call
+ * itself allocates and frees nothing.
+ *
+ * A call whose hybrid_state_prefill_workspace_bytes(...) exceeds the maximum
+ * returns HA_ERR_INVALID_ARG before anything is enqueued (e.g. d = 128 and
+ * 32 heads allow up to 47 requests per call).  HA_ERR_HIP: the scratch
+ * array's address could not be obtained on the stream's device.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race and
+ * give undefined results; order them on one stream.  The array keeps the last
+ * call's contents, which no call depends on.
+ */
+#define HYBRID_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+ha_status hybrid_state_prefill_noalloc(const void* k, const void* v,
+                                       const int64_t* cu_seqlens,
+                                       int64_t total_tokens, int64_t max_len,
+                                       float* state, const int32_t* slots,
+                                       int32_t n_req, int32_t n_slots,
+                                       int32_t heads, int32_t d, int32_t chunk,
+                                       ha_dtype dtype, void* stream);
+
+/*
  * Normalised variant.  The pages say the retrofit largely follows LoLCATs
  * (summary page, sections "problem solving" and "method"; abstract page) and
  * print no formula for a normaliser; the reading implemented here is that

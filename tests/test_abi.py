@@ -33,7 +33,8 @@ def test_header_declares_the_calls():
     for n in ("hybrid_attn_step", "hybrid_attn_step_commit", "hybrid_state_commit", "hybrid_state_prefill",
               "hybrid_state_prefill_workspace_bytes", "hybrid_exact_step", "hybrid_exact_step_workspace_bytes",
               "hybrid_attn_step_norm", "hybrid_attn_step_commit_norm", "hybrid_state_commit_norm",
-              "hybrid_state_prefill_norm", "hybrid_last_error", "hybrid_abi_version"):
+              "hybrid_state_prefill_norm", "hybrid_state_prefill_noalloc", "hybrid_last_error",
+              "hybrid_abi_version"):
         assert n in names
 
 
@@ -248,6 +249,22 @@ def test_empty_batches_are_noops(lib):
     assert commit_norm(lib, k=None, v=None, state=None, z=None, slots=None, n_req=0) == binding.HA_OK
     assert prefill_norm(lib, k=None, v=None, cu=None, state=None, z=None, slots=None, ws=None, ws_bytes=0,
                         n_req=0) == binding.HA_OK
+
+
+def test_noalloc_prefill_validates_before_touching_the_gpu(lib):
+    """The prefill that uses the library's own scratch: an empty batch is a
+    no-op, and a call needing more than the scratch's fixed maximum, or with
+    bad arguments, is rejected before any device call."""
+    fn = lib.hybrid_state_prefill_noalloc
+    assert fn(None, None, None, 0, 0, None, None, 0, 2, 4, 64, 256, binding.HA_BF16, None) == binding.HA_OK
+    need = bh.hybrid_state_prefill_workspace_bytes(64, 32, 128, 10 ** 6, 0, 256)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert fn(1, 1, 1, 10 ** 6, 0, 1, 1, 64, 64, 32, 128, 256, binding.HA_BF16, None) == binding.HA_ERR_INVALID_ARG
+    assert "scratch" in lib.hybrid_last_error().decode()
+    assert bh.hybrid_state_prefill_workspace_bytes(47, 32, 128, 10 ** 6, 0, 256) <= binding.NOALLOC_SCRATCH_BYTES
+    assert fn(1, 1, 1, 100, 0, 1, 1, 2, 2, 4, 48, 256, binding.HA_BF16, None) == binding.HA_ERR_UNSUPPORTED
+    assert fn(1, 1, 1, 100, 0, 1, 1, 2, 2, 4, 64, 0, binding.HA_BF16, None) == binding.HA_ERR_INVALID_ARG
+    assert fn(1, 1, 1, 100, 0, 1, 1, -1, 2, 4, 64, 256, binding.HA_BF16, None) == binding.HA_ERR_INVALID_ARG
 
 
 def test_prefill_workspace_size(lib):

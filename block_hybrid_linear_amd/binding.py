@@ -8,6 +8,7 @@ library is an error.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -18,7 +19,8 @@ from .build import LIB as LIB_PATH
 
 HA_OK, HA_ERR_INVALID_ARG, HA_ERR_UNSUPPORTED, HA_ERR_HIP = 0, 1, 2, 3
 HA_F32, HA_BF16 = 0, 1
-MAX_BLK = 128
+MAX_BLK = 256
+EXACT_MAX_BLK = 128
 
 _lock = threading.Lock()
 _lib = None
@@ -107,6 +109,17 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on_stream(stream):
+    """Context in which tensors are allocated (and filled) on ``stream``, so
+    that the caching allocator orders their reuse, and any fill kernel, with
+    the library's kernels on that stream; a no-op for the current stream."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream))
+    return torch.cuda.stream(stream)
+
+
 def abi_version() -> int:
     return load_library().hybrid_abi_version()
 
@@ -134,7 +147,8 @@ def hybrid_attn_step(q, k, v, state, slots, out=None, blk_lens=None, scale=None,
     """out = Softmax(scale Q K^T) V + ReLU(Q) S[slots] for q/k/v [n_req, blk, H, d];
     state [n_slots, H, d, d] fp32 (each d x d block stores S transposed)."""
     if out is None:
-        out = torch.zeros_like(q)
+        with _on_stream(stream):
+            out = torch.zeros_like(q)
     args = _step_args(q, k, v, state, slots, out, blk_lens, scale)
     _check("hybrid_attn_step", load_library().hybrid_attn_step(*args, _stream(stream)))
     return out
@@ -159,7 +173,8 @@ def hybrid_attn_step_commit(q, k, v, state, slots, out=None, blk_lens=None, scal
     state[slots] += ReLU(K)^T V in the same pass: the last denoising step of a
     block fused with its commit.  Requests must use distinct slots."""
     if out is None:
-        out = torch.zeros_like(q)
+        with _on_stream(stream):
+            out = torch.zeros_like(q)
     args = _step_args(q, k, v, state, slots, out, blk_lens, scale)
     _check("hybrid_attn_step_commit", load_library().hybrid_attn_step_commit(*args, _stream(stream)))
     return out
@@ -214,7 +229,7 @@ def hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len,
     return int(load_library().hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk))
 
 
-def _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace):
+def _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace, stream=None):
     total, H, d = k.shape
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k, v must share shape and dtype")
@@ -227,7 +242,8 @@ def _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace):
         max_len = 0     # only an upper bound; the kernels do not need it
     need = hybrid_state_prefill_workspace_bytes(n_req, H, d, total, max_len, chunk)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+        with _on_stream(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
     args = (_dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens, "cu_seqlens", torch.int64), total, max_len,
             _dev(state, "state", torch.float32), _dev(slots, "slots", torch.int32), n_req, state.shape[0], H, d,
             chunk, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _dtype_code(k))
@@ -243,7 +259,7 @@ def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256
     ``workspace`` is a GPU uint8 tensor of at least
     ``hybrid_state_prefill_workspace_bytes`` bytes; if omitted one is
     allocated through torch."""
-    args, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    args, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace, stream)
     _check("hybrid_state_prefill", load_library().hybrid_state_prefill(*args, _stream(stream)))
     return state
 
@@ -251,7 +267,7 @@ def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256
 def prepare_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256, workspace=None, stream=None):
     """Prepared form of hybrid_state_prefill (see prepare_step); keeps its
     workspace alive."""
-    args, ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    args, ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace, stream)
     args = args + (_stream(stream),)
     fn = load_library().hybrid_state_prefill
 
@@ -290,7 +306,7 @@ def hybrid_exact_step_workspace_bytes(n_req, heads, blk, d) -> int:
     return int(load_library().hybrid_exact_step_workspace_bytes(n_req, heads, blk, d))
 
 
-def _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace):
+def _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace, stream=None):
     n_req, blk, H, d = q.shape
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape and dtype")
@@ -308,7 +324,8 @@ def _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chun
         scale = d ** -0.5
     need = hybrid_exact_step_workspace_bytes(n_req, H, blk, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        with _on_stream(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     total = k_cache.shape[0]
     args = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache") if total else None,
             _dev(v_cache, "v_cache") if total else None, _dev(cu_prefix, "cu_prefix", torch.int64), total,
@@ -324,8 +341,9 @@ def hybrid_exact_step(q, k, v, k_cache, v_cache, cu_prefix, out=None, blk_lens=N
     [total_prefix, H, d], request r owns rows cu_prefix[r]..cu_prefix[r+1]-1)
     and itself -- the step block-hybrid attention replaces."""
     if out is None:
-        out = torch.zeros_like(q)
-    args, _ws = _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace)
+        with _on_stream(stream):
+            out = torch.zeros_like(q)
+    args, _ws = _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace, stream)
     _check("hybrid_exact_step", load_library().hybrid_exact_step(*args, _stream(stream)))
     return out
 
@@ -334,7 +352,7 @@ def prepare_exact_step(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens=None,
                        workspace=None, stream=None):
     """Prepared form of hybrid_exact_step (see prepare_step); keeps its
     workspace alive."""
-    args, ws = _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace)
+    args, ws = _exact_args(q, k, v, k_cache, v_cache, cu_prefix, out, blk_lens, scale, chunk, workspace, stream)
     args = args + (_stream(stream),)
     fn = load_library().hybrid_exact_step
 
@@ -366,7 +384,8 @@ def hybrid_attn_step_norm(q, k, v, state, z, slots, out=None, blk_lens=None, sca
     """out_i = (sum_j exp(l_ij) v_j + ReLU(q_i) S) / (sum_j exp(l_ij) + ReLU(q_i).z)
     for q/k/v [n_req, blk, H, d], state [n_slots, H, d, d], z [n_slots, H, d]."""
     if out is None:
-        out = torch.zeros_like(q)
+        with _on_stream(stream):
+            out = torch.zeros_like(q)
     args = _with_z(_step_args(q, k, v, state, slots, out, blk_lens, scale), z, state, 4)
     _check("hybrid_attn_step_norm", load_library().hybrid_attn_step_norm(*args, _stream(stream)))
     return out
@@ -388,7 +407,8 @@ def hybrid_attn_step_commit_norm(q, k, v, state, z, slots, out=None, blk_lens=No
     """hybrid_attn_step_norm from the current S and z, then S += ReLU(K)^T V and
     z += sum_j ReLU(k_j) in the same call.  Requests must use distinct slots."""
     if out is None:
-        out = torch.zeros_like(q)
+        with _on_stream(stream):
+            out = torch.zeros_like(q)
     args = _with_z(_step_args(q, k, v, state, slots, out, blk_lens, scale), z, state, 4)
     _check("hybrid_attn_step_commit_norm", load_library().hybrid_attn_step_commit_norm(*args, _stream(stream)))
     return out
@@ -417,7 +437,7 @@ def hybrid_state_prefill_norm(k, v, cu_seqlens, state, z, slots, max_len=None, c
                               stream=None):
     """state[slots[r]] and z[slots[r]] overwritten by the sums over prompt r of
     ReLU(k_t)^T v_t and ReLU(k_t) (see hybrid_state_prefill)."""
-    args, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    args, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace, stream)
     args = _with_z(args, z, state, 6)
     _check("hybrid_state_prefill_norm", load_library().hybrid_state_prefill_norm(*args, _stream(stream)))
     return state
@@ -425,7 +445,7 @@ def hybrid_state_prefill_norm(k, v, cu_seqlens, state, z, slots, max_len=None, c
 
 def prepare_prefill_norm(k, v, cu_seqlens, state, z, slots, max_len=None, chunk=256, workspace=None, stream=None):
     """Prepared form of hybrid_state_prefill_norm; keeps its workspace alive."""
-    args, ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace)
+    args, ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace, stream)
     args = _with_z(args, z, state, 6) + (_stream(stream),)
     fn = load_library().hybrid_state_prefill_norm
 

@@ -54,13 +54,13 @@ size_t plan_bytes(int32_t n_req) { return ((size_t)(n_req + 2) * sizeof(int64_t)
 
 // Checks shared by step and commit.  Returns HA_OK or the failure status.
 ha_status check_block_call(const char* fn, int32_t n_req, int32_t n_slots, int32_t heads,
-                           int32_t blk, int32_t d, ha_dtype dtype)
+                           int32_t blk, int32_t d, ha_dtype dtype, int32_t max_blk = HYBRID_ATTN_MAX_BLK)
 {
     if (n_req < 0) return fail(HA_ERR_INVALID_ARG, "%s: n_req must be >= 0 (got %d)", fn, n_req);
     if (n_slots <= 0) return fail(HA_ERR_INVALID_ARG, "%s: n_slots must be > 0 (got %d)", fn, n_slots);
     if (heads <= 0) return fail(HA_ERR_INVALID_ARG, "%s: heads must be > 0 (got %d)", fn, heads);
-    if (blk <= 0 || blk > HYBRID_ATTN_MAX_BLK)
-        return fail(HA_ERR_INVALID_ARG, "%s: blk must be in [1, %d] (got %d)", fn, HYBRID_ATTN_MAX_BLK, blk);
+    if (blk <= 0 || blk > max_blk)
+        return fail(HA_ERR_INVALID_ARG, "%s: blk must be in [1, %d] (got %d)", fn, max_blk, blk);
     if (!known_dtype(dtype)) return fail(HA_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
     if (!supported_d(d)) return fail(HA_ERR_UNSUPPORTED, "%s: head dim d=%d not in {16, 32, 64, 128}", fn, d);
     if ((int64_t)n_req * heads > 0x7fffffffLL)
@@ -369,7 +369,7 @@ ha_status hybrid_state_prefill_norm(const void* k, const void* v, const int64_t*
 
 size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads, int32_t blk, int32_t d)
 {
-    if (n_req <= 0 || heads <= 0 || blk <= 0 || blk > HYBRID_ATTN_MAX_BLK || d <= 0) return 0;
+    if (n_req <= 0 || heads <= 0 || blk <= 0 || blk > HYBRID_ATTN_EXACT_MAX_BLK || d <= 0) return 0;
     return plan_bytes(n_req) + ((size_t)ha::exact_slices(d, blk) + (size_t)n_req * (size_t)heads) *
                                    (size_t)ha::exact_slot_floats(blk, d) * sizeof(float);
 }
@@ -381,7 +381,7 @@ ha_status hybrid_exact_step(const void* q, const void* k, const void* v, const v
                             size_t workspace_bytes, ha_dtype dtype, void* stream)
 {
     static const char* fn = "hybrid_exact_step";
-    ha_status st = check_block_call(fn, n_req, 1, heads, blk, d, dtype);
+    ha_status st = check_block_call(fn, n_req, 1, heads, blk, d, dtype, HYBRID_ATTN_EXACT_MAX_BLK);
     if (st != HA_OK) return st;
     if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
     if (chunk <= 0) return fail(HA_ERR_INVALID_ARG, "%s: chunk must be > 0 (got %d)", fn, chunk);

@@ -902,28 +902,45 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
 }
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core step for long blocks (64 < blk <= 128): same layout as
-// above, but the keys are visited one 32-key tile at a time with an online
-// softmax (running max and sum, accumulator rescaled when the max grows), so
-// the register footprint does not grow with the block; the S^T stream is
-// issued after the key loop and added to the normalised softmax output.
+// bf16 matrix-core step for long blocks (65..256 rows): one workgroup per
+// (request, head, 32-query tile) with D/32 waves (wave ct owns value columns
+// [32 ct, 32 ct + 32)), numbered so that the tiles of a unit share an XCD.
+// The keys and values stream through LDS in 32-row stages (double-buffered;
+// the next stage's loads are issued before the current one is used), and
+// each wave runs an online softmax over them (running max and sum per query,
+// accumulator rescaled when the max grows), so nothing grows with the block.
+// The wave's S^T operands are loaded straight from the state after the last
+// key stage (32 contiguous bytes of row cA per lane and k-step) and added to
+// the normalised softmax output.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(4 * D / 32 * kWave) void step_bf16_mfma_long(StepArgs a)
+template <int D, bool kNorm>
+__global__ __launch_bounds__(D / 32 * kWave) void step_long_bf16(StepArgs a)
 {
-    constexpr int KS = D / 16;
-    constexpr int NC = D / 32;
-    const int unit = blockIdx.x;
+#pragma clang fp contract(off)
+    constexpr int NC = D / 32, KS = D / 16, NT = NC * kWave;
+    constexpr int P = D + 8;
+    constexpr int PK = D == 128 ? D + 24 : P, PV = D == 128 ? D + 32 : P;
+    constexpr int CPR = D / 8, C = 32 * CPR / NT;   // 16-byte chunks per thread of a 32-row tile
+    static_assert(C * NT == 32 * CPR, "even staging split");
+    __shared__ __attribute__((aligned(16))) uint16_t sq[32 * P], sk[2][32 * PK], sv[2][32 * PV];
+    __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];
+
+    const int b = blockIdx.x;
+    const int nqt = (a.blk + 31) / 32;     // query tiles per unit in the grid
+    const int qt = (b / 8) % nqt;
+    const int unit = b / (8 * nqt) * 8 + b % 8;
+    if (unit >= a.n_req * a.heads) return;
     const int r = unit / a.heads, h = unit % a.heads;
     int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
     Br = Br > a.blk ? a.blk : Br;
     const int slot = a.slots[r];
-    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;
+    if (Br <= qt * 32 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
 
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    const int qt = w / NC, ct = w % NC;
-    if (qt * 32 >= Br) return;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int ct = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l32 = lane % 32, hh = lane / 32;
+    const int g = lane / 16, jl = lane % 16;
     const int64_t rs = (int64_t)a.heads * D;
     const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + base;
@@ -931,49 +948,64 @@ __global__ __launch_bounds__(4 * D / 32 * kWave) void step_bf16_mfma_long(StepAr
     const uint16_t* v = static_cast<const uint16_t*>(a.v) + base;
     uint16_t* out = static_cast<uint16_t*>(a.out) + base;
     const float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
-    const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
-    const int nkt = (Br + 31) / 32;
     const int last = Br - 1;
+    const int nkt = (Br + 31) / 32;
     const float sl2 = a.scale * 1.4426950408889634f;
 
-    const int i = qt * 32 + l32;
-    const uint16_t* qrow = q + (int64_t)(i < Br ? i : last) * rs + 8 * hh;
-    u16x8 qv[KS];
+    auto load_tile = [&](const uint16_t* src, int row0, u32x4 (&x)[C]) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qv[s] = *reinterpret_cast<const u16x8*>(qrow + 16 * s);
+        for (int u = 0; u < C; ++u) {
+            const int t = tid + u * NT, row = row0 + t / CPR, c8 = (t % CPR) * 8;
+            x[u] = *reinterpret_cast<const u32x4*>(src + (int64_t)(row < Br ? row : last) * rs + c8);
+        }
+    };
+    auto store_tile = [&](uint16_t* dst, int pitch, const u32x4 (&x)[C]) {
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
+            const int t = tid + u * NT;
+            *reinterpret_cast<u32x4*>(dst + (t / CPR) * pitch + (t % CPR) * 8) = x[u];
+        }
+    };
 
+    u32x4 xq[C], xk[C], xv[C];
+    load_tile(q, qt * 32, xq);
+    load_tile(k, 0, xk);
+    load_tile(v, 0, xv);
+    store_tile(sq, P, xq);
+    if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
+
+    const uint16_t* qrow = sq + l32 * P + 8 * hh;
+    // V^T operand column of lane i in 16-lane group g (matching cA below)
+    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
     float m = -INFINITY, l = 0.f;
     f32x16 o = {};
 #pragma unroll 1
     for (int jt = 0; jt < nkt; ++jt) {
-        const int j = jt * 32 + l32;
-        const uint16_t* krow = k + (int64_t)(j < Br ? j : last) * rs + 8 * hh;
-        u16x8 kv[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kv[s] = *reinterpret_cast<const u16x8*>(krow + 16 * s);
-        u16x8 vop[2];
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int jj = jt * 32 + 16 * gp + 8 * (e / 4) + 4 * hh + e % 4;
-                vop[gp][e] = v[(int64_t)(jj < Br ? jj : last) * rs + cA];
-            }
+        const int buf = jt & 1;
+        store_tile(sk[buf], PK, xk);
+        store_tile(sv[buf], PV, xv);
+        __syncthreads();     // also: every wave finished with this buffer two stages ago
+        if (jt + 1 < nkt) {
+            load_tile(k, (jt + 1) * 32, xk);
+            load_tile(v, (jt + 1) * 32, xv);
         }
         f32x16 lt = {};
+        const uint16_t* kr = sk[buf] + l32 * PK + 8 * hh;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) lt = mfma32(as_bf16x8(kv[s]), as_bf16x8(qv[s]), lt);
+        for (int s = 0; s < KS; ++s)
+            lt = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
+                        as_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)), lt);
         float mt = -INFINITY;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-            const int jr = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-            const float x = jr < Br ? lt[rr] * sl2 : -INFINITY;
+            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+            const float x = j < Br ? lt[rr] * sl2 : -INFINITY;
             lt[rr] = x;
             mt = fmaxf(mt, x);
         }
         mt = half_pair_max(mt);
-        const float mn = fmaxf(m, mt);
-        const float corr = __builtin_amdgcn_exp2f(m - mn);     // 0 on the first tile
+        const float mn = fmaxf(m, mt);                        // finite: key jt*32 is valid
+        const float corr = __builtin_amdgcn_exp2f(m - mn);    // 0 on the first tile
         float ls = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -988,52 +1020,68 @@ __global__ __launch_bounds__(4 * D / 32 * kWave) void step_bf16_mfma_long(StepAr
         for (int rr = 0; rr < 16; ++rr) o[rr] *= corr;
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-            float p[8];
+            const int row0 = 16 * gp + 4 * hh + jl / 4;
+            const s16x4 v0 = lds_read_tr4(sv[buf] + row0 * PV + vcol);
+            const s16x4 v1 = lds_read_tr4(sv[buf] + (row0 + 8) * PV + vcol);
+            u16x8 vop;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = lt[8 * gp + e];
+            for (int e = 0; e < 4; ++e) {
+                vop[e] = static_cast<uint16_t>(v0[e]);
+                vop[4 + e] = static_cast<uint16_t>(v1[e]);
+            }
+            float pp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pp[e] = lt[8 * gp + e];
             bf16x8 phi, plo;
-            split_hi_lo(p, phi, plo);
-            o = mfma32(as_bf16x8(vop[gp]), phi, o);
-            o = mfma32(as_bf16x8(vop[gp]), plo, o);
+            split_hi_lo(pp, phi, plo);
+            o = mfma32(as_bf16x8(vop), phi, o);
+            o = mfma32(as_bf16x8(vop), plo, o);
         }
     }
-    const float inv = __builtin_amdgcn_rcpf(l);
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) o[rr] *= inv;
-
+    // the S^T operands (row cA, features 16 s + 8 hh .. + 7), then the
+    // normalisation of the softmax part and the linear part
+    const int cA = 32 * ct + 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
     const f32x4* srow = reinterpret_cast<const f32x4*>(st + (int64_t)cA * D + 8 * hh);
+    f32x4 sr[KS][2];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const f32x4 s0 = srow[4 * s], s1 = srow[4 * s + 1];
-        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-        bf16x8 shi, slo;
-        split_hi_lo(sv, shi, slo);
-        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv[s]));
-        o = mfma32(shi, pq, o);
-        o = mfma32(slo, pq, o);
+        sr[s][0] = srow[4 * s];
+        sr[s][1] = srow[4 * s + 1];
     }
-    if (i < Br) {
-        u16x8 o0, o1;
+    float alpha, beta = 1.f;
+    if constexpr (kNorm) norm_weights(m, l, query_dot_z<D>(sq + l32 * P, sz, hh), alpha, beta);
+    else alpha = __builtin_amdgcn_rcpf(l);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o0[e] = f32_to_bf16_bits(o[e]);
-            o1[e] = f32_to_bf16_bits(o[8 + e]);
-        }
-        u16x8* op = reinterpret_cast<u16x8*>(out + (int64_t)i * rs + 32 * ct + 16 * hh);
-        op[0] = o0;
-        op[1] = o1;
+    for (int rr = 0; rr < 16; ++rr) o[rr] *= alpha;
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const float sv8[8] = {sr[s][0][0], sr[s][0][1], sr[s][0][2], sr[s][0][3],
+                              sr[s][1][0], sr[s][1][1], sr[s][1][2], sr[s][1][3]};
+        bf16x8 shi, slo;
+        split_hi_lo(sv8, shi, slo);
+        const bf16x8 pq = as_bf16x8(relu_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)));
+        acc = mfma32(shi, pq, acc);
+        acc = mfma32(slo, pq, acc);
     }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) o[rr] = kNorm ? fmaf(beta, acc[rr], o[rr]) : o[rr] + acc[rr];
+    const int i = qt * 32 + l32;
+    if (i < Br) store_tile_global<D>(out + (int64_t)i * rs, o, hh, ct);
 }
 
 // ---------------------------------------------------------------------------
 // Plain fp32-arithmetic step for fp32 inputs (any supported d) and for bf16
-// with d = 16.  One workgroup of 256 threads per (request, head); the B_r x B_r
-// softmax matrix lives in LDS, everything else is read from global memory.
+// with d = 16.  One workgroup of 256 threads per (request, head); query rows
+// are taken in groups of up to 32 whose softmax rows live in LDS, everything
+// else is read from global memory.
 // ---------------------------------------------------------------------------
+constexpr int kGenericRows = 32;
+
 template <typename T>
 __global__ __launch_bounds__(256) void step_generic(StepArgs a)
 {
-    extern __shared__ float P[];                  // [Br][Br], then the linear term's weight per row
+    extern __shared__ float P[];                  // [rows][Br], then the linear term's weight per row
     const int D = a.d;
     const int unit = blockIdx.x;
     const int r = unit / a.heads, h = unit % a.heads;
@@ -1048,55 +1096,62 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
     const T* v = static_cast<const T*>(a.v) + base;
     T* out = static_cast<T*>(a.out) + base;
     const float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
-
-    for (int idx = threadIdx.x; idx < Br * Br; idx += blockDim.x) {
-        const int i = idx / Br, j = idx % Br;
-        float dot = 0.f;
-        for (int c = 0; c < D; ++c) dot = fmaf(Elem<T>::load(q, i * rs + c), Elem<T>::load(k, j * rs + c), dot);
-        P[idx] = a.scale * dot;
-    }
-    __syncthreads();
-    float* wlin = P + Br * Br;
     const float* zg = a.z ? a.z + ((int64_t)slot * a.heads + h) * D : nullptr;
-    for (int i = threadIdx.x; i < Br; i += blockDim.x) {
-        float m = -INFINITY;
-        for (int j = 0; j < Br; ++j) m = fmaxf(m, P[i * Br + j]);
-        float sum = 0.f;
-        for (int j = 0; j < Br; ++j) {
-            const float p = expf(P[i * Br + j] - m);
-            P[i * Br + j] = p;
-            sum += p;
+    const int rows = a.blk < kGenericRows ? a.blk : kGenericRows;   // as allocated: rows x (blk + 1) floats
+    float* wlin = P + rows * Br;
+
+    for (int i0 = 0; i0 < Br; i0 += rows) {
+        const int nr = Br - i0 < rows ? Br - i0 : rows;
+        __syncthreads();                          // the previous group's rows are consumed
+        for (int idx = threadIdx.x; idx < nr * Br; idx += blockDim.x) {
+            const int i = i0 + idx / Br, j = idx % Br;
+            float dot = 0.f;
+            for (int c = 0; c < D; ++c) dot = fmaf(Elem<T>::load(q, i * rs + c), Elem<T>::load(k, j * rs + c), dot);
+            P[idx] = a.scale * dot;
         }
-        float inv = 1.f / sum, beta = 1.f;
-        if (zg) {
-            // normalised variant: one denominator, both sides divided by e^c,
-            // c = max(m, ln(phi(q).z)) (kept above -69, where e^-c stays finite)
-            float qz = 0.f;
-            for (int f = 0; f < D; ++f) qz = fmaf(relu(Elem<T>::load(q, i * rs + f)), zg[f], qz);
-            float c = m;
-            if (qz > 0.f) c = fmaxf(c, logf(qz));
-            c = fmaxf(c, -69.f);
-            const float ws = expf(m - c), wl = expf(-c);
-            const float den = fmaf(ws, sum, wl * qz);
-            inv = ws / den;
-            beta = wl / den;
+        __syncthreads();
+        for (int ii = threadIdx.x; ii < nr; ii += blockDim.x) {
+            const int i = i0 + ii;
+            float* row = P + ii * Br;
+            float m = -INFINITY;
+            for (int j = 0; j < Br; ++j) m = fmaxf(m, row[j]);
+            float sum = 0.f;
+            for (int j = 0; j < Br; ++j) {
+                const float p = expf(row[j] - m);
+                row[j] = p;
+                sum += p;
+            }
+            float inv = 1.f / sum, beta = 1.f;
+            if (zg) {
+                // normalised variant: one denominator, both sides divided by e^c,
+                // c = max(m, ln(phi(q).z)) (kept above -69, where e^-c stays finite)
+                float qz = 0.f;
+                for (int f = 0; f < D; ++f) qz = fmaf(relu(Elem<T>::load(q, i * rs + f)), zg[f], qz);
+                float c = m;
+                if (qz > 0.f) c = fmaxf(c, logf(qz));
+                c = fmaxf(c, -69.f);
+                const float ws = expf(m - c), wl = expf(-c);
+                const float den = fmaf(ws, sum, wl * qz);
+                inv = ws / den;
+                beta = wl / den;
+            }
+            for (int j = 0; j < Br; ++j) row[j] *= inv;
+            wlin[ii] = beta;
         }
-        for (int j = 0; j < Br; ++j) P[i * Br + j] *= inv;
-        wlin[i] = beta;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < Br * D; idx += blockDim.x) {
-        const int i = idx / D, c = idx % D;
-        float acc = 0.f;
-        for (int j = 0; j < Br; ++j) acc = fmaf(P[i * Br + j], Elem<T>::load(v, j * rs + c), acc);
-        if (zg) {
-            float lin = 0.f;
-            for (int f = 0; f < D; ++f) lin = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], lin);
-            acc = fmaf(wlin[i], lin, acc);
-        } else {
-            for (int f = 0; f < D; ++f) acc = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], acc);
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+            const int ii = idx / D, i = i0 + ii, c = idx % D;
+            float acc = 0.f;
+            for (int j = 0; j < Br; ++j) acc = fmaf(P[ii * Br + j], Elem<T>::load(v, j * rs + c), acc);
+            if (zg) {
+                float lin = 0.f;
+                for (int f = 0; f < D; ++f) lin = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], lin);
+                acc = fmaf(wlin[ii], lin, acc);
+            } else {
+                for (int f = 0; f < D; ++f) acc = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], acc);
+            }
+            Elem<T>::store(out, i * rs + c, acc);
         }
-        Elem<T>::store(out, i * rs + c, acc);
     }
 }
 
@@ -1109,12 +1164,12 @@ static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
         if constexpr (D >= 64) step_pair_bf16_mfma<D, false, false><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
         else step_bf16_mfma<D, 2, false><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
     }
-    else step_bf16_mfma_long<D><<<units, 4 * D / 32 * kWave, 0, stream>>>(a);
+    else step_long_bf16<D, false><<<step_grid(units, (a.blk + 31) / 32), D / 32 * kWave, 0, stream>>>(a);
 }
 
-// Normalised variant on the matrix cores: blocks of up to 32 rows (d >= 32)
-// and 33..64 rows (d = 64, 128); returns false for the shapes that take the
-// fp32 kernel.
+// Normalised variant on the matrix cores: blocks of up to 32 rows (d >= 32),
+// 33..64 rows (d = 64, 128) and 65..256 rows; returns false for the shapes
+// that take the fp32 kernel.
 template <int D>
 static bool launch_step_norm_d(const StepArgs& a, int units, hipStream_t stream)
 {
@@ -1122,11 +1177,13 @@ static bool launch_step_norm_d(const StepArgs& a, int units, hipStream_t stream)
         step_bf16_mfma<D, 1, true><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
         return true;
     }
+    if (a.blk > 64) {
+        step_long_bf16<D, true><<<step_grid(units, (a.blk + 31) / 32), D / 32 * kWave, 0, stream>>>(a);
+        return true;
+    }
     if constexpr (D >= 64) {
-        if (a.blk <= 64) {
-            step_pair_bf16_mfma<D, false, true><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
-            return true;
-        }
+        step_pair_bf16_mfma<D, false, true><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
+        return true;
     }
     return false;
 }
@@ -1235,7 +1292,8 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream)
         }
     }
     if (!done) {
-        const size_t lds = sizeof(float) * ((size_t)a.blk * a.blk + a.blk);
+        const int rows = a.blk < kGenericRows ? a.blk : kGenericRows;
+        const size_t lds = sizeof(float) * ((size_t)rows * a.blk + rows);
         if (a.dtype_bf16) step_generic<uint16_t><<<units, 256, lds, stream>>>(a);
         else step_generic<float><<<units, 256, lds, stream>>>(a);
     }

@@ -37,8 +37,11 @@
  *                               holds S TRANSPOSED: state[s][h][c][f] =
  *                               S[f][c] = sum phi(k)_f v_c, i.e. row = value
  *                               dimension c, column = feature f of phi(k).
- *                               (This orientation lets the step kernel read S
- *                               straight into matrix-core operands.)
+ *                               The step contracts S over f; stored this way,
+ *                               the 8 consecutive f a lane's matrix-core
+ *                               operand holds are 32 contiguous bytes (one
+ *                               16-byte load pair, or one 16-byte LDS read),
+ *                               where row = f would make them a column.
  *   slots         int32[n_req]  request r uses state slot slots[r].
  *   blk_lens      int32[n_req]  valid rows B_r of request r's block, or NULL
  *                               for "all blk rows valid".
@@ -52,7 +55,8 @@
  * Errors: a non-OK status other than HA_ERR_HIP is returned BEFORE anything
  * is enqueued, so outputs and the state are untouched.  hybrid_last_error()
  * gives a message for the calling thread's last non-OK status.
- *   HA_ERR_INVALID_ARG  NULL pointer, negative or zero size, blk > 128,
+ *   HA_ERR_INVALID_ARG  NULL pointer, negative or zero size, blk > 256
+ *                       (blk > 128 for hybrid_exact_step),
  *                       non-finite scale, chunk < 1, workspace too small,
  *                       a q/k/v/out/state/cache pointer not 16-byte aligned
  *                       or a workspace not 256-byte aligned (allocations
@@ -75,8 +79,9 @@
 extern "C" {
 #endif
 
-#define HYBRID_ATTN_ABI_VERSION 1
-#define HYBRID_ATTN_MAX_BLK 128
+#define HYBRID_ATTN_ABI_VERSION 2
+#define HYBRID_ATTN_MAX_BLK 256         /* rows of an active block */
+#define HYBRID_ATTN_EXACT_MAX_BLK 128   /* rows of an active block in hybrid_exact_step */
 
 typedef enum {
     HA_OK = 0,
@@ -154,6 +159,8 @@ ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v,
  * total_tokens: HOST scalar, rows of k and v.
  * max_len: HOST scalar >= 0, an upper bound of the prompt lengths; the
  *   current kernels do not need it (kept for ABI stability).
+ * slots: the requests of one call must use distinct slots (two requests
+ *   writing one slot in the same call would leave either one's sum there).
  * chunk: prompts are cut into chunks of `chunk` tokens; for every head (or
  *   pair of adjacent heads) the chunks of all prompts form one list, which is
  *   split into the same number of equal ranges, one per workgroup, so the

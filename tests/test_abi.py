@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert bh.abi_version() == 1
+    assert bh.abi_version() == 2
 
 
 N = None
@@ -110,7 +110,7 @@ def last(lib):
     (dict(d=48), binding.HA_ERR_UNSUPPORTED, "head dim"),
     (dict(dtype=7), binding.HA_ERR_UNSUPPORTED, "dtype"),
     (dict(blk=0), binding.HA_ERR_INVALID_ARG, "blk"),
-    (dict(blk=129), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(blk=257), binding.HA_ERR_INVALID_ARG, "blk"),
     (dict(n_req=-1), binding.HA_ERR_INVALID_ARG, "n_req"),
     (dict(n_slots=0), binding.HA_ERR_INVALID_ARG, "n_slots"),
     (dict(heads=0), binding.HA_ERR_INVALID_ARG, "heads"),
@@ -182,7 +182,7 @@ def test_exact_rejects(lib, kw, status, msg):
 
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(d=100), binding.HA_ERR_UNSUPPORTED, "head dim"),
-    (dict(blk=129), binding.HA_ERR_INVALID_ARG, "blk"),
+    (dict(blk=257), binding.HA_ERR_INVALID_ARG, "blk"),
     (dict(scale=float("nan")), binding.HA_ERR_INVALID_ARG, "scale"),
     (dict(z=None), binding.HA_ERR_INVALID_ARG, "z"),
     (dict(state=None), binding.HA_ERR_INVALID_ARG, "non-NULL"),

@@ -64,9 +64,9 @@ def test_worked_example_generation():
 # --------------------------------------------------------------------------
 
 STEP_CASES = [  # (d, blk)
-    (128, 32), (128, 64), (128, 100), (128, 128), (128, 1), (128, 5),
-    (64, 32), (64, 33), (64, 128), (32, 17), (32, 64), (32, 96),
-    (16, 4), (16, 32), (16, 128),
+    (128, 32), (128, 64), (128, 100), (128, 128), (128, 1), (128, 5), (128, 200), (128, 256),
+    (64, 32), (64, 33), (64, 128), (64, 256), (32, 17), (32, 64), (32, 96), (32, 200),
+    (16, 4), (16, 32), (16, 128), (16, 256),
 ]
 
 
@@ -130,7 +130,8 @@ def _bf16_ulp(x):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (64, 64), (32, 64), (128, 1), (64, 20)])
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (64, 64), (32, 64), (128, 1), (64, 20), (128, 200),
+                                   (64, 256)])
 def test_step_outputs_correctly_rounded(d, blk, fused):
     """The matrix-core step keeps fp32 S and P at ~16 significand bits (hi + lo
     bf16), so every bf16 output is within one bf16 ulp of the exact value plus
@@ -169,8 +170,9 @@ def test_step_deterministic():
 # Commit
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (128, 100), (128, 128), (128, 1),
-                                   (64, 32), (64, 77), (32, 32), (32, 5), (16, 4), (16, 64)])
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (128, 100), (128, 128), (128, 1), (128, 200), (128, 256),
+                                   (64, 32), (64, 77), (64, 256), (32, 32), (32, 5), (32, 200), (16, 4), (16, 64),
+                                   (16, 256)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_commit_parity(d, blk, dtype):
     n_req, H, n_slots = 3, 4, 5
@@ -197,8 +199,8 @@ def test_commit_parity(d, blk, dtype):
 # Fused last step + commit
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (128, 33), (128, 1), (128, 100), (64, 64), (64, 17),
-                                   (32, 64), (32, 5), (16, 32)])
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (128, 33), (128, 1), (128, 100), (128, 200), (128, 256),
+                                   (64, 64), (64, 17), (64, 256), (32, 64), (32, 5), (32, 256), (16, 32)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_step_commit_parity(d, blk, dtype):
     """Output from the old state and the updated state both match the oracle's
@@ -368,18 +370,41 @@ def test_prefill_equals_commits_and_resume_bitwise():
     assert torch.equal(resumed, sc)
 
 
-def test_state_roundtrip_layout():
-    """The library's transposed state layout: a state built by the oracle and
-    stored transposed gives the oracle's step output."""
+def test_state_layout_row_is_value_dim():
+    """The state block is stored as S^T: state[slot][h][c][f] = S[f][c] (row =
+    value dim, column = feature of phi(k)).  Committing one token whose key
+    has a single positive feature f0 writes v into column f0 and nothing else;
+    a step with V = 0 then gives relu(q) @ S, which differs from relu(q) @ S^T
+    by far more than the tolerance (so the other orientation fails here)."""
     n_req, blk, H, d = 2, 32, 2, 128
+    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
+    k1 = torch.full((n_req, 1, H, d), -1.0, dtype=torch.bfloat16, device=DEV)
+    f0 = [5, 77]
+    for r in range(n_req):
+        k1[r, 0, :, f0[r]] = 1.0
+    v1 = gen((n_req, 1, H, d), 12490, torch.bfloat16)
+    state = torch.zeros(n_req, H, d, d, device=DEV)
+    bh.hybrid_state_commit(k1, v1, state, slots)
+    torch.cuda.synchronize()
+    St = to64(state)
+    for r in range(n_req):
+        expect = np.zeros((H, d, d))
+        expect[:, :, f0[r]] = to64(v1)[r, 0]
+        assert np.array_equal(St[r], expect), f"request {r}: commit did not write column f0 = v"
+
     q, k, v = (gen((n_req, blk, H, d), 12500 + t, torch.bfloat16) for t in range(3))
     S = np.random.default_rng(5).standard_normal((n_req, H, d, d)) * 10
+    S[..., :d // 2, d // 2:] += 40.0                      # far from symmetric
     state = state_from_oracle(S)
-    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
     out = bh.hybrid_attn_step(q, k, torch.zeros_like(v), state, slots)
     torch.cuda.synchronize()
-    ref = oracle.step(q, k, np.zeros(v.shape), state_to_oracle(state), scale=d ** -0.5)
-    assert_parity(out, ref, torch.bfloat16, "layout")
+    Sd = state_to_oracle(state)                           # S[f][c]
+    qr = np.maximum(to64(q), 0.0)
+    ref = np.einsum("rihf,rhfc->rihc", qr, Sd)
+    ref_t = np.einsum("rihf,rhcf->rihc", qr, Sd)
+    assert_parity(out, ref, torch.bfloat16, "relu(q) @ S")
+    assert np.abs(ref - ref_t).max() > 10 * 2e-2 * np.abs(ref).max()
+    assert_parity(out, oracle.step(q, k, np.zeros(v.shape), Sd, scale=d ** -0.5), torch.bfloat16, "oracle")
 
 
 def test_prefill_many_ragged_requests():
@@ -501,3 +526,27 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(out_g, out_e), f"replay {rep}: output differs"
         assert torch.equal(s_g, s_e), f"replay {rep}: state differs"
         _ = (q.float() * 2).sum().item()   # unrelated eager work between replays
+
+
+def test_side_stream_calls():
+    """Calls enqueued on a stream other than the current one, with the output
+    and the prefill workspace allocated by the binding: they are allocated
+    and filled on that stream, so the results match the oracle."""
+    n_req, blk, H, d = 2, 48, 4, 128
+    q, k, v = (gen((n_req, blk, H, d), 19000 + t, torch.bfloat16) for t in range(3))
+    lens = [900, 2500]
+    cu = synth.cu_from_lengths(lens)
+    kp = gen((int(cu[-1]), H, d), 19010, torch.bfloat16)
+    vp = gen((int(cu[-1]), H, d), 19011, torch.bfloat16)
+    slots = torch.arange(n_req, dtype=torch.int32, device=DEV)
+    state = torch.full((n_req, H, d, d), 7.0, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda._sleep(50_000_000)                 # keep the current stream busy meanwhile
+    bh.hybrid_state_prefill(kp, vp, cu.to(DEV), state, slots, stream=side)
+    out = bh.hybrid_attn_step(q, k, v, state, slots, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    S = oracle.prefill(kp, vp, cu)
+    assert_parity(state_to_oracle(state), S, torch.bfloat16, "prefill on a side stream")
+    assert_parity(out, oracle.step(q, k, v, S, scale=d ** -0.5), torch.bfloat16, "step on a side stream")

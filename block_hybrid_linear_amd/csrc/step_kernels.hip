@@ -657,6 +657,10 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     // flight meanwhile); with the commit, whose old-tile reads follow the
     // first barrier, staging it before that barrier measured faster
     constexpr bool kDeferS = !kCommit;
+    // the step also loads V last and stages it after the linear part, so the
+    // products with the state run while V arrives and only the products with
+    // P follow the last byte
+    constexpr bool kLateV = !kCommit;
     __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * PK], sv[R * PV];
     __shared__ __attribute__((aligned(16))) uint16_t shi[D * P], slo[D * P];   // S^T = hi + lo
     __shared__ __attribute__((aligned(16))) u16x8 sp[2][2][2][2][kWave];       // [qt][jt][gp][hi, lo][lane]
@@ -691,15 +695,19 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     const float sl2 = a.scale * 1.4426950408889634f;
 
     // ---- loads: Q, K, V rows (rows past B_r repeat row B_r - 1; non-temporal,
-    // read once: 9.6 % faster than ordinary loads), then S^T
+    // read once: 9.6 % faster than ordinary loads), then S^T (and then V with
+    // kLateV)
     u32x4 cq[CPT], ck[CPT], cv[CPT];
+    auto v_off = [&](int u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        return (int64_t)(row < Br ? row : last) * rs + c8;
+    };
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
-        const int64_t off = (int64_t)(row < Br ? row : last) * rs + c8;
+        const int64_t off = v_off(u);
         cq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + off));
         ck[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
-        cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+        if constexpr (!kLateV) cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
     }
     // 16-byte chunk u of this thread's S^T share: the step reads whole rows
     // (chunk tid + u NT); with the commit, feature blocks (chunks 2b, 2b + 1
@@ -719,14 +727,26 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         if constexpr (kDeferS) sc[u] = __builtin_nontemporal_load(sp4);
         else sc[u] = *sp4;
     }
+    if constexpr (kLateV) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u)
+            cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + v_off(u)));
+    }
     __builtin_amdgcn_sched_barrier(0);
+    auto stage_v = [&]() {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+            *reinterpret_cast<u32x4*>(sv + row * PV + c8) = cv[u];
+        }
+    };
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
         const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
         *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
         *reinterpret_cast<u32x4*>(sk + row * PK + c8) = ck[u];
-        *reinterpret_cast<u32x4*>(sv + row * PV + c8) = cv[u];
     }
+    if constexpr (!kLateV) stage_v();
     // this thread's S^T chunks into LDS as hi + lo bf16 (waits for their loads)
     auto stage_s = [&]() {
         __builtin_amdgcn_sched_barrier(0);
@@ -832,24 +852,34 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
     // + 4 (q / 2) + i % 4, q = i / 4, matching cA)
     const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
     f32x16 opv[2] = {{}, {}};
+    auto pv = [&]() {
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
+        for (int jt = 0; jt < 2; ++jt) {
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-            const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
-            const s16x4 v0 = lds_read_tr4(sv + row0 * PV + vcol);
-            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * PV + vcol);
-            u16x8 vop;
+            for (int gp = 0; gp < 2; ++gp) {
+                const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+                const s16x4 v0 = lds_read_tr4(sv + row0 * PV + vcol);
+                const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * PV + vcol);
+                u16x8 vop;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vop[e] = static_cast<uint16_t>(v0[e]);
-                vop[4 + e] = static_cast<uint16_t>(v1[e]);
+                for (int e = 0; e < 4; ++e) {
+                    vop[e] = static_cast<uint16_t>(v0[e]);
+                    vop[4 + e] = static_cast<uint16_t>(v1[e]);
+                }
+                opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][0][lane]), opv[jt]);
+                opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][1][lane]), opv[jt]);
             }
-            opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][0][lane]), opv[jt]);
-            opv[jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][1][lane]), opv[jt]);
         }
+    };
+    if constexpr (kLateV) {
+        linear();
+        stage_v();                                   // waits for V, the last loads
+        __syncthreads();
+        pv();
+    } else {
+        pv();
+        if (kDeferS || has_l) linear();
     }
-    if (kDeferS || has_l) linear();
     // keep the softmax statistics' LDS reads (and their wait) between the
     // matrix-core work above and the first use of its results
     __builtin_amdgcn_sched_barrier(0);
@@ -897,6 +927,261 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         }
         // normalised variant: z += sum phi(k) over the block (the step used the
         // copy staged before the first barrier)
+        if constexpr (kNorm) commit_z<D, PK>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Step for blocks of 33..64 rows at D = 128, optionally followed by the
+// commit, with one wave per SIMD: one workgroup per (request, head) of four
+// waves; wave ct produces the outputs of BOTH query tiles for value columns
+// [32 ct, 32 ct + 32), so the S^T rows it needs (rows [32 ct, 32 ct + 32),
+// 16 KB) are needed by no other wave.  It loads them in 128-byte row pieces
+// behind its share of Q, K and V and consumes them a 32-feature quarter at a
+// time as they arrive, through a private LDS buffer (fp32; no barrier), so
+// that after the last byte only one quarter's multiplications and the stores
+// remain.  Wave ct also computes the logit tile (query tile ct / 2, key tile
+// ct % 2) and publishes its probabilities and row statistics in LDS, as the
+// head-pair kernel does; the V^T operands of the products with P are read
+// once for both query tiles.
+// With the commit, the wave owns state rows [32 ct, 32 ct + 32) (every
+// feature tile): the old tile of feature tile qq is taken from the quarter
+// buffer in the accumulator layout, phi(K)^T V is added after the outputs
+// are stored, and the rows that only this wave read are written back.
+// ---------------------------------------------------------------------------
+template <bool kCommit, bool kNorm>
+__global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
+{
+#pragma clang fp contract(off)
+    constexpr int D = 128, NC = D / 32, NT = NC * kWave;
+    constexpr int R = 64, P = D + 8, CPR = D / 8;
+    constexpr int PK = D + 24, PV = D + 32;        // as in the head-pair kernel
+    constexpr int CPT = R * CPR / NT;              // 16-byte Q, K, V chunks per thread
+    constexpr int SQP = 36;                        // fp32 row pitch of a quarter buffer
+    static_assert(CPT * NT == R * CPR, "even staging split");
+    __shared__ __attribute__((aligned(16))) uint16_t sq[R * P], sk[R * PK], sv[R * PV];
+    __shared__ __attribute__((aligned(16))) u16x8 sp[2][2][2][2][kWave];       // [qt][jt][gp][hi, lo][lane]
+    __shared__ float smax[2][2][32], ssum[2][2][32];                            // [qt][jt][query]
+    __shared__ __attribute__((aligned(16))) float sz[kNorm ? D : 4];
+    __shared__ float sqz[kNorm ? 2 : 1][32];
+    __shared__ __attribute__((aligned(16))) float sbuf[NC][32 * SQP];          // each wave's quarter buffer
+
+    const int unit = blockIdx.x;
+    const int r = unit / a.heads, h = unit % a.heads;
+    int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
+    Br = Br > a.blk ? a.blk : Br;
+    const int slot = a.slots[r];
+    if (Br <= 0 || slot < 0 || slot >= a.n_slots) return;   // uniform per workgroup
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int ct = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int l32 = lane % 32, hh = lane / 32;
+    const int g = lane / 16, jl = lane % 16;
+    const int64_t rs = (int64_t)a.heads * D;
+    const int64_t base = ((int64_t)r * a.blk * a.heads + h) * D;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + base;
+    const uint16_t* k = static_cast<const uint16_t*>(a.k) + base;
+    const uint16_t* v = static_cast<const uint16_t*>(a.v) + base;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + base;
+    const int64_t soff = ((int64_t)slot * a.heads + h) * D * D;
+    const float* st = (kCommit ? a.state_rw : a.state) + soff;
+    const int last = Br - 1;
+    const float sl2 = a.scale * 1.4426950408889634f;
+
+    // ---- loads: Q, K, V rows (rows past B_r repeat row B_r - 1), then the
+    // wave's S^T rows: load i of quarter qq gives lane l features
+    // 32 qq + 4 (l % 8) .. + 3 of row 32 ct + 8 i + l / 8.  All non-temporal:
+    // each byte is read once (the commit takes its old values from LDS).
+    u32x4 cq[CPT], ck[CPT], cv[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        const int64_t off = (int64_t)(row < Br ? row : last) * rs + c8;
+        cq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + off));
+        ck[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+        cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+    }
+    f32x4 sraw[4][4];
+    const float* stile = st + (int64_t)(32 * ct + lane / 8) * D + 4 * (lane % 8);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sraw[qq][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(stile + (int64_t)8 * i * D + 32 * qq));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int t = tid + u * NT, row = t / CPR, c8 = (t % CPR) * 8;
+        *reinterpret_cast<u32x4*>(sq + row * P + c8) = cq[u];
+        *reinterpret_cast<u32x4*>(sk + row * PK + c8) = ck[u];
+        *reinterpret_cast<u32x4*>(sv + row * PV + c8) = cv[u];
+    }
+    if constexpr (kNorm) stage_z<D>(sz, a.z + ((int64_t)slot * a.heads + h) * D, tid);
+    __syncthreads();
+
+    // ---- logit tile (query tile ct / 2, key tile ct % 2): probabilities
+    // relative to the tile's row max (hi + lo, lane order), max and sum
+    {
+        const int qt = ct / 2, jt = ct % 2;
+        const uint16_t* qrow = sq + (qt * 32 + l32) * P + 8 * hh;
+        f32x16 lt = {};
+        const uint16_t* kr = sk + (jt * 32 + l32) * PK + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            lt = mfma32(as_bf16x8(*reinterpret_cast<const u16x8*>(kr + 16 * s)),
+                        as_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)), lt);
+        float m = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int j = jt * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
+            const float x = j < Br ? lt[rr] * sl2 : -INFINITY;
+            lt[rr] = x;
+            m = fmaxf(m, x);
+        }
+        m = half_pair_max(m);
+        const float mb = m == -INFINITY ? 0.f : m;   // key tile 1 has no valid key when B_r <= 32
+        float sum = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(lt[rr] - mb);
+            lt[rr] = p;
+            sum += p;
+        }
+        sum = half_pair_sum(sum);
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            float pp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pp[e] = lt[8 * gp + e];
+            bf16x8 phi, plo;
+            split_hi_lo(pp, phi, plo);
+            sp[qt][jt][gp][0][lane] = __builtin_bit_cast(u16x8, phi);
+            sp[qt][jt][gp][1][lane] = __builtin_bit_cast(u16x8, plo);
+        }
+        if (hh == 0) {
+            smax[qt][jt][l32] = m;
+            ssum[qt][jt][l32] = sum;
+        }
+        if constexpr (kNorm) {
+            if (jt == 0) {
+                const float qz = query_dot_z<D>(qrow - 8 * hh, sz, hh);
+                if (hh == 0) sqz[qt][l32] = qz;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- O^T = V^T P^T for both query tiles (V^T through the transposing read,
+    // once per key step for both), merged with the two-tile softmax weights
+    const int vcol = 32 * ct + 16 * ((jl % 4) % 2) + 8 * (g % 2) + 4 * ((jl % 4) / 2);
+    f32x16 opv[2][2] = {{{}, {}}, {{}, {}}};
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            const int row0 = jt * 32 + 16 * gp + 4 * hh + jl / 4;
+            const s16x4 v0 = lds_read_tr4(sv + row0 * PV + vcol);
+            const s16x4 v1 = lds_read_tr4(sv + (row0 + 8) * PV + vcol);
+            u16x8 vop;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vop[e] = static_cast<uint16_t>(v0[e]);
+                vop[4 + e] = static_cast<uint16_t>(v1[e]);
+            }
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                opv[qt][jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][0][lane]), opv[qt][jt]);
+                opv[qt][jt] = mfma32(as_bf16x8(vop), as_bf16x8(sp[qt][jt][gp][1][lane]), opv[qt][jt]);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float beta[2] = {1.f, 1.f}, c0[2], c1[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const float m0 = smax[qt][0][l32], m1 = smax[qt][1][l32];
+        const float mx = fmaxf(m0, m1);              // finite: key 0 is valid
+        if constexpr (kNorm) {
+            const float qz = sqz[qt][l32];
+            float c = mx;
+            if (qz > 0.f) c = fmaxf(c, __builtin_amdgcn_logf(qz));
+            c = fmaxf(c, -100.f);
+            const float e0 = __builtin_amdgcn_exp2f(m0 - c), e1 = __builtin_amdgcn_exp2f(m1 - c);
+            const float wl = __builtin_amdgcn_exp2f(-c);
+            const float inv = __builtin_amdgcn_rcpf(ssum[qt][0][l32] * e0 + ssum[qt][1][l32] * e1 + wl * qz);
+            c0[qt] = e0 * inv;
+            c1[qt] = e1 * inv;
+            beta[qt] = wl * inv;
+        } else {
+            const float e0 = __builtin_amdgcn_exp2f(m0 - mx), e1 = __builtin_amdgcn_exp2f(m1 - mx);
+            const float inv = __builtin_amdgcn_rcpf(ssum[qt][0][l32] * e0 + ssum[qt][1][l32] * e1);
+            c0[qt] = e0 * inv;
+            c1[qt] = e1 * inv;
+        }
+    }
+
+    // ---- linear part O^T += S^T phi(Q)^T, a quarter (32 features) at a time
+    // as it arrives: the raw rows go to the wave's buffer and come back as A
+    // operands (row cA - 32 ct, features 16 s + 8 hh .. + 7); LDS accesses of
+    // one wave complete in order, so no barrier is needed
+    const int arow = 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
+    float* qb = sbuf[ct];
+    f32x16 o[2] = {{}, {}};                          // the linear part first, as the head-pair kernel
+    f32x16 old[kCommit ? 4 : 1];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4*>(qb + (8 * i + lane / 8) * SQP + 4 * (lane % 8)) = sraw[qq][i];
+        if constexpr (kCommit) {
+            // the old tile of feature tile qq in the accumulator layout (rows
+            // 32 ct + 16 hh + rr, features 32 qq + l32)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) old[qq][rr] = qb[(16 * hh + rr) * SQP + l32];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * qq + s2;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(qb + arow * SQP + 16 * s2 + 8 * hh);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(qb + arow * SQP + 16 * s2 + 8 * hh + 4);
+            const float sv8[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            bf16x8 shi, slo;
+            split_hi_lo(sv8, shi, slo);
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
+                const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
+                o[qt] = mfma32(shi, pq, o[qt]);
+                o[qt] = mfma32(slo, pq, o[qt]);
+            }
+        }
+    }
+    // the sum of the two parts in the head-pair kernel's order, so the fused
+    // call's outputs are bit-identical to the plain step's
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            if constexpr (kNorm) o[qt][rr] = o[qt][rr] * beta[qt] + (opv[qt][0][rr] * c0[qt] + opv[qt][1][rr] * c1[qt]);
+            else o[qt][rr] = o[qt][rr] + (opv[qt][0][rr] * c0[qt] + opv[qt][1][rr] * c1[qt]);
+        }
+    }
+
+    // ---- outputs straight from the accumulators (rows past B_r are not written)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+        if (qt * 32 + l32 < Br) store_tile_global<D>(out + (int64_t)(qt * 32 + l32) * rs, o[qt], hh, ct);
+
+    if constexpr (kCommit) {
+        // ---- the commit of the wave's rows: S^T[c][f] += sum_j V[j][c] ReLU(K[j][f])
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft) {
+            const f32x16 acc = commit_tile<D, 2, PK, PV>(old[ft], sk, sv, Br, ct, ft, lane);
+            float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) __builtin_nontemporal_store(acc[rr], tile + (int64_t)rr * D);
+        }
         if constexpr (kNorm) commit_z<D, PK>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
     }
 }
@@ -1240,8 +1525,8 @@ hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
             break;
         default:
             if (two) {
-                if (norm) step_pair_bf16_mfma<128, true, true><<<units, block, 0, stream>>>(a);
-                else step_pair_bf16_mfma<128, true, false><<<units, block, 0, stream>>>(a);
+                if (norm) step_unit_bf16<true, true><<<units, 4 * kWave, 0, stream>>>(a);
+                else step_unit_bf16<true, false><<<units, 4 * kWave, 0, stream>>>(a);
             } else {
                 if (norm) step_commit_bf16_mfma<128, 1, true, true><<<units, block, 0, stream>>>(a);
                 else step_commit_bf16_mfma<128, 1, true, false><<<units, block, 0, stream>>>(a);

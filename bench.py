@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 import block_hybrid_linear_amd as bh  # noqa: E402
 from block_hybrid_linear_amd import synth  # noqa: E402
-from block_hybrid_linear_amd.workloads import BLOCK_LOOP, PREFILL_DECODE, SERVING_STEP  # noqa: E402
+from block_hybrid_linear_amd.workloads import BLOCK_LOOP, PREFILL_DECODE, SERVING_STEP, SINGLE_STEP  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
@@ -231,7 +231,21 @@ def graph_call_us(job: Job, reps: int = 3) -> dict:
 # CPU baseline: the oracle on a bounded sample of the same workload's units
 # ---------------------------------------------------------------------------
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(job: Job, budget_s: float) -> dict:
+    """The fp64 oracle on all requests x a subset of heads of the same job,
+    scaled by heads: with all the host's threads, and with one thread."""
+    import numpy as np
+
     import oracle
     wl = job.wl
     n, H = wl.n_req, wl.heads
@@ -246,7 +260,6 @@ def cpu_baseline(job: Job, budget_s: float) -> dict:
         st = job.sets[0]
         qkv = [(st["q"][i][:, :, hs].cpu(), st["k"][i][:, :, hs].cpu(), st["v"][i][:, :, hs].cpu())
                for i in range(len(st["q"]))]
-        import numpy as np
         t0 = time.perf_counter()
         S = np.zeros((n, h_s, wl.d, wl.d))
         if wl.prompt_range:
@@ -260,16 +273,32 @@ def cpu_baseline(job: Job, budget_s: float) -> dict:
                 S = oracle.commit(qkv[i - 1][1], qkv[i - 1][2], S)
         return time.perf_counter() - t0
 
-    dt1 = run(1)                                   # calibration on one head
-    h_s = 1
-    while h_s * 2 <= H and dt1 * h_s * 2 <= budget_s:
-        h_s *= 2
-    dt = run(h_s) if h_s > 1 else dt1
-    return {"value": round(job.tokens * (h_s / H) / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"all {n} requests x {h_s} of {H} heads of the same job (prefill + every step and "
-                      f"commit for those units), {dt:.1f} s of fp64 oracle time, scaled by {H}/{h_s}",
-            "seconds": round(dt, 2)}
+    def timed(budget: float) -> tuple[int, float]:
+        dt1 = run(1)                               # calibration on one head
+        h_s = 1
+        while h_s * 2 <= H and dt1 * h_s * 2 <= budget:
+            h_s *= 2
+        return h_s, (run(h_s) if h_s > 1 else dt1)
+
+    def entry(h_s: int, dt: float, cores: int) -> dict:
+        return {"value": round(job.tokens * (h_s / H) / dt, 1), "unit": "tokens/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"all {n} requests x {h_s} of {H} heads of the same job (prefill + every step and "
+                          f"commit for those units), {dt:.1f} s of fp64 oracle time on {cores} thread(s), "
+                          f"scaled by {H}/{h_s}",
+                "seconds": round(dt, 2)}
+
+    threads = oracle.num_threads()
+    h_s, dt = timed(budget_s)
+    res = entry(h_s, dt, threads)
+    oracle.set_num_threads(1)
+    try:
+        h1, dt1 = timed(budget_s / 2)
+    finally:
+        oracle.set_num_threads(threads)
+    res["single_core"] = entry(h1, dt1, 1)
+    res["cpu_model"] = cpu_model()
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -327,11 +356,12 @@ def time_call(fn, iters: int, warm: int = 2) -> float:
     return a.elapsed_time(b) / iters
 
 
-def commit_context(dev="cuda", rotate: int = 4) -> dict:
+def commit_context(dev="cuda", rotate: int = 8) -> dict:
     """hybrid_state_commit alone at the block-loop shapes (32 requests x 32
     heads, d = 128, B = 32): the calls cycle through `rotate` input sets (K/V
-    and S, ~143 MB each, so not served from the last-level cache), captured
-    as one HIP graph of 40 calls and replayed."""
+    and S, 84 MB each: 671 MB cycled, more than twice the 256 MB last-level
+    cache and the 32 MB of L2 together), captured as one HIP graph of 40
+    calls and replayed."""
     W = BLOCK_LOOP
     n, H, d, B = W.n_req, W.heads, W.d, W.blk
     slots = torch.arange(n, dtype=torch.int32, device=dev)
@@ -356,6 +386,7 @@ def commit_context(dev="cuda", rotate: int = 4) -> dict:
     byts, flops = commit_cost(n * H, B, d)
     del g
     return {"workload": W.name, "call": "hybrid_state_commit", "n_req": n, "heads": H, "head_dim": d, "block": B,
+            "input_sets": rotate, "distinct_bytes": rotate * (2 * n * B * H * d * 2 + n * H * d * d * 4),
             "us": round(ms * 1e3, 2), "alg_bytes": byts, "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -453,6 +484,160 @@ def norm_context(dev="cuda", rotate: int = 4) -> dict:
     res["prefill"] = {"workload": W.name, "plain_us": round(t_p * 1e3, 1), "norm_us": round(t_n * 1e3, 1),
                       "norm_GBps": round(pb / (t_n * 1e-3) / 1e9, 1)}
     del kp, vp
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# The other workloads, each timed as the calls it is made of
+# ---------------------------------------------------------------------------
+
+def _graph_ms(fns, side, reps: int = 3) -> float:
+    """ms per replay of the calls `fns` captured (in order) as one HIP graph on
+    `side`, the stream they enqueue on, after one warm replay."""
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for fn in fns:
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / reps
+
+
+def _rate(byts: float, flops: float, us: float) -> dict:
+    gbs = byts / (us * 1e-6) / 1e9
+    tfs = flops / (us * 1e-6) / 1e12
+    return {"us": round(us, 2), "alg_bytes": int(byts), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "TFLOPs": round(tfs, 2),
+            "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 5)}
+
+
+def launch_floor_us(calls: int = 200) -> float:
+    """us per launch of an (almost) empty kernel replayed in a HIP graph: the
+    floor under every call of the step."""
+    side = torch.cuda.Stream()
+    return _graph_ms([lambda: torch.cuda._sleep(0)] * calls, side) * 1e3 / calls
+
+
+def single_step_context(dev="cuda", calls: int = 200) -> dict:
+    """The single-denoising-step workload (1 request x 16 heads, d = 64,
+    B = 32; a 4096-token prefix folded into S, drawn as N(0, 4096 / 2) fp32):
+    one call moves 0.52 MB, so it is launch-bound; timed as `calls` calls
+    replayed in a HIP graph and launched one by one."""
+    W = SINGLE_STEP
+    n, H, d, B = W.n_req, W.heads, W.d, W.blk
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    S = synth.normal((n, H, d, d), synth.seed_of(W.index, 0, 0, synth.TENSOR_S), dtype=torch.float32, device=dev)
+    S.mul_((W.prefix_fixed / 2) ** 0.5)
+    q, k, v = (synth.normal((n, B, H, d), synth.seed_of(W.index, 0, 0, t), device=dev) for t in range(3))
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    fn = bh.prepare_step(q, k, v, S, slots, out, scale=W.scale, stream=side)
+    us_graph = _graph_ms([fn] * calls, side) * 1e3 / calls
+    fe = bh.prepare_step(q, k, v, S, slots, out, scale=W.scale)
+    us_eager = time_call(fe, calls) * 1e3
+    byts, flops = step_cost(n * H, B, d)
+    floor = launch_floor_us()
+    return {"workload": W.name, "n_req": n, "heads": H, "head_dim": d, "block": B,
+            "graph": _rate(byts, flops, us_graph), "eager": _rate(byts, flops, us_eager),
+            "launch_floor_us": round(floor, 2), "hbm_floor_us": round(byts / (HBM_PEAK_GBS * 1e3), 3),
+            "note": "0.52 MB per call: launch-bound (graph time minus the empty-kernel floor is the kernel's own)"}
+
+
+def block_loop_context(dev="cuda") -> dict:
+    """The full block loop (32 requests x 32 heads, d = 128, 32 blocks of
+    B = 32, 8 denoising steps per block with Q/K/V ~ N(0, 0.5^2) drawn anew
+    for every step, all 6.4 GB resident before timing): each block's 8
+    hybrid_attn_step calls and then one hybrid_state_commit of its last
+    step's K, V -- 288 calls -- captured as one HIP graph and replayed; the
+    same loop with each block's last step fused with its commit
+    (hybrid_attn_step_commit: 256 calls); and each kind of call alone."""
+    W = BLOCK_LOOP
+    n, H, d, B = W.n_req, W.heads, W.d, W.blk
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    state = torch.zeros(n, H, d, d, device=dev)
+    out = torch.empty(n, B, H, d, dtype=torch.bfloat16, device=dev)
+    qkv = [[synth.normal((n, B, H, d), synth.seed_of(W.index, b, t, tid), std=W.std, device=dev)
+            for tid in range(3)] for b in range(W.n_blocks) for t in range(W.steps_per_block)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    steps = [bh.prepare_step(q, k, v, state, slots, out, scale=W.scale, stream=side) for q, k, v in qkv]
+    T = W.steps_per_block
+    last = [qkv[b * T + T - 1] for b in range(W.n_blocks)]
+    commits = [bh.prepare_commit(k, v, state, slots, stream=side) for _, k, v in last]
+    fused = [bh.prepare_step_commit(q, k, v, state, slots, out, scale=W.scale, stream=side) for q, k, v in last]
+    plain_loop, fused_loop = [], []
+    for b in range(W.n_blocks):
+        plain_loop += steps[b * T:(b + 1) * T] + [commits[b]]
+        fused_loop += steps[b * T:(b + 1) * T - 1] + [fused[b]]
+    sb, sf = step_cost(n * H, B, d)
+    cb, cf = commit_cost(n * H, B, d)
+    fb, ff = step_commit_cost(n * H, B, d)
+    nb = W.n_blocks
+    loop_bytes, loop_flops = nb * T * sb + nb * cb, nb * T * sf + nb * cf
+    fused_bytes, fused_flops = nb * (T - 1) * sb + nb * fb, nb * (T - 1) * sf + nb * ff
+    res = {"workload": W.name, "n_req": n, "heads": H, "head_dim": d, "block": B, "blocks": nb,
+           "steps_per_block": T, "qkv_std": W.std, "calls": len(plain_loop)}
+    state.zero_()
+    ms = _graph_ms(plain_loop, side)
+    tok = nb * T * n * B                      # active-block token-steps of the loop
+    res["loop"] = {"ms": round(ms, 3), "alg_bytes": loop_bytes, "GBps": round(loop_bytes / (ms * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(loop_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "hbm_floor_ms": round(loop_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3),
+                   "token_steps_per_s": round(tok / (ms * 1e-3), 1),
+                   "committed_tokens_per_s": round(nb * n * B / (ms * 1e-3), 1)}
+    state.zero_()
+    ms = _graph_ms(fused_loop, side)
+    res["fused_loop"] = {"ms": round(ms, 3), "alg_bytes": fused_bytes,
+                         "GBps": round(fused_bytes / (ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(fused_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "hbm_floor_ms": round(fused_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3),
+                         "token_steps_per_s": round(tok / (ms * 1e-3), 1)}
+    state.zero_()
+    res["step"] = _rate(sb, sf, _graph_ms(steps, side) * 1e3 / len(steps))
+    res["commit"] = _rate(cb, cf, _graph_ms(commits, side) * 1e3 / len(commits))
+    res["step_commit"] = _rate(fb, ff, _graph_ms(fused, side) * 1e3 / len(fused))
+    del qkv, steps, commits, fused, plain_loop, fused_loop
+    torch.cuda.empty_cache()
+    return res
+
+
+def cold_decode_context(dev="cuda", rotate: int = 40) -> dict:
+    """The prefill + decode workload's decode calls (8 requests x 32 heads,
+    d = 128, B = 64) with cold state: `rotate` sets of state and Q/K/V
+    (33.5 MB each: 1.3 GB between two uses of one set, against 256 MB of
+    last-level cache and 32 MB of L2), `rotate` calls per HIP graph."""
+    W = PREFILL_DECODE
+    n, H, d, B = W.n_req, W.heads, W.d, W.blk
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    sets = []
+    for i in range(rotate):
+        S = synth.normal((n, H, d, d), synth.seed_of(W.index, 50 + i, 0, synth.TENSOR_S), dtype=torch.float32,
+                         device=dev)
+        q, k, v = (synth.normal((n, B, H, d), synth.seed_of(W.index, 50 + i, 0, t), device=dev) for t in range(3))
+        sets.append((q, k, v, S, torch.empty_like(q)))
+    side = torch.cuda.Stream()
+    st = [bh.prepare_step(q, k, v, S, slots, o, scale=W.scale, stream=side) for q, k, v, S, o in sets]
+    sc = [bh.prepare_step_commit(q, k, v, S, slots, o, scale=W.scale, stream=side) for q, k, v, S, o in sets]
+    sb, sf = step_cost(n * H, B, d)
+    fb, ff = step_commit_cost(n * H, B, d)
+    res = {"workload": W.name, "input_sets": rotate, "distinct_bytes": rotate * sb,
+           "step": _rate(sb, sf, _graph_ms(st, side) * 1e3 / rotate),
+           "step_commit": _rate(fb, ff, _graph_ms(sc, side) * 1e3 / rotate)}
+    del sets, st, sc
     torch.cuda.empty_cache()
     return res
 
@@ -693,6 +878,19 @@ def main():
             gbs = byts / (us * 1e-6) / 1e9
             kernels[kind].update({"graph_us": round(us, 2), "graph_GBps": round(gbs, 1),
                                   "graph_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    # the denoising calls alone: per bench step, each block's steps and fused
+    # last step (one denoising step of the hybrid layer for all requests and
+    # heads per call), at their in-graph per-call times
+    dec_kinds = [k for k in ("step", "step_commit") if k in kernels]
+    denoise = None
+    if dec_kinds:
+        calls = sum(kernels[k]["calls_per_step"] for k in dec_kinds)
+        dec_us = sum(kernels[k]["calls_per_step"] * kernels[k]["graph_us"] for k in dec_kinds)
+        tok = wl.n_blocks * wl.steps_per_block * wl.n_req * wl.blk
+        denoise = {"calls_per_step": calls, "token_steps_per_step": tok, "us_per_step": round(dec_us, 2),
+                   "token_steps_per_s": round(tok / (dec_us * 1e-6), 1),
+                   "denoising_steps_per_s": round(calls / (dec_us * 1e-6), 1),
+                   "from": "graph_us of the step and step_commit calls (state as the bench step leaves it)"}
     dom = max(kernels, key=lambda k: kernels[k]["share_of_step"])
     kd = kernels[dom]
     traffic = measured_traffic(dom, wl.name)
@@ -716,14 +914,29 @@ def main():
                    "kernels_from": "HIP events around each call of the eager steps; graph_* from each "
                                    "kind's calls of one step replayed back to back in a HIP graph"},
         "kernels": kernels,
+        "denoise": denoise,
     }
     if not args.no_context:
         log("[bench] context: hybrid step vs exact full-prefix step at the serving shapes")
         result["context"] = exact_context()
         log("[bench] context: the normalised variant beside the plain calls")
         result["context"]["norm"] = norm_context()
-        log("[bench] context: the commit alone at the block-loop shapes")
+        log("[bench] context: the commit alone at the block-loop shapes (cold)")
         result["context"]["commit"] = commit_context()
+        if wl is PREFILL_DECODE:
+            log("[bench] context: the decode calls with cold state")
+            cold = cold_decode_context()
+            result["context"]["cold_decode"] = cold
+            if denoise is not None:
+                cs, cc = cold["step"]["us"], cold["step_commit"]["us"]
+                dec_us = kernels["step"]["calls_per_step"] * cs + kernels["step_commit"]["calls_per_step"] * cc
+                denoise["cold"] = {"us_per_step": round(dec_us, 2),
+                                   "token_steps_per_s": round(denoise["token_steps_per_step"] / (dec_us * 1e-6), 1),
+                                   "denoising_steps_per_s": round(denoise["calls_per_step"] / (dec_us * 1e-6), 1)}
+        log("[bench] context: the single-step workload")
+        result["context"]["single_step"] = single_step_context()
+        log("[bench] context: the block-loop workload end to end")
+        result["context"]["block_loop"] = block_loop_context()
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(job, args.cpu_budget)

@@ -56,6 +56,8 @@ def _load():
             build(force=False)
             lib = ctypes.CDLL(_LIB)
             lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
             lib.oracle_step.argtypes = [_D, _D, _D, _D, _I32, _I32, _D] + [ctypes.c_int] * 5 + [ctypes.c_double]
             lib.oracle_commit.argtypes = [_D, _D, _D, _I32, _I32] + [ctypes.c_int] * 5
             lib.oracle_prefill.argtypes = [_D, _D, _I64, _D, _I32] + [ctypes.c_int] * 4
@@ -102,6 +104,12 @@ def _p(a, typ):
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the following calls (the units of a call are spread
+    over them; nothing inside a unit changes)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def step(q, k, v, S, slots=None, blk_lens=None, scale=None) -> np.ndarray:

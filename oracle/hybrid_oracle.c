@@ -69,6 +69,16 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the following calls (n >= 1); changes nothing inside a unit. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Index helpers for the token-major [n][T][H][d] layout. */
 static size_t tok(int64_t r, int64_t t, int64_t h, int64_t T, int64_t H, int64_t d)
 {

@@ -668,84 +668,109 @@ def _fill_normal_(x: torch.Tensor, seed: int, chunk: int = 1 << 28) -> torch.Ten
     return x
 
 
-def layer_stack(dev="cuda", steps: int = 3) -> dict:
-    L, LH = STACK["layers"], STACK["hybrid_layers"]
-    n, H, d, B, F = STACK["n_req"], STACK["heads"], STACK["head_dim"], STACK["block"], STACK["mlp_inter"]
-    hid = H * d
-    hybrid_at = {(2 * i + 1) * L // (2 * LH) for i in range(LH)}   # spread over the stack: 1, 5, 8, 11, 15, 18
-    assert len(hybrid_at) == LH
-    base = 7_000_000
-    wsc = lambda fan_in: fan_in ** -0.5                 # noqa: E731
-    weights = []
-    for l in range(L):
-        w = [synth.normal((hid, hid), base + 100 * l + t, std=wsc(hid), device=dev) for t in range(4)]  # q k v o
-        w.append(synth.normal((hid, 2 * F), base + 100 * l + 4, std=wsc(hid), device=dev))            # gate|up
-        w.append(synth.normal((F, hid), base + 100 * l + 5, std=wsc(F), device=dev))                  # down
-        weights.append(w)
-    x0 = synth.normal((n * B, hid), base + 99_000, device=dev)
-    slots = torch.arange(n, dtype=torch.int32, device=dev)
-    out = {"config": dict(STACK), "hybrid_layer_indices": sorted(hybrid_at), "results": []}
-    for lo, hi in STACK["prefix_ranges"]:
+class LayerStack:
+    """A stand-in decoder stack for one denoising step of the active block:
+    per layer RMSNorm, Q/K/V projections, attention, output projection and a
+    SwiGLU MLP, with seeded random bf16 weights.  Layers in `hybrid_at` run
+    hybrid_attn_step over a per-layer fp32 state (entries ~ N(0, P_r / 2)),
+    the others hybrid_exact_step over a packed bf16 KV cache of the requests'
+    prefixes (one cache buffer shared by the exact layers: at 9-43 GB it
+    cannot stay in any cache, so sharing it changes no traffic)."""
+
+    def __init__(self, cfg: dict, prefix_range, dev="cuda", base: int = 7_000_000):
+        L, LH = cfg["layers"], cfg["hybrid_layers"]
+        self.n, self.H, self.d, self.B, self.F = (cfg["n_req"], cfg["heads"], cfg["head_dim"], cfg["block"],
+                                                  cfg["mlp_inter"])
+        n, H, d, B, F = self.n, self.H, self.d, self.B, self.F
+        self.hid = hid = H * d
+        self.hybrid_at = {(2 * i + 1) * L // (2 * LH) for i in range(LH)}   # spread over the stack
+        assert len(self.hybrid_at) == LH
+        wsc = lambda fan_in: fan_in ** -0.5                 # noqa: E731
+        self.weights = []
+        for l in range(L):
+            w = [synth.normal((hid, hid), base + 100 * l + t, std=wsc(hid), device=dev) for t in range(4)]  # qkvo
+            w.append(synth.normal((hid, 2 * F), base + 100 * l + 4, std=wsc(hid), device=dev))            # gate|up
+            w.append(synth.normal((F, hid), base + 100 * l + 5, std=wsc(F), device=dev))                  # down
+            self.weights.append(w)
+        self.x0 = synth.normal((n * B, hid), base + 99_000, device=dev)
+        self.slots = torch.arange(n, dtype=torch.int32, device=dev)
+        lo, hi = prefix_range
         P = synth.uniform_int(n, lo, hi, base + 98_000 + lo)
         cu = synth.cu_from_lengths(P)
-        total = int(cu[-1])
-        cud = cu.to(dev)
-        kc = _fill_normal_(torch.empty((total, H, d), dtype=torch.bfloat16, device=dev), base + 1)
-        vc = _fill_normal_(torch.empty((total, H, d), dtype=torch.bfloat16, device=dev), base + 2)
-        states = {l: synth.normal((n, H, d, d), base + 200 + l, dtype=torch.float32, device=dev)
-                  .mul_(torch.sqrt(P.double() / 2).float().to(dev).view(-1, 1, 1, 1)) for l in hybrid_at}
-        ws = torch.empty(bh.hybrid_exact_step_workspace_bytes(n, H, B, d), dtype=torch.uint8, device=dev)
-        attn_out = torch.empty((n, B, H, d), dtype=torch.bfloat16, device=dev)
+        self.cu = cu
+        self.total = total = int(cu[-1])
+        self.cud = cu.to(dev)
+        self.kc = _fill_normal_(torch.empty((total, H, d), dtype=torch.bfloat16, device=dev), base + 1)
+        self.vc = _fill_normal_(torch.empty((total, H, d), dtype=torch.bfloat16, device=dev), base + 2)
+        self.states = {l: synth.normal((n, H, d, d), base + 200 + l, dtype=torch.float32, device=dev)
+                       .mul_(torch.sqrt(P.double() / 2).float().to(dev).view(-1, 1, 1, 1)) for l in self.hybrid_at}
+        self.ws = torch.empty(bh.hybrid_exact_step_workspace_bytes(n, H, B, d), dtype=torch.uint8, device=dev)
+        self.attn_out = torch.empty((n, B, H, d), dtype=torch.bfloat16, device=dev)
 
-        def forward(hybrid: bool, attn_ms=None):
-            x = x0.clone()
-            for l, (wq, wk, wv, wo, wgu, wd) in enumerate(weights):
-                h = torch.nn.functional.rms_norm(x, (hid,))
-                q, k, v = ((h @ w).view(n, B, H, d) for w in (wq, wk, wv))
-                e0 = e1 = None
-                if attn_ms is not None:
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                if hybrid and l in hybrid_at:
-                    bh.hybrid_attn_step(q, k, v, states[l], slots, out=attn_out)
-                else:
-                    bh.hybrid_exact_step(q, k, v, kc, vc, cud, out=attn_out, chunk=256, workspace=ws)
-                if attn_ms is not None:
-                    e1.record()
-                    attn_ms.append((l, e0, e1))
-                x = x + attn_out.view(n * B, hid) @ wo
-                h = torch.nn.functional.rms_norm(x, (hid,))
-                g, u = (h @ wgu).split(F, dim=1)
-                x = x + (torch.nn.functional.silu(g) * u) @ wd
-            return x
+    def forward(self, hybrid: bool, attn_ms=None, capture=None):
+        """One denoising step through the stack.  `attn_ms` collects (layer,
+        start event, end event) around each attention call; `capture` (a
+        dict) receives each layer's q, k, v and attention output."""
+        n, H, d, B, F, hid = self.n, self.H, self.d, self.B, self.F, self.hid
+        x = self.x0.clone()
+        for l, (wq, wk, wv, wo, wgu, wd) in enumerate(self.weights):
+            h = torch.nn.functional.rms_norm(x, (hid,))
+            q, k, v = ((h @ w).view(n, B, H, d) for w in (wq, wk, wv))
+            e0 = e1 = None
+            if attn_ms is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            if hybrid and l in self.hybrid_at:
+                bh.hybrid_attn_step(q, k, v, self.states[l], self.slots, out=self.attn_out)
+            else:
+                bh.hybrid_exact_step(q, k, v, self.kc, self.vc, self.cud, out=self.attn_out, chunk=256,
+                                     workspace=self.ws)
+            if attn_ms is not None:
+                e1.record()
+                attn_ms.append((l, e0, e1))
+            if capture is not None:
+                capture[l] = (q.clone(), k.clone(), v.clone(), self.attn_out.clone())
+            x = x + self.attn_out.view(n * B, hid) @ wo
+            h = torch.nn.functional.rms_norm(x, (hid,))
+            g, u = (h @ wgu).split(F, dim=1)
+            x = x + (torch.nn.functional.silu(g) * u) @ wd
+        return x
 
-        res = {"prefix_range": [lo, hi], "prefix_tokens": total, "kv_cache_GB": round(2 * kc.numel() * 2 / 1e9, 2)}
+
+def layer_stack(dev="cuda", steps: int = 3) -> dict:
+    L, LH = STACK["layers"], STACK["hybrid_layers"]
+    out = {"config": dict(STACK), "results": []}
+    for lo, hi in STACK["prefix_ranges"]:
+        stk = LayerStack(STACK, (lo, hi), dev)
+        out["hybrid_layer_indices"] = sorted(stk.hybrid_at)
+        res = {"prefix_range": [lo, hi], "prefix_tokens": stk.total,
+               "kv_cache_GB": round(2 * stk.kc.numel() * 2 / 1e9, 2)}
         for mode in ("exact", "hybrid"):
             hyb = mode == "hybrid"
             for _ in range(2):
-                forward(hyb)
+                stk.forward(hyb)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             for _ in range(steps):
-                forward(hyb)
+                stk.forward(hyb)
             b.record()
             torch.cuda.synchronize()
             step_ms = a.elapsed_time(b) / steps
             evs = []
-            forward(hyb, evs)
+            stk.forward(hyb, evs)
             torch.cuda.synchronize()
             att = [(l, e0.elapsed_time(e1)) for l, e0, e1 in evs]
             res[f"{mode}_step_ms"] = round(step_ms, 3)
             res[f"{mode}_attention_ms"] = round(sum(t for _, t in att), 3)
             if hyb:
-                res["hybrid_layer_attention_ms"] = round(sum(t for l, t in att if l in hybrid_at) / LH, 4)
-            res["exact_layer_attention_ms"] = round(sum(t for l, t in att if not (hyb and l in hybrid_at)) /
+                res["hybrid_layer_attention_ms"] = round(sum(t for l, t in att if l in stk.hybrid_at) / LH, 4)
+            res["exact_layer_attention_ms"] = round(sum(t for l, t in att if not (hyb and l in stk.hybrid_at)) /
                                                     (L - (LH if hyb else 0)), 4)
             log(f"[stack] prefixes {lo}-{hi}: {mode} stack {step_ms:.2f} ms per step")
         res["speedup"] = round(res["exact_step_ms"] / res["hybrid_step_ms"], 3)
         out["results"].append(res)
-        del kc, vc, states, ws
+        del stk
         torch.cuda.empty_cache()
     return out
 

@@ -175,3 +175,70 @@ def test_prefill_decode_sampled():
     got = np.stack([state_to_oracle(state)[r, h:h + 1] for r, h in units])
     es = assert_parity(got, S_ref, torch.bfloat16, "final state")
     log(f"prefill + decode: prefill rel err {ep:.2e}, worst step {worst:.2e}, final state {es:.2e}")
+
+
+def test_prefill_decode_parts_isolated():
+    """The prefill + decode workload's decode calls at their full size (8
+    requests x 32 heads, d = 128, B = 64), each part of the output isolated:
+    S = 0 (softmax part only) and V = 0 (linear part only), for the step and
+    for the fused step + commit.  Compared on every head of the request with
+    the shortest prompt and one head of each other request, whose states are
+    the oracle's prefill of their prompts (the other units get random states).
+    At these prefix lengths the linear part dominates the output, so the
+    whole-output rule alone would not see an error in the softmax part."""
+    W = PREFILL_DECODE
+    lens = synth.uniform_int(W.n_req, *W.prompt_range, synth.seed_of(W.index, tensor=synth.TENSOR_LEN))
+    cu = synth.cu_from_lengths(lens)
+    total = int(cu[-1])
+    pk = synth.normal((total, W.heads, W.d), synth.seed_of(W.index, 99, 0, synth.TENSOR_K), device=DEV)
+    pv = synth.normal((total, W.heads, W.d), synth.seed_of(W.index, 99, 0, synth.TENSOR_V), device=DEV)
+    r0 = int(torch.argmin(lens))
+    units = sorted({(r0, h) for h in range(W.heads)} | {(r, (7 * r + 3) % W.heads) for r in range(W.n_req)})
+    log(f"isolation: {len(units)} units, all heads of request {r0} ({int(lens[r0])} prompt tokens)")
+    ks_ = [pk[int(cu[r]):int(cu[r + 1]), h:h + 1].cpu() for r, h in units]
+    vs_ = [pv[int(cu[r]):int(cu[r + 1]), h:h + 1].cpu() for r, h in units]
+    S_ref = oracle.prefill(torch.cat(ks_), torch.cat(vs_), synth.cu_from_lengths([x.shape[0] for x in ks_]))
+    del pk, pv
+    state = synth.normal((W.n_req, W.heads, W.d, W.d), synth.seed_of(W.index, 98, 0, synth.TENSOR_S),
+                         dtype=torch.float32, device=DEV).mul_(150.0)
+    Sl = state_from_oracle(S_ref)                               # [units, 1, d, d], library layout
+    for i, (r, h) in enumerate(units):
+        state[r, h] = Sl[i, 0]
+    slots = torch.arange(W.n_req, dtype=torch.int32, device=DEV)
+    q, k, v = (synth.normal((W.n_req, W.blk, W.heads, W.d), synth.seed_of(W.index, 0, 0, t), device=DEV)
+               for t in range(3))
+    qs, ks, vs = _gather(q, units), _gather(k, units), _gather(v, units)
+    zv = torch.zeros_like(v)
+    for name, call in (("step", bh.hybrid_attn_step), ("fused step + commit", bh.hybrid_attn_step_commit)):
+        out_s = call(q, k, v, torch.zeros_like(state), slots, scale=W.scale)
+        out_l = call(q, k, zv, state.clone(), slots, scale=W.scale)
+        torch.cuda.synchronize()
+        es = assert_parity(_gather(out_s, units), oracle.step(qs, ks, vs, 0 * S_ref, scale=W.scale), torch.bfloat16,
+                           f"{name}: softmax part (S = 0)")
+        el = assert_parity(_gather(out_l, units), oracle.step(qs, ks, np.zeros(vs.shape), S_ref, scale=W.scale),
+                           torch.bfloat16, f"{name}: linear part (V = 0)")
+        log(f"{name}: softmax part rel err {es:.2e}, linear part rel err {el:.2e}")
+
+
+def test_block_loop_linear_part_isolated():
+    """The block loop's calls at full size (32 requests x 32 heads, d = 128,
+    B = 32) with V = 0 over a state of 31 committed blocks' magnitude, for the
+    step and the fused step + commit, compared on every head of one request
+    and one head of each other (the loop itself starts from S = 0, which
+    isolates the softmax part of its first block)."""
+    W = BLOCK_LOOP
+    units = sorted({(5, h) for h in range(W.heads)} | {(r, (11 * r + 1) % W.heads) for r in range(W.n_req)})
+    S = synth.normal((W.n_req, W.heads, W.d, W.d), synth.seed_of(W.index, 97, 0, synth.TENSOR_S),
+                     dtype=torch.float32, device=DEV).mul_(4.0)
+    slots = torch.arange(W.n_req, dtype=torch.int32, device=DEV)
+    q, k = (synth.normal((W.n_req, W.blk, W.heads, W.d), synth.seed_of(W.index, 31, 7, t), std=W.std, device=DEV)
+            for t in range(2))
+    zv = torch.zeros_like(q)
+    S_units = np.stack([state_to_oracle(S)[r, h:h + 1] for r, h in units])
+    qs, ks = _gather(q, units), _gather(k, units)
+    ref = oracle.step(qs, ks, np.zeros(qs.shape), S_units, scale=W.scale)
+    for name, call in (("step", bh.hybrid_attn_step), ("fused step + commit", bh.hybrid_attn_step_commit)):
+        out = call(q, k, zv, S.clone(), slots, scale=W.scale)
+        torch.cuda.synchronize()
+        e = assert_parity(_gather(out, units), ref, torch.bfloat16, f"{name}: linear part (V = 0)")
+        log(f"block loop {name}: linear part rel err {e:.2e}")

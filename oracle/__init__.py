@@ -58,15 +58,16 @@ def _load():
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
             lib.oracle_set_num_threads.restype = None
-            lib.oracle_step.argtypes = [_D, _D, _D, _D, _I32, _I32, _D] + [ctypes.c_int] * 5 + [ctypes.c_double]
-            lib.oracle_commit.argtypes = [_D, _D, _D, _I32, _I32] + [ctypes.c_int] * 5
-            lib.oracle_prefill.argtypes = [_D, _D, _I64, _D, _I32] + [ctypes.c_int] * 4
-            for fn in (lib.oracle_step_recompute, lib.oracle_exact_step, lib.oracle_step_norm_recompute):
-                fn.argtypes = [_D, _D, _D, _D, _D, _I64, _I32, _D] + [ctypes.c_int] * 4 + [ctypes.c_double]
-            lib.oracle_step_norm.argtypes = [_D, _D, _D, _D, _D, _I32, _I32, _D] + [ctypes.c_int] * 5 + \
-                [ctypes.c_double]
-            lib.oracle_znorm_commit.argtypes = [_D, _D, _I32, _I32] + [ctypes.c_int] * 5
-            lib.oracle_znorm_prefill.argtypes = [_D, _I64, _D, _I32] + [ctypes.c_int] * 4
+            i = ctypes.c_int
+            lib.oracle_step.argtypes = [_D, _D, _D, _D, _I32, _I32, _D] + [i] * 5 + [ctypes.c_double, i]
+            lib.oracle_commit.argtypes = [_D, _D, _D, _I32, _I32] + [i] * 6
+            lib.oracle_prefill.argtypes = [_D, _D, _I64, _D, _I32] + [i] * 5
+            for fn in (lib.oracle_step_recompute, lib.oracle_step_norm_recompute):
+                fn.argtypes = [_D, _D, _D, _D, _D, _I64, _I32, _D] + [i] * 4 + [ctypes.c_double, i]
+            lib.oracle_exact_step.argtypes = [_D, _D, _D, _D, _D, _I64, _I32, _D] + [i] * 4 + [ctypes.c_double]
+            lib.oracle_step_norm.argtypes = [_D, _D, _D, _D, _D, _I32, _I32, _D] + [i] * 5 + [ctypes.c_double, i]
+            lib.oracle_znorm_commit.argtypes = [_D, _D, _I32, _I32] + [i] * 6
+            lib.oracle_znorm_prefill.argtypes = [_D, _I64, _D, _I32] + [i] * 5
             for fn in (lib.oracle_step, lib.oracle_commit, lib.oracle_prefill,
                        lib.oracle_step_recompute, lib.oracle_exact_step, lib.oracle_step_norm,
                        lib.oracle_znorm_commit, lib.oracle_znorm_prefill, lib.oracle_step_norm_recompute):
@@ -102,6 +103,17 @@ def _p(a, typ):
     return None if a is None else a.ctypes.data_as(typ)
 
 
+# The feature maps phi (hybrid_oracle.c): "relu" max(x, 0), the pages' worked
+# example; "elu1" ELU(x) + 1 (x + 1 for x > 0, e^x otherwise).
+PHI = {"relu": 0, "elu1": 1}
+
+
+def _map(phi: str) -> int:
+    if phi not in PHI:
+        raise ValueError(f"unknown feature map {phi!r} (one of {sorted(PHI)})")
+    return PHI[phi]
+
+
 def num_threads() -> int:
     return _load().oracle_num_threads()
 
@@ -112,7 +124,7 @@ def set_num_threads(n: int) -> None:
     _load().oracle_set_num_threads(int(n))
 
 
-def step(q, k, v, S, slots=None, blk_lens=None, scale=None) -> np.ndarray:
+def step(q, k, v, S, slots=None, blk_lens=None, scale=None, phi="relu") -> np.ndarray:
     """O = Softmax(scale Q_a K_a^T) V_a + phi(Q_a) S per (request, head).
 
     Rows at or past ``blk_lens[r]`` are returned as zeros (never written)."""
@@ -127,11 +139,11 @@ def step(q, k, v, S, slots=None, blk_lens=None, scale=None) -> np.ndarray:
         scale = 1.0 / np.sqrt(d)
     out = np.zeros_like(q)
     _load().oracle_step(_p(q, _D), _p(k, _D), _p(v, _D), _p(S, _D), _p(slots, _I32),
-                        _p(bl, _I32), _p(out, _D), n_req, n_slots, H, blk, d, float(scale))
+                        _p(bl, _I32), _p(out, _D), n_req, n_slots, H, blk, d, float(scale), _map(phi))
     return out
 
 
-def commit(k, v, S, slots=None, blk_lens=None) -> np.ndarray:
+def commit(k, v, S, slots=None, blk_lens=None, phi="relu") -> np.ndarray:
     """Returns S + phi(K)^T V for each request's slot (a new fp64 array)."""
     k, v = _f64(k), _f64(v)
     S = np.array(_f64(S), copy=True)
@@ -141,11 +153,11 @@ def commit(k, v, S, slots=None, blk_lens=None) -> np.ndarray:
     slots = _i32(slots if slots is not None else np.arange(n_req), n_req)
     bl = _i32(blk_lens, n_req)
     _load().oracle_commit(_p(k, _D), _p(v, _D), _p(S, _D), _p(slots, _I32), _p(bl, _I32),
-                          n_req, n_slots, H, blk, d)
+                          n_req, n_slots, H, blk, d, _map(phi))
     return S
 
 
-def prefill(k, v, cu_seqlens, S=None, slots=None, n_slots=None) -> np.ndarray:
+def prefill(k, v, cu_seqlens, S=None, slots=None, n_slots=None, phi="relu") -> np.ndarray:
     """Returns the state with each request's slot overwritten by
     sum_t phi(k_t)^T v_t over its prompt (packed [total, H, d])."""
     k, v = _f64(k), _f64(v)
@@ -158,11 +170,11 @@ def prefill(k, v, cu_seqlens, S=None, slots=None, n_slots=None) -> np.ndarray:
     S = np.array(_f64(S), copy=True)
     slots = _i32(slots if slots is not None else np.arange(n_req), n_req)
     _load().oracle_prefill(_p(k, _D), _p(v, _D), _p(cu, _I64), _p(S, _D), _p(slots, _I32),
-                           n_req, S.shape[0], H, d)
+                           n_req, S.shape[0], H, d, _map(phi))
     return S
 
 
-def _prefix_form(fn, q, k, v, kp, vp, cu_seqlens, blk_lens, scale):
+def _prefix_form(fn, q, k, v, kp, vp, cu_seqlens, blk_lens, scale, *extra):
     q, k, v, kp, vp = _f64(q), _f64(k), _f64(v), _f64(kp), _f64(vp)
     n_req, blk, H, d = q.shape
     cu = np.ascontiguousarray(_np(cu_seqlens), dtype=np.int64)
@@ -172,14 +184,14 @@ def _prefix_form(fn, q, k, v, kp, vp, cu_seqlens, blk_lens, scale):
         scale = 1.0 / np.sqrt(d)
     out = np.zeros_like(q)
     fn(_p(q, _D), _p(k, _D), _p(v, _D), _p(kp, _D), _p(vp, _D), _p(cu, _I64), _p(bl, _I32),
-       _p(out, _D), n_req, H, blk, d, float(scale))
+       _p(out, _D), n_req, H, blk, d, float(scale), *extra)
     return out
 
 
-def step_recompute(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None) -> np.ndarray:
+def step_recompute(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None, phi="relu") -> np.ndarray:
     """The formula's own form: softmax part + (phi(Q_a) phi(K_p)^T) V_p from the
     retained prefix keys/values (packed [total, H, d])."""
-    return _prefix_form(_load().oracle_step_recompute, q, k, v, kp, vp, cu_seqlens, blk_lens, scale)
+    return _prefix_form(_load().oracle_step_recompute, q, k, v, kp, vp, cu_seqlens, blk_lens, scale, _map(phi))
 
 
 def exact_step(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None) -> np.ndarray:
@@ -193,7 +205,7 @@ def exact_step(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None) -> np.nda
 # S (a reading of the pages' LoLCATs-based retrofit; see hybrid_oracle.c).
 
 
-def step_norm(q, k, v, S, z, slots=None, blk_lens=None, scale=None) -> np.ndarray:
+def step_norm(q, k, v, S, z, slots=None, blk_lens=None, scale=None, phi="relu") -> np.ndarray:
     """O_i = (sum_j exp(l_ij) v_j + phi(q_i) S) / (sum_j exp(l_ij) + phi(q_i) . z)
     per (request, head); rows at or past ``blk_lens[r]`` are zeros."""
     q, k, v, S, z = _f64(q), _f64(k), _f64(v), _f64(S), _f64(z)
@@ -207,11 +219,11 @@ def step_norm(q, k, v, S, z, slots=None, blk_lens=None, scale=None) -> np.ndarra
         scale = 1.0 / np.sqrt(d)
     out = np.zeros_like(q)
     _load().oracle_step_norm(_p(q, _D), _p(k, _D), _p(v, _D), _p(S, _D), _p(z, _D), _p(slots, _I32),
-                             _p(bl, _I32), _p(out, _D), n_req, n_slots, H, blk, d, float(scale))
+                             _p(bl, _I32), _p(out, _D), n_req, n_slots, H, blk, d, float(scale), _map(phi))
     return out
 
 
-def znorm_commit(k, z, slots=None, blk_lens=None) -> np.ndarray:
+def znorm_commit(k, z, slots=None, blk_lens=None, phi="relu") -> np.ndarray:
     """Returns z + sum_j phi(k_j) over each request's valid block rows."""
     k = _f64(k)
     z = np.array(_f64(z), copy=True)
@@ -220,11 +232,12 @@ def znorm_commit(k, z, slots=None, blk_lens=None) -> np.ndarray:
     assert z.shape == (n_slots, H, d)
     slots = _i32(slots if slots is not None else np.arange(n_req), n_req)
     bl = _i32(blk_lens, n_req)
-    _load().oracle_znorm_commit(_p(k, _D), _p(z, _D), _p(slots, _I32), _p(bl, _I32), n_req, n_slots, H, blk, d)
+    _load().oracle_znorm_commit(_p(k, _D), _p(z, _D), _p(slots, _I32), _p(bl, _I32), n_req, n_slots, H, blk, d,
+                                _map(phi))
     return z
 
 
-def znorm_prefill(k, cu_seqlens, z=None, slots=None, n_slots=None) -> np.ndarray:
+def znorm_prefill(k, cu_seqlens, z=None, slots=None, n_slots=None, phi="relu") -> np.ndarray:
     """Returns z with each request's slot overwritten by sum_t phi(k_t) over its
     prompt (packed [total, H, d])."""
     k = _f64(k)
@@ -236,11 +249,13 @@ def znorm_prefill(k, cu_seqlens, z=None, slots=None, n_slots=None) -> np.ndarray
         z = np.zeros((n_slots if n_slots is not None else n_req, H, d))
     z = np.array(_f64(z), copy=True)
     slots = _i32(slots if slots is not None else np.arange(n_req), n_req)
-    _load().oracle_znorm_prefill(_p(k, _D), _p(cu, _I64), _p(z, _D), _p(slots, _I32), n_req, z.shape[0], H, d)
+    _load().oracle_znorm_prefill(_p(k, _D), _p(cu, _I64), _p(z, _D), _p(slots, _I32), n_req, z.shape[0], H, d,
+                                 _map(phi))
     return z
 
 
-def step_norm_recompute(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None) -> np.ndarray:
+def step_norm_recompute(q, k, v, kp, vp, cu_seqlens, blk_lens=None, scale=None, phi="relu") -> np.ndarray:
     """The normalised output with one weight per key: exp(l_ij) for block keys
     and phi(q_i) . phi(k_t) for the retained prefix tokens (packed [total, H, d])."""
-    return _prefix_form(_load().oracle_step_norm_recompute, q, k, v, kp, vp, cu_seqlens, blk_lens, scale)
+    return _prefix_form(_load().oracle_step_norm_recompute, q, k, v, kp, vp, cu_seqlens, blk_lens, scale,
+                        _map(phi))

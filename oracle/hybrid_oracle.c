@@ -57,8 +57,20 @@
 #include <omp.h>
 #endif
 
-/* phi(x) = ReLU(x): the feature map of the worked example [W]. */
-static double phi(double x) { return x > 0.0 ? x : 0.0; }
+/*
+ * The feature map phi, chosen by `map` in every function that applies it:
+ *   0  ReLU: phi(x) = max(x, 0), the worked example's map [W];
+ *   1  ELU + 1: phi(x) = x + 1 for x > 0 and e^x otherwise, another fixed
+ *      map.  [F] calls phi only "a kernel-function map"; ELU + 1 is the
+ *      common fixed choice of linear attention, positive everywhere (so the
+ *      normalised variant's denominator never vanishes) and continuous with
+ *      a continuous slope at 0.
+ */
+static double feature(int map, double x)
+{
+    if (map == 1) return x > 0.0 ? x + 1.0 : exp(x);
+    return x > 0.0 ? x : 0.0;
+}
 
 int oracle_num_threads(void)
 {
@@ -123,7 +135,7 @@ static void softmax_block_row(const double* qi, const double* kb, const double* 
  */
 void oracle_step(const double* q, const double* k, const double* v, const double* S,
                  const int32_t* slots, const int32_t* blk_lens, double* out,
-                 int n_req, int n_slots, int H, int blk, int d, double scale)
+                 int n_req, int n_slots, int H, int blk, int d, double scale, int map)
 {
     (void)n_slots;
     const size_t stride = (size_t)H * d;
@@ -143,7 +155,7 @@ void oracle_step(const double* q, const double* k, const double* v, const double
                 /* linear part: phi(q_i) S, S summarising the previous blocks */
                 for (int c = 0; c < d; ++c) {
                     double lin = 0.0;
-                    for (int f = 0; f < d; ++f) lin += phi(qi[f]) * Su[(size_t)f * d + c];
+                    for (int f = 0; f < d; ++f) lin += feature(map, qi[f]) * Su[(size_t)f * d + c];
                     acc[c] += lin;
                 }
                 double* oi = out + tok(r, i, h, blk, H, d);
@@ -160,7 +172,7 @@ void oracle_step(const double* q, const double* k, const double* v, const double
  * S[f][c] += sum_{j < Br} phi(K[j][f]) V[j][c], in place.
  */
 void oracle_commit(const double* k, const double* v, double* S, const int32_t* slots,
-                   const int32_t* blk_lens, int n_req, int n_slots, int H, int blk, int d)
+                   const int32_t* blk_lens, int n_req, int n_slots, int H, int blk, int d, int map)
 {
     (void)n_slots;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -172,7 +184,7 @@ void oracle_commit(const double* k, const double* v, double* S, const int32_t* s
                 for (int c = 0; c < d; ++c) {
                     double sum = 0.0;
                     for (int j = 0; j < Br; ++j)
-                        sum += phi(k[tok(r, j, h, blk, H, d) + f]) * v[tok(r, j, h, blk, H, d) + c];
+                        sum += feature(map, k[tok(r, j, h, blk, H, d) + f]) * v[tok(r, j, h, blk, H, d) + c];
                     Su[(size_t)f * d + c] += sum;
                 }
             }
@@ -188,7 +200,7 @@ void oracle_commit(const double* k, const double* v, double* S, const int32_t* s
  * [total][H][d] with request r's tokens at rows cu[r] .. cu[r+1]-1.
  */
 void oracle_prefill(const double* k, const double* v, const int64_t* cu, double* S,
-                    const int32_t* slots, int n_req, int n_slots, int H, int d)
+                    const int32_t* slots, int n_req, int n_slots, int H, int d, int map)
 {
     (void)n_slots;
     const size_t stride = (size_t)H * d;
@@ -202,7 +214,7 @@ void oracle_prefill(const double* k, const double* v, const int64_t* cu, double*
                 const double* kt = k + t * stride + (size_t)h * d;
                 const double* vt = v + t * stride + (size_t)h * d;
                 for (int f = 0; f < d; ++f) {
-                    const double pk = phi(kt[f]);
+                    const double pk = feature(map, kt[f]);
                     for (int c = 0; c < d; ++c) Su[(size_t)f * d + c] += pk * vt[c];
                 }
             }
@@ -222,7 +234,7 @@ void oracle_prefill(const double* k, const double* v, const int64_t* cu, double*
 void oracle_step_recompute(const double* q, const double* k, const double* v,
                            const double* kp, const double* vp, const int64_t* cu,
                            const int32_t* blk_lens, double* out,
-                           int n_req, int H, int blk, int d, double scale)
+                           int n_req, int H, int blk, int d, double scale, int map)
 {
     const size_t stride = (size_t)H * d;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -242,7 +254,7 @@ void oracle_step_recompute(const double* q, const double* k, const double* v,
                 for (int64_t t = 0; t < P; ++t) {
                     const double* kt = kp + (cu[r] + t) * stride + h * d;
                     double dot = 0.0;
-                    for (int f = 0; f < d; ++f) dot += phi(qi[f]) * phi(kt[f]);
+                    for (int f = 0; f < d; ++f) dot += feature(map, qi[f]) * feature(map, kt[f]);
                     a[t] = dot;
                 }
                 /* times V_p */
@@ -321,7 +333,7 @@ void oracle_exact_step(const double* q, const double* k, const double* v,
  */
 void oracle_step_norm(const double* q, const double* k, const double* v, const double* S, const double* z,
                       const int32_t* slots, const int32_t* blk_lens, double* out,
-                      int n_req, int n_slots, int H, int blk, int d, double scale)
+                      int n_req, int n_slots, int H, int blk, int d, double scale, int map)
 {
     (void)n_slots;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -354,11 +366,11 @@ void oracle_step_norm(const double* q, const double* k, const double* v, const d
                 /* prefix: phi(q_i) S over the numerator, phi(q_i) . z over the denominator */
                 const double em = exp(-m);
                 double qz = 0.0;
-                for (int f = 0; f < d; ++f) qz += phi(qi[f]) * zu[f];
+                for (int f = 0; f < d; ++f) qz += feature(map, qi[f]) * zu[f];
                 den += em * qz;
                 for (int c = 0; c < d; ++c) {
                     double lin = 0.0;
-                    for (int f = 0; f < d; ++f) lin += phi(qi[f]) * Su[(size_t)f * d + c];
+                    for (int f = 0; f < d; ++f) lin += feature(map, qi[f]) * Su[(size_t)f * d + c];
                     oi[c] = (oi[c] + em * lin) / den;
                 }
             }
@@ -369,7 +381,7 @@ void oracle_step_norm(const double* q, const double* k, const double* v, const d
 
 /* [N] Commit of the normaliser state: z[f] += sum_{j < Br} phi(K[j][f]). */
 void oracle_znorm_commit(const double* k, double* z, const int32_t* slots, const int32_t* blk_lens,
-                         int n_req, int n_slots, int H, int blk, int d)
+                         int n_req, int n_slots, int H, int blk, int d, int map)
 {
     (void)n_slots;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -379,7 +391,7 @@ void oracle_znorm_commit(const double* k, double* z, const int32_t* slots, const
             double* zu = z + ((size_t)slots[r] * H + h) * d;
             for (int f = 0; f < d; ++f) {
                 double sum = 0.0;
-                for (int j = 0; j < Br; ++j) sum += phi(k[tok(r, j, h, blk, H, d) + f]);
+                for (int j = 0; j < Br; ++j) sum += feature(map, k[tok(r, j, h, blk, H, d) + f]);
                 zu[f] += sum;
             }
         }
@@ -388,7 +400,7 @@ void oracle_znorm_commit(const double* k, double* z, const int32_t* slots, const
 
 /* [N] Prefill of the normaliser state: z[f] = sum_{t < L_r} phi(K[t][f]). */
 void oracle_znorm_prefill(const double* k, const int64_t* cu, double* z, const int32_t* slots,
-                          int n_req, int n_slots, int H, int d)
+                          int n_req, int n_slots, int H, int d, int map)
 {
     (void)n_slots;
     const size_t stride = (size_t)H * d;
@@ -399,7 +411,7 @@ void oracle_znorm_prefill(const double* k, const int64_t* cu, double* z, const i
             for (int f = 0; f < d; ++f) zu[f] = 0.0;
             for (int64_t t = cu[r]; t < cu[r + 1]; ++t) {
                 const double* kt = k + t * stride + (size_t)h * d;
-                for (int f = 0; f < d; ++f) zu[f] += phi(kt[f]);
+                for (int f = 0; f < d; ++f) zu[f] += feature(map, kt[f]);
             }
         }
     }
@@ -415,7 +427,7 @@ void oracle_znorm_prefill(const double* k, const int64_t* cu, double* z, const i
 void oracle_step_norm_recompute(const double* q, const double* k, const double* v,
                                 const double* kp, const double* vp, const int64_t* cu,
                                 const int32_t* blk_lens, double* out,
-                                int n_req, int H, int blk, int d, double scale)
+                                int n_req, int H, int blk, int d, double scale, int map)
 {
     const size_t stride = (size_t)H * d;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -438,7 +450,7 @@ void oracle_step_norm_recompute(const double* q, const double* k, const double* 
                 for (int64_t t = 0; t < P; ++t) {
                     const double* kt = kp + (cu[r] + t) * stride + h * d;
                     double dot = 0.0;
-                    for (int f = 0; f < d; ++f) dot += phi(qi[f]) * phi(kt[f]);
+                    for (int f = 0; f < d; ++f) dot += feature(map, qi[f]) * feature(map, kt[f]);
                     w[Br + t] = exp(-m) * dot;
                 }
                 double den = 0.0;

@@ -25,13 +25,14 @@
 
 #include "../../include/hybrid_attn.h"
 
+/* the last argument selects the feature map; 0 is ReLU */
 void oracle_step(const double* q, const double* k, const double* v, const double* S, const int32_t* slots,
                  const int32_t* blk_lens, double* out, int n_req, int n_slots, int H, int blk, int d,
-                 double scale);
+                 double scale, int map);
 void oracle_commit(const double* k, const double* v, double* S, const int32_t* slots, const int32_t* blk_lens,
-                   int n_req, int n_slots, int H, int blk, int d);
+                   int n_req, int n_slots, int H, int blk, int d, int map);
 void oracle_prefill(const double* k, const double* v, const int64_t* cu, double* S, const int32_t* slots,
-                    int n_req, int n_slots, int H, int d);
+                    int n_req, int n_slots, int H, int d, int map);
 
 enum { N_REQ = 3, N_SLOTS = 4, H = 2, D = 128, BLK = 48, CHUNK = 256 };
 static const int32_t kSlots[N_REQ] = {2, 0, 3};
@@ -179,7 +180,7 @@ int main(void)
     HIP_CHECK(hipDeviceSynchronize());
     HIP_CHECK(hipMemcpy(st, dst, st_elems * 4, hipMemcpyDeviceToHost));
     state_to_oracle(st0, Sref);
-    oracle_prefill(pk, pv, cu, Sref, kSlots, N_REQ, N_SLOTS, H, D);
+    oracle_prefill(pk, pv, cu, Sref, kSlots, N_REQ, N_SLOTS, H, D, 0);
     state_to_oracle(st, S);
     check("prefill: state", S, Sref, st_elems);
     if (memcmp(st + (size_t)1 * H * D * D, st0 + (size_t)1 * H * D * D, (size_t)H * D * D * 4) != 0) {
@@ -195,7 +196,7 @@ int main(void)
                               NULL));
     HIP_CHECK(hipDeviceSynchronize());
     HIP_CHECK(hipMemcpy(hout, dout, blk_elems * 2, hipMemcpyDeviceToHost));
-    oracle_step(q, k, v, S, kSlots, kLens, ref, N_REQ, N_SLOTS, H, BLK, D, (double)scale);
+    oracle_step(q, k, v, S, kSlots, kLens, ref, N_REQ, N_SLOTS, H, BLK, D, (double)scale, 0);
     int untouched = 1;
     for (int r = 0; r < N_REQ; ++r)
         for (int i = 0; i < BLK; ++i)
@@ -217,7 +218,7 @@ int main(void)
     HA_CHECK(hybrid_state_commit(dk, dv, dst, dslots, dlens, N_REQ, N_SLOTS, H, BLK, D, HA_BF16, NULL));
     HIP_CHECK(hipDeviceSynchronize());
     memcpy(Sref, S, st_elems * 8);
-    oracle_commit(k, v, Sref, kSlots, kLens, N_REQ, N_SLOTS, H, BLK, D);
+    oracle_commit(k, v, Sref, kSlots, kLens, N_REQ, N_SLOTS, H, BLK, D, 0);
     HIP_CHECK(hipMemcpy(st, dst, st_elems * 4, hipMemcpyDeviceToHost));
     state_to_oracle(st, S);
     check("commit: state", S, Sref, st_elems);

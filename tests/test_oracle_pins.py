@@ -466,3 +466,131 @@ def test_znorm_is_sum_of_relu_keys_in_any_order():
     lens = np.array([2], dtype=np.int32)                 # ragged block: rows past B_r are not read
     zr = oracle.znorm_commit(blocks[0], np.zeros((1, H, d)), blk_lens=lens)
     np.testing.assert_allclose(zr[0], relu(blocks[0][0, :2]).sum(0), rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# The ELU + 1 feature map (phi(x) = x + 1 for x > 0, e^x otherwise), pinned to
+# torch's ELU (a library routine), closed forms and the same invariants
+# --------------------------------------------------------------------------
+
+def elu1_lib(x):
+    """torch.nn.functional.elu(x) + 1 in fp64 (the library's ELU, alpha = 1)."""
+    return torch.nn.functional.elu(torch.from_numpy(np.asarray(x, dtype=np.float64))).numpy() + 1.0
+
+
+def test_elu1_map_closed_forms():
+    """phi(0) = 1 (ReLU: 0), phi(x) = x + 1 above 0, e^x below: one query row
+    against a state whose row f is e_f scaled, so the linear part reads phi
+    back feature by feature."""
+    d = 6
+    q = np.array([0.0, 2.5, -1.0, -40.0, 1e-9, -1e-9]).reshape(1, 1, 1, d)
+    S = np.eye(d).reshape(1, 1, d, d) * 3.0
+    o = oracle.step(q, q, np.zeros_like(q), S, phi="elu1")
+    expect = 3.0 * np.array([1.0, 3.5, math.exp(-1.0), math.exp(-40.0), 1.0 + 1e-9, math.exp(-1e-9)])
+    np.testing.assert_allclose(o[0, 0, 0], expect, rtol=1e-15, atol=0)
+    o_relu = oracle.step(q, q, np.zeros_like(q), S, phi="relu")
+    np.testing.assert_allclose(o_relu[0, 0, 0], 3.0 * np.maximum(q[0, 0, 0], 0.0), rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("d", [2, 16, 64])
+def test_elu1_zero_values_is_library_elu_times_S(d):
+    """V_a = 0 with phi = ELU + 1: the linear term is (elu(Q_a) + 1) @ S
+    (torch ELU, numpy matmul); the scale does not touch it."""
+    n, blk, H = 2, 5, 2
+    q, k = rnd(n, blk, H, d), rnd(n, blk, H, d)
+    S = rnd(n, H, d, d)
+    o = oracle.step(q, k, np.zeros_like(q), S, scale=0.1, phi="elu1")
+    for r in range(n):
+        for h in range(H):
+            np.testing.assert_allclose(o[r, :, h], elu1_lib(q[r, :, h]) @ S[r, h], rtol=1e-12, atol=1e-12)
+
+
+def test_elu1_zero_queries_give_column_sums_of_S():
+    """Q_a = 0: phi(0) = 1 for every feature, so the linear part is the sum of
+    S's rows (and the softmax part the mean of the valid values)."""
+    n, blk, H, d = 1, 6, 2, 5
+    k, v = rnd(n, blk, H, d), rnd(n, blk, H, d)
+    S = rnd(n, H, d, d)
+    o = oracle.step(np.zeros((n, blk, H, d)), k, v, S, phi="elu1")
+    for h in range(H):
+        expect = v[0, :, h].mean(axis=0) + S[0, h].sum(axis=0)
+        np.testing.assert_allclose(o[0, :, h], np.broadcast_to(expect, (blk, d)), rtol=1e-12, atol=1e-12)
+
+
+def test_elu1_empty_prefix_is_sdpa():
+    """The map does not touch the softmax part: S = 0 gives SDPA."""
+    n, blk, H, d = 2, 7, 3, 8
+    q, k, v = rnd(n, blk, H, d), rnd(n, blk, H, d), rnd(n, blk, H, d)
+    o = oracle.step(q, k, v, np.zeros((n, H, d, d)), scale=0.3, phi="elu1")
+    np.testing.assert_allclose(o, sdpa64(q, k, v, 0.3), rtol=1e-12, atol=1e-12)
+
+
+def test_elu1_commit_and_prefill_are_library_products():
+    """One committed token: S += outer(elu(k) + 1, v); a prefill is
+    (elu(K) + 1)^T V over the prompt (torch ELU, numpy outer/matmul)."""
+    d, H = 6, 2
+    k, v = rnd(1, 1, H, d), rnd(1, 1, H, d)
+    S0 = rnd(1, H, d, d)
+    S = oracle.commit(k, v, S0, phi="elu1")
+    for h in range(H):
+        np.testing.assert_allclose(S[0, h], S0[0, h] + np.outer(elu1_lib(k[0, 0, h]), v[0, 0, h]),
+                                   rtol=1e-13, atol=1e-13)
+    lens = [0, 1, 9, 30]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    kp, vp = rnd(cu[-1], H, d), rnd(cu[-1], H, d)
+    Sp = oracle.prefill(kp, vp, cu, phi="elu1")
+    for r in range(4):
+        for h in range(H):
+            kk, vv = kp[cu[r]:cu[r + 1], h], vp[cu[r]:cu[r + 1], h]
+            np.testing.assert_allclose(Sp[r, h], elu1_lib(kk).T @ vv, rtol=1e-12, atol=1e-12)
+    assert np.all(Sp[0] == 0.0)
+
+
+def test_elu1_state_form_equals_formula_form_all_tiny_sizes():
+    """The method's associativity with phi = ELU + 1: phi(Q)(phi(K_p)^T V_p) ==
+    (phi(Q) phi(K_p)^T) V_p, for every B <= 3, d <= 3 and prefix <= 5, with the
+    prefix folded by prefill and by commits in any order."""
+    worst = 0.0
+    for blk, d, P in itertools.product(range(1, 4), range(1, 4), range(0, 6)):
+        H = 2
+        q, k, v = rnd(1, blk, H, d), rnd(1, blk, H, d), rnd(1, blk, H, d)
+        kp, vp = rnd(P, H, d), rnd(P, H, d)
+        S = oracle.prefill(kp, vp, [0, P], phi="elu1")
+        a = oracle.step(q, k, v, S, phi="elu1")
+        b = oracle.step_recompute(q, k, v, kp, vp, [0, P], phi="elu1")
+        worst = max(worst, float(np.abs(a - b).max()) / max(1.0, float(np.abs(b).max())))
+        Sc = np.zeros((1, H, d, d))
+        for t in RNG.permutation(P):
+            Sc = oracle.commit(kp[None, t:t + 1], vp[None, t:t + 1], Sc, phi="elu1")
+        np.testing.assert_allclose(Sc, S, rtol=1e-12, atol=1e-12)
+    assert worst <= 1e-12
+
+
+def test_elu1_normalised_variant():
+    """Normalised with phi = ELU + 1: z is sum(elu(k) + 1) over the prompt
+    (torch ELU); the state form equals the per-key form over all tiny sizes;
+    phi > 0, so the denominator stays positive for all-negative inputs."""
+    H, d = 2, 4
+    lens = [0, 3, 11]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    kp, vp = rnd(cu[-1], H, d), rnd(cu[-1], H, d)
+    z = oracle.znorm_prefill(kp, cu, phi="elu1")
+    for r in range(3):
+        np.testing.assert_allclose(z[r], elu1_lib(kp[cu[r]:cu[r + 1]]).sum(axis=0), rtol=1e-13, atol=1e-13)
+    z1 = oracle.znorm_commit(kp[None, :5], np.zeros((1, H, d)), phi="elu1")
+    np.testing.assert_allclose(z1[0], elu1_lib(kp[:5]).sum(axis=0), rtol=1e-13, atol=1e-13)
+    for blk, dd, P in itertools.product(range(1, 4), range(1, 4), range(0, 5)):
+        q, k, v = rnd(1, blk, 1, dd), rnd(1, blk, 1, dd), rnd(1, blk, 1, dd)
+        kk, vv = rnd(P, 1, dd), rnd(P, 1, dd)
+        S = oracle.prefill(kk, vv, [0, P], phi="elu1")
+        zz = oracle.znorm_prefill(kk, [0, P], phi="elu1")
+        a = oracle.step_norm(q, k, v, S, zz, phi="elu1")
+        b = oracle.step_norm_recompute(q, k, v, kk, vv, [0, P], phi="elu1")
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    qn = -np.abs(rnd(1, 4, 1, 3)) - 5.0
+    kn = -np.abs(rnd(6, 1, 3)) - 5.0
+    S = oracle.prefill(kn, rnd(6, 1, 3), [0, 6], phi="elu1")
+    zz = oracle.znorm_prefill(kn, [0, 6], phi="elu1")
+    assert np.all(zz > 0)
+    o = oracle.step_norm(qn, qn, rnd(1, 4, 1, 3), S, zz, phi="elu1")
+    assert np.all(np.isfinite(o))

@@ -18,6 +18,12 @@ denominator, with z = sum ReLU(k) next to S):
     hybrid_attn_step_norm, hybrid_attn_step_commit_norm,
     hybrid_state_commit_norm, hybrid_state_prefill_norm
 
+the same calls with the feature map as an argument (ReLU, the worked
+example's, or ELU + 1), plain or normalised by whether z is given:
+
+    hybrid_attn_step_phi, hybrid_attn_step_commit_phi,
+    hybrid_state_commit_phi, hybrid_state_prefill_phi
+
 the prefill for callers that cannot allocate (its workspace is the library's
 own device scratch):
 
@@ -31,7 +37,8 @@ and, for comparison, the exact step the method replaces:
 PyTorch only provides device memory and streams.
 """
 from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_attn_step_commit,
-                      hybrid_attn_step_commit_norm, hybrid_attn_step_norm, hybrid_exact_step,
+                      hybrid_attn_step_commit_norm, hybrid_attn_step_commit_phi, hybrid_attn_step_norm,
+                      hybrid_attn_step_phi, hybrid_exact_step, hybrid_state_commit_phi, hybrid_state_prefill_phi,
                       hybrid_exact_step_workspace_bytes, hybrid_state_commit, hybrid_state_commit_norm,
                       hybrid_state_prefill, hybrid_state_prefill_noalloc, hybrid_state_prefill_norm,
                       hybrid_state_prefill_workspace_bytes,
@@ -39,7 +46,8 @@ from .binding import (HybridAttnError, abi_version, hybrid_attn_step, hybrid_att
                       prepare_step, prepare_step_commit, prepare_step_commit_norm, prepare_step_norm)
 
 __all__ = ["HybridAttnError", "abi_version", "hybrid_attn_step", "hybrid_attn_step_commit",
-           "hybrid_attn_step_commit_norm", "hybrid_attn_step_norm", "hybrid_exact_step",
+           "hybrid_attn_step_commit_norm", "hybrid_attn_step_commit_phi", "hybrid_attn_step_norm",
+           "hybrid_attn_step_phi", "hybrid_exact_step", "hybrid_state_commit_phi", "hybrid_state_prefill_phi",
            "hybrid_exact_step_workspace_bytes", "hybrid_state_commit", "hybrid_state_commit_norm",
            "hybrid_state_prefill", "hybrid_state_prefill_noalloc", "hybrid_state_prefill_norm",
            "hybrid_state_prefill_workspace_bytes",

@@ -19,6 +19,8 @@ from .build import LIB as LIB_PATH
 
 HA_OK, HA_ERR_INVALID_ARG, HA_ERR_UNSUPPORTED, HA_ERR_HIP = 0, 1, 2, 3
 HA_F32, HA_BF16 = 0, 1
+HA_PHI_RELU, HA_PHI_ELU1 = 0, 1
+FEATURE_MAPS = {"relu": HA_PHI_RELU, "elu1": HA_PHI_ELU1}
 MAX_BLK = 256
 EXACT_MAX_BLK = 128
 
@@ -63,6 +65,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.hybrid_state_commit_norm.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
         lib.hybrid_state_prefill_norm.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp,
                                                   sz, ctypes.c_int, vp]
+        lib.hybrid_attn_step_phi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                             ctypes.c_int, ctypes.c_int, vp]
+        lib.hybrid_attn_step_commit_phi.argtypes = lib.hybrid_attn_step_phi.argtypes
+        lib.hybrid_state_commit_phi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                                ctypes.c_int, vp]
+        lib.hybrid_state_prefill_phi.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i32, vp, sz,
+                                                 ctypes.c_int, ctypes.c_int, vp]
+        for fn in (lib.hybrid_attn_step_phi, lib.hybrid_attn_step_commit_phi, lib.hybrid_state_commit_phi,
+                   lib.hybrid_state_prefill_phi):
+            fn.restype = ctypes.c_int
         for fn in (lib.hybrid_attn_step, lib.hybrid_state_commit, lib.hybrid_state_prefill, lib.hybrid_exact_step,
                    lib.hybrid_attn_step_commit, lib.hybrid_attn_step_norm, lib.hybrid_attn_step_commit_norm,
                    lib.hybrid_state_commit_norm, lib.hybrid_state_prefill_norm, lib.hybrid_state_prefill_noalloc):
@@ -455,3 +467,62 @@ def prepare_prefill_norm(k, v, cu_seqlens, state, z, slots, max_len=None, chunk=
             _check("hybrid_state_prefill_norm", st)
     run.workspace = ws
     return run
+
+
+# ---------------------------------------------------------------------------
+# The calls with the feature map as an argument ("relu" or "elu1"); z = None
+# gives the plain sum, a z tensor [n_slots, H, d] the normalised variant.
+
+def _phi_code(phi) -> int:
+    if isinstance(phi, str):
+        if phi not in FEATURE_MAPS:
+            raise ValueError(f"unknown feature map {phi!r} (one of {sorted(FEATURE_MAPS)})")
+        return FEATURE_MAPS[phi]
+    return int(phi)
+
+
+def _opt_z(z, state):
+    return None if z is None else _check_z(z, state)
+
+
+def hybrid_attn_step_phi(q, k, v, state, slots, phi, z=None, out=None, blk_lens=None, scale=None, stream=None):
+    """hybrid_attn_step (z = None) or hybrid_attn_step_norm (z given) with the
+    feature map ``phi`` ("relu" or "elu1")."""
+    if out is None:
+        with _on_stream(stream):
+            out = torch.zeros_like(q)
+    a = _step_args(q, k, v, state, slots, out, blk_lens, scale)
+    args = a[:4] + (_opt_z(z, state),) + a[4:13] + (_phi_code(phi), a[13])
+    _check("hybrid_attn_step_phi", load_library().hybrid_attn_step_phi(*args, _stream(stream)))
+    return out
+
+
+def hybrid_attn_step_commit_phi(q, k, v, state, slots, phi, z=None, out=None, blk_lens=None, scale=None,
+                                stream=None):
+    """The step from the current state, then state (and z) updated by the
+    block, with the feature map ``phi``.  Requests must use distinct slots."""
+    if out is None:
+        with _on_stream(stream):
+            out = torch.zeros_like(q)
+    a = _step_args(q, k, v, state, slots, out, blk_lens, scale)
+    args = a[:4] + (_opt_z(z, state),) + a[4:13] + (_phi_code(phi), a[13])
+    _check("hybrid_attn_step_commit_phi", load_library().hybrid_attn_step_commit_phi(*args, _stream(stream)))
+    return out
+
+
+def hybrid_state_commit_phi(k, v, state, slots, phi, z=None, blk_lens=None, stream=None):
+    """state[slots] += phi(K)^T V (and z += sum phi(k) when z is given)."""
+    a = _commit_args(k, v, state, slots, blk_lens)
+    args = a[:3] + (_opt_z(z, state),) + a[3:10] + (_phi_code(phi), a[10])
+    _check("hybrid_state_commit_phi", load_library().hybrid_state_commit_phi(*args, _stream(stream)))
+    return state
+
+
+def hybrid_state_prefill_phi(k, v, cu_seqlens, state, slots, phi, z=None, max_len=None, chunk=256, workspace=None,
+                             stream=None):
+    """state[slots[r]] (and z[slots[r]]) overwritten by the sums over prompt r
+    of phi(k_t)^T v_t (and phi(k_t)), with the feature map ``phi``."""
+    a, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace, stream)
+    args = a[:6] + (_opt_z(z, state),) + a[6:14] + (_phi_code(phi), a[14])
+    _check("hybrid_state_prefill_phi", load_library().hybrid_state_prefill_phi(*args, _stream(stream)))
+    return state

@@ -82,12 +82,16 @@ namespace {
 
 // The step, the fused step + commit, the commit and the prefill, with z =
 // NULL for the plain sum and z non-NULL for the normalised variant.
+bool known_map(int phi) { return phi == HA_PHI_RELU || phi == HA_PHI_ELU1; }
+
 ha_status step_impl(const char* fn, const void* q, const void* k, const void* v, const float* state, float* z,
                     const int32_t* slots, void* out, const int32_t* blk_lens, int32_t n_req, int32_t n_slots,
-                    int32_t heads, int32_t blk, int32_t d, float scale, ha_dtype dtype, void* stream, bool norm)
+                    int32_t heads, int32_t blk, int32_t d, float scale, ha_dtype dtype, void* stream, bool norm,
+                    int phi = HA_PHI_RELU)
 {
     ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
     if (st != HA_OK) return st;
+    if (!known_map(phi)) return fail(HA_ERR_UNSUPPORTED, "%s: unknown feature map %d", fn, phi);
     if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
     if (n_req == 0) return HA_OK;
     if (!q || !k || !v || !state || !slots || !out || (norm && !z))
@@ -95,17 +99,18 @@ ha_status step_impl(const char* fn, const void* q, const void* k, const void* v,
                     norm ? ", z" : "");
     if ((st = check_aligned(fn, {q, k, v, state, out, z}, nullptr)) != HA_OK) return st;
     ha::StepArgs a{q, k, v, state, nullptr, slots, out, blk_lens, z, n_req, n_slots, heads, blk, d, scale,
-                   dtype == HA_BF16};
+                   dtype == HA_BF16, phi};
     return hip_status(ha::launch_step(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 ha_status step_commit_impl(const char* fn, const void* q, const void* k, const void* v, float* state, float* z,
                            const int32_t* slots, void* out, const int32_t* blk_lens, int32_t n_req,
                            int32_t n_slots, int32_t heads, int32_t blk, int32_t d, float scale, ha_dtype dtype,
-                           void* stream, bool norm)
+                           void* stream, bool norm, int phi = HA_PHI_RELU)
 {
     ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
     if (st != HA_OK) return st;
+    if (!known_map(phi)) return fail(HA_ERR_UNSUPPORTED, "%s: unknown feature map %d", fn, phi);
     if (!std::isfinite(scale)) return fail(HA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
     if (n_req == 0) return HA_OK;
     if (!q || !k || !v || !state || !slots || !out || (norm && !z))
@@ -113,16 +118,17 @@ ha_status step_commit_impl(const char* fn, const void* q, const void* k, const v
                     norm ? ", z" : "");
     if ((st = check_aligned(fn, {q, k, v, state, out, z}, nullptr)) != HA_OK) return st;
     ha::StepArgs a{q, k, v, state, state, slots, out, blk_lens, z, n_req, n_slots, heads, blk, d, scale,
-                   dtype == HA_BF16};
+                   dtype == HA_BF16, phi};
     return hip_status(ha::launch_step_commit(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 ha_status commit_impl(const char* fn, const void* k, const void* v, float* state, float* z, const int32_t* slots,
                       const int32_t* blk_lens, int32_t n_req, int32_t n_slots, int32_t heads, int32_t blk,
-                      int32_t d, ha_dtype dtype, void* stream, bool norm)
+                      int32_t d, ha_dtype dtype, void* stream, bool norm, int phi = HA_PHI_RELU)
 {
     ha_status st = check_block_call(fn, n_req, n_slots, heads, blk, d, dtype);
     if (st != HA_OK) return st;
+    if (!known_map(phi)) return fail(HA_ERR_UNSUPPORTED, "%s: unknown feature map %d", fn, phi);
     if (n_req == 0) return HA_OK;
     if (!k || !v || !state || !slots || (norm && !z))
         return fail(HA_ERR_INVALID_ARG, "%s: k, v, state%s and slots must be non-NULL", fn, norm ? ", z" : "");
@@ -139,10 +145,11 @@ ha_status commit_impl(const char* fn, const void* k, const void* v, float* state
     a.blk = blk;
     a.d = d;
     a.dtype_bf16 = dtype == HA_BF16;
+    a.phi = phi;
     hipError_t e = ha::launch_commit(a, static_cast<hipStream_t>(stream));
     if (e == hipSuccess && norm) {
         ha::StepArgs zc{nullptr, k, v, nullptr, nullptr, slots, nullptr, blk_lens, z, n_req, n_slots, heads, blk,
-                        d, 0.f, dtype == HA_BF16};
+                        d, 0.f, dtype == HA_BF16, phi};
         e = ha::launch_znorm_commit(zc, static_cast<hipStream_t>(stream));
     }
     return hip_status(e, fn);
@@ -157,8 +164,9 @@ size_t prefill_slots(int32_t n_req, int32_t heads, int32_t d)
 ha_status prefill_check(const char* fn, const void* k, const void* v, const int64_t* cu_seqlens,
                         int64_t total_tokens, int64_t max_len, float* state, float* z, const int32_t* slots,
                         int32_t n_req, int32_t n_slots, int32_t heads, int32_t d, int32_t chunk, ha_dtype dtype,
-                        bool norm)
+                        bool norm, int phi = HA_PHI_RELU)
 {
+    if (!known_map(phi)) return fail(HA_ERR_UNSUPPORTED, "%s: unknown feature map %d", fn, phi);
     if (n_req < 0) return fail(HA_ERR_INVALID_ARG, "%s: n_req must be >= 0 (got %d)", fn, n_req);
     if (n_slots <= 0) return fail(HA_ERR_INVALID_ARG, "%s: n_slots must be > 0 (got %d)", fn, n_slots);
     if (heads <= 0) return fail(HA_ERR_INVALID_ARG, "%s: heads must be > 0 (got %d)", fn, heads);
@@ -181,10 +189,10 @@ ha_status prefill_check(const char* fn, const void* k, const void* v, const int6
 ha_status prefill_impl(const char* fn, const void* k, const void* v, const int64_t* cu_seqlens,
                        int64_t total_tokens, int64_t max_len, float* state, float* z, const int32_t* slots,
                        int32_t n_req, int32_t n_slots, int32_t heads, int32_t d, int32_t chunk, void* workspace,
-                       size_t workspace_bytes, ha_dtype dtype, void* stream, bool norm)
+                       size_t workspace_bytes, ha_dtype dtype, void* stream, bool norm, int phi = HA_PHI_RELU)
 {
     if (ha_status st = prefill_check(fn, k, v, cu_seqlens, total_tokens, max_len, state, z, slots, n_req, n_slots,
-                                     heads, d, chunk, dtype, norm);
+                                     heads, d, chunk, dtype, norm, phi);
         st != HA_OK || n_req == 0)
         return st;
     const size_t need = hybrid_state_prefill_workspace_bytes(n_req, heads, d, total_tokens, max_len, chunk);
@@ -212,6 +220,7 @@ ha_status prefill_impl(const char* fn, const void* k, const void* v, const int64
     a.heads = heads;
     a.d = d;
     a.dtype_bf16 = dtype == HA_BF16;
+    a.phi = phi;
     return hip_status(ha::launch_prefill(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -365,6 +374,41 @@ ha_status hybrid_state_prefill_norm(const void* k, const void* v, const int64_t*
 {
     return prefill_impl("hybrid_state_prefill_norm", k, v, cu_seqlens, total_tokens, max_len, state, z, slots,
                         n_req, n_slots, heads, d, chunk, workspace, workspace_bytes, dtype, stream, true);
+}
+
+ha_status hybrid_attn_step_phi(const void* q, const void* k, const void* v, const float* state, const float* z,
+                               const int32_t* slots, void* out, const int32_t* blk_lens, int32_t n_req,
+                               int32_t n_slots, int32_t heads, int32_t blk, int32_t d, float scale,
+                               ha_feature_map phi, ha_dtype dtype, void* stream)
+{
+    return step_impl("hybrid_attn_step_phi", q, k, v, state, const_cast<float*>(z), slots, out, blk_lens, n_req,
+                     n_slots, heads, blk, d, scale, dtype, stream, z != nullptr, (int)phi);
+}
+
+ha_status hybrid_attn_step_commit_phi(const void* q, const void* k, const void* v, float* state, float* z,
+                                      const int32_t* slots, void* out, const int32_t* blk_lens, int32_t n_req,
+                                      int32_t n_slots, int32_t heads, int32_t blk, int32_t d, float scale,
+                                      ha_feature_map phi, ha_dtype dtype, void* stream)
+{
+    return step_commit_impl("hybrid_attn_step_commit_phi", q, k, v, state, z, slots, out, blk_lens, n_req, n_slots,
+                            heads, blk, d, scale, dtype, stream, z != nullptr, (int)phi);
+}
+
+ha_status hybrid_state_commit_phi(const void* k, const void* v, float* state, float* z, const int32_t* slots,
+                                  const int32_t* blk_lens, int32_t n_req, int32_t n_slots, int32_t heads,
+                                  int32_t blk, int32_t d, ha_feature_map phi, ha_dtype dtype, void* stream)
+{
+    return commit_impl("hybrid_state_commit_phi", k, v, state, z, slots, blk_lens, n_req, n_slots, heads, blk, d,
+                       dtype, stream, z != nullptr, (int)phi);
+}
+
+ha_status hybrid_state_prefill_phi(const void* k, const void* v, const int64_t* cu_seqlens, int64_t total_tokens,
+                                   int64_t max_len, float* state, float* z, const int32_t* slots, int32_t n_req,
+                                   int32_t n_slots, int32_t heads, int32_t d, int32_t chunk, void* workspace,
+                                   size_t workspace_bytes, ha_feature_map phi, ha_dtype dtype, void* stream)
+{
+    return prefill_impl("hybrid_state_prefill_phi", k, v, cu_seqlens, total_tokens, max_len, state, z, slots, n_req,
+                        n_slots, heads, d, chunk, workspace, workspace_bytes, dtype, stream, z != nullptr, (int)phi);
 }
 
 size_t hybrid_exact_step_workspace_bytes(int32_t n_req, int32_t heads, int32_t blk, int32_t d)

@@ -49,6 +49,8 @@ __device__ __forceinline__ u16x8 relu_bf16x8(u16x8 x) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
 
+
+
 // Split 8 fp32 values into bf16 hi + lo with hi + lo == x to about 2^-17
 // relative (hi = RNE(x), lo = RNE(x - hi)); bf16 x bf16 products are exact in
 // fp32, so two matrix-core passes reproduce fp32 operands to ~16 bits.
@@ -61,6 +63,44 @@ __device__ __forceinline__ void split_hi_lo(const float* x, bf16x8& hi, bf16x8& 
     }
     hi = as_bf16x8(h);
     lo = as_bf16x8(l);
+}
+
+// Feature maps phi (the ha_feature_map values): 0 = ReLU, the worked
+// example's map; 1 = ELU + 1, phi(x) = x + 1 for x > 0 and e^x otherwise.
+template <int M>
+__device__ __forceinline__ float phi_of(float x)
+{
+    if constexpr (M == 1) return x > 0.f ? x + 1.f : expf(x);
+    else return x > 0.f ? x : 0.f;
+}
+
+__device__ __forceinline__ float phi_rt(int map, float x) { return map == 1 ? phi_of<1>(x) : phi_of<0>(x); }
+
+// phi of 8 packed bf16 as a matrix-core operand: ReLU of a bf16 is a bf16
+// (hi only, kExact); ELU + 1 is computed in fp32 and split into hi + lo bf16
+// (the caller adds the lo pass), and f keeps the fp32 values for sums.
+template <int M>
+struct PhiOp {
+    static constexpr bool kExact = M == 0;
+    bf16x8 hi, lo;
+    float f[8];
+};
+
+template <int M>
+__device__ __forceinline__ PhiOp<M> phi_op(u16x8 x)
+{
+    PhiOp<M> r;
+    if constexpr (M == 0) {
+        const u16x8 y = relu_bf16x8(x);
+        r.hi = as_bf16x8(y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.f[e] = bf16_bits_to_f32(y[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.f[e] = phi_of<1>(bf16_bits_to_f32(x[e]));
+        split_hi_lo(r.f, r.hi, r.lo);
+    }
+    return r;
 }
 
 // The same split for two floats, each result packed as a bf16 pair (element 0

@@ -20,6 +20,7 @@ struct StepArgs {
     int32_t n_req, n_slots, heads, blk, d;
     float scale;
     bool dtype_bf16;
+    int32_t phi;                // feature map: 0 = ReLU, 1 = ELU + 1
 };
 
 // ReLU(K)^T V over token rows, shared by the block commit and prompt prefill.
@@ -47,6 +48,7 @@ struct PhiKVArgs {
     int32_t hp;                 // prefill: heads per unit (1 or 2, divides heads)
     int32_t n_req, n_slots, heads, blk, d;
     bool dtype_bf16;
+    int32_t phi;                // feature map: 0 = ReLU, 1 = ELU + 1
 };
 
 // Heads per prefill unit: bf16 with d = 128 and an even head count streams two

@@ -44,6 +44,10 @@ namespace ha {
 // c = 32 ct + 8 (r/4) + 4 (l/32) + r%4 and f = 32 ft + l%32, so every register
 // of a wave is two 128-byte runs of one state row: coalesced read-modify-write.
 // ---------------------------------------------------------------------------
+// Two bf16 -inf: the key rows that pad a stage (phi(-inf) = 0 for ReLU and
+// for ELU + 1, where a zero key would give phi = 1).
+constexpr uint32_t kPadKeys = 0xFF80FF80u;
+
 template <int D> struct PhiKVShape;
 template <> struct PhiKVShape<128> { static constexpr int NW = 4, T = 64; };
 template <> struct PhiKVShape<64> { static constexpr int NW = 4, T = 128; };
@@ -85,7 +89,7 @@ struct PhiKVTile {
 
 // Adds ReLU(K)^T V over rows [0, nrows) of (kb, vb) (rows rs elements apart)
 // into acc.  nrows >= 1.  Every thread of the workgroup must call it.
-template <int D, int PF>
+template <int D, int PF, int M = 0>
 __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint16_t* vb, int64_t rs,
                                                  int64_t nrows, typename PhiKVTile<D>::Lds& lds,
                                                  f32x16 (&acc)[PhiKVTile<D>::TPW])
@@ -113,11 +117,14 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
             x[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + tc * rs));   // read once
         }
     };
-    // zero rows past the range, transpose the 8x8 bf16 block, write 8 rows
+    // rows past the range: values 0 and keys -inf (phi(-inf) = 0 for every
+    // map, so they add nothing to S or to sums of phi(k)); transpose the 8x8
+    // bf16 block, write 8 rows
+    const uint32_t pad = tensor == 0 ? kPadKeys : 0u;
     auto store_stage = [&](int buf, int64_t t0, const u32x4 (&xin)[8]) {
         u32x4 x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (t0 + tg * 8 + e < nrows) ? xin[e] : u32x4{0, 0, 0, 0};
+        for (int e = 0; e < 8; ++e) x[e] = (t0 + tg * 8 + e < nrows) ? xin[e] : u32x4{pad, pad, pad, pad};
         uint16_t* dst = lds[buf][tensor];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -141,7 +148,9 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
                 const int t = w * TPW + u, ct = t / NT, ft = t % NT;
                 const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(ct * 32 + l32, g));
                 const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(ft * 32 + l32, g));
-                acc[u] = mfma32(as_bf16x8(av), as_bf16x8(relu_bf16x8(bk)), acc[u]);
+                const PhiOp<M> kp = phi_op<M>(bk);           // ELU + 1: hi + lo, two passes
+                acc[u] = mfma32(as_bf16x8(av), kp.hi, acc[u]);
+                if constexpr (!PhiOp<M>::kExact) acc[u] = mfma32(as_bf16x8(av), kp.lo, acc[u]);
             }
         }
     };
@@ -199,7 +208,7 @@ __device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (
 // Commit: one workgroup per (request, head); the accumulators start from the
 // old state tiles, so the matrix cores add ReLU(K)^T V onto S in fp32.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int M = 0>
 __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(PhiKVArgs a)
 {
     using P = PhiKVTile<D>;
@@ -214,8 +223,8 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(Ph
     float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
     f32x16 acc[P::TPW];
     tiles_io<D>(st, acc, false, threadIdx.x / kWave);
-    phikv_accumulate<D, 1>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
-                           Br, lds, acc);
+    phikv_accumulate<D, 1, M>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
+                              Br, lds, acc);
     tiles_io<D>(st, acc, true, threadIdx.x / kWave);
 }
 
@@ -371,7 +380,7 @@ constexpr int prefill_threads() { return (PrefillTile<D, HP>::type::NW + Prefill
 // consecutive token rows, which HBM serves faster than rows 8 apart.  LDS
 // group g holds that permutation of the stage's tokens for K and V alike, so
 // the token reduction is unchanged.
-template <int D, int HP, bool kNorm>
+template <int D, int HP, bool kNorm, int M = 0>
 __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_slices_bf16_mfma(PhiKVArgs a)
 {
     using P = typename PrefillTile<D, HP>::type;
@@ -418,12 +427,14 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
         stage_advance(a, ld, T);
     };
     // The stage buffer is reloaded right after it is stored, so rows past the
-    // piece are zeroed in place (no second copy of the stage in registers).
+    // piece are padded in place (no second copy of the stage in registers):
+    // values 0, keys -inf, whose phi is 0 for every map.
+    const uint32_t pad = tensor == 0 ? kPadKeys : 0u;
     auto store_stage = [&](int buf, int64_t valid, u32x4 (&x)[8]) {
         if (valid < T) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (tg + TG * e >= valid) x[e] = u32x4{0, 0, 0, 0};
+                if (tg + TG * e >= valid) x[e] = u32x4{pad, pad, pad, pad};
         }
         uint16_t* dst = lds[buf][tensor];
 #pragma unroll
@@ -460,18 +471,24 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
             for (int u = 0; u < TPW; ++u) {
                 const int t = w4 * TPW + u, ct = t / NT, ft = t % NT;
                 const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(hw * D + ct * 32 + l32, g));
-                const u16x8 bk = relu_bf16x8(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g)));
-                acc[u] = mfma32(as_bf16x8(av), as_bf16x8(bk), acc[u]);
+                const PhiOp<M> kp = phi_op<M>(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g)));
+                acc[u] = mfma32(as_bf16x8(av), kp.hi, acc[u]);
+                if constexpr (!PhiOp<M>::kExact) acc[u] = mfma32(as_bf16x8(av), kp.lo, acc[u]);   // ELU + 1
                 if constexpr (kNorm && HP == 2) {
                     // head pairs: the z sums from the operand in hand (a second
                     // read as below does not fit in the registers); every wave
                     // sums, only the writer waves' sums are stored
                     if (u < NZ) {
-                        const u32x4 w = __builtin_bit_cast(u32x4, bk);
                         float s8 = 0.f;
+                        if constexpr (M == 0) {
+                            const u32x4 w = __builtin_bit_cast(u32x4, kp.hi);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
+                            for (int e = 0; e < 4; ++e)
+                                s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) s8 += kp.f[2 * e] + kp.f[2 * e + 1];
+                        }
                         zacc[u] += s8;
                     }
                 }
@@ -488,11 +505,17 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
 #pragma unroll
             for (int u = 0; u < NZ; ++u) {
                 const int ft = (w4 * TPW + u) % NT;
-                const u32x4 w = __builtin_bit_cast(
-                    u32x4, relu_bf16x8(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g))));
+                const u16x8 kr = *reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g));
                 float s8 = 0.f;
+                if constexpr (M == 0) {
+                    const u32x4 w = __builtin_bit_cast(u32x4, relu_bf16x8(kr));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
+                    for (int e = 0; e < 4; ++e) s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s8 += phi_of<M>(bf16_bits_to_f32(kr[2 * e])) + phi_of<M>(bf16_bits_to_f32(kr[2 * e + 1]));
+                }
                 zacc[u] += s8;
             }
         }
@@ -580,13 +603,13 @@ __global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
             const int c = e / D, f = e % D;
             float acc = 0.f;
             for (int64_t t = 0; t < t1 - t0; ++t)
-                acc = fmaf(Elem<T>::load(vb, t * rs + c), relu(Elem<T>::load(kb, t * rs + f)), acc);
+                acc = fmaf(Elem<T>::load(vb, t * rs + c), phi_rt(a.phi, Elem<T>::load(kb, t * rs + f)), acc);
             dst[e] = acc;
         }
         if (a.z) {                                       // normalised variant: sum phi(k) of the piece
             for (int f = threadIdx.x; f < D; f += blockDim.x) {
                 float acc = 0.f;
-                for (int64_t t = 0; t < t1 - t0; ++t) acc += relu(Elem<T>::load(kb, t * rs + f));
+                for (int64_t t = 0; t < t1 - t0; ++t) acc += phi_rt(a.phi, Elem<T>::load(kb, t * rs + f));
                 a.zpartial[piece * D + f] = acc;
             }
         }
@@ -658,7 +681,7 @@ __global__ __launch_bounds__(256) void commit_generic(PhiKVArgs a)
         const int c = e / D, f = e % D;
         float acc = 0.f;
         for (int j = 0; j < Br; ++j)
-            acc = fmaf(Elem<T>::load(vb, j * rs + c), relu(Elem<T>::load(kb, j * rs + f)), acc);
+            acc = fmaf(Elem<T>::load(vb, j * rs + c), phi_rt(a.phi, Elem<T>::load(kb, j * rs + f)), acc);
         st[e] += acc;
     }
 }
@@ -668,10 +691,20 @@ hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream)
 {
     const dim3 grid(a.n_req * a.heads);
     if (a.dtype_bf16 && a.d >= 32) {
+        const bool elu = a.phi == 1;
         switch (a.d) {
-        case 32: commit_bf16_mfma<32><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a); break;
-        case 64: commit_bf16_mfma<64><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a); break;
-        default: commit_bf16_mfma<128><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a); break;
+        case 32:
+            if (elu) commit_bf16_mfma<32, 1><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a);
+            else commit_bf16_mfma<32, 0><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a);
+            break;
+        case 64:
+            if (elu) commit_bf16_mfma<64, 1><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a);
+            else commit_bf16_mfma<64, 0><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a);
+            break;
+        default:
+            if (elu) commit_bf16_mfma<128, 1><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+            else commit_bf16_mfma<128, 0><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+            break;
         }
     } else if (a.dtype_bf16) {
         commit_generic<uint16_t><<<grid, 256, 0, stream>>>(a);
@@ -681,18 +714,18 @@ hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <bool kNorm>
+template <bool kNorm, int M>
 static void launch_prefill_slices(const PhiKVArgs& a, dim3 grid, hipStream_t stream)
 {
     switch (a.d) {
-    case 32: prefill_slices_bf16_mfma<32, 1, kNorm><<<grid, prefill_threads<32, 1>(), 0, stream>>>(a); break;
-    case 64: prefill_slices_bf16_mfma<64, 1, kNorm><<<grid, prefill_threads<64, 1>(), 0, stream>>>(a); break;
+    case 32: prefill_slices_bf16_mfma<32, 1, kNorm, M><<<grid, prefill_threads<32, 1>(), 0, stream>>>(a); break;
+    case 64: prefill_slices_bf16_mfma<64, 1, kNorm, M><<<grid, prefill_threads<64, 1>(), 0, stream>>>(a); break;
     default:
         if (a.hp == 2) {
-            prefill_slices_bf16_mfma<128, 2, kNorm><<<grid, prefill_threads<128, 2>(), 0, stream>>>(a);
+            prefill_slices_bf16_mfma<128, 2, kNorm, M><<<grid, prefill_threads<128, 2>(), 0, stream>>>(a);
             break;
         }
-        prefill_slices_bf16_mfma<128, 1, kNorm><<<grid, prefill_threads<128, 1>(), 0, stream>>>(a);
+        prefill_slices_bf16_mfma<128, 1, kNorm, M><<<grid, prefill_threads<128, 1>(), 0, stream>>>(a);
         break;
     }
 }
@@ -705,8 +738,13 @@ hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream)
     if (a.total_tokens > 0) {
         const dim3 grid(a.slices);
         if (a.dtype_bf16 && a.d >= 32) {
-            if (a.z) launch_prefill_slices<true>(a, grid, stream);
-            else launch_prefill_slices<false>(a, grid, stream);
+            if (a.phi == 1) {
+                if (a.z) launch_prefill_slices<true, 1>(a, grid, stream);
+                else launch_prefill_slices<false, 1>(a, grid, stream);
+            } else {
+                if (a.z) launch_prefill_slices<true, 0>(a, grid, stream);
+                else launch_prefill_slices<false, 0>(a, grid, stream);
+            }
         } else if (a.dtype_bf16) {
             prefill_slices_generic<uint16_t><<<grid, 256, 0, stream>>>(a);
         } else {

@@ -81,19 +81,19 @@ __device__ __forceinline__ void norm_weights(float m, float A, float qz, float& 
 // phi(q).z for the query whose staged row starts at qrow (pitch D + 8 bf16)
 // against z staged in LDS: lane half hh sums features [hh D/2, hh D/2 + D/2),
 // then the halves are added (every lane returns its query's full sum).
-template <int D>
+template <int D, int M = 0>
 __device__ __forceinline__ float query_dot_z(const uint16_t* qrow, const float* zl, int hh)
 {
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
         const int f0 = hh * (D / 2) + 8 * c;
-        const u16x8 qv = relu_bf16x8(*reinterpret_cast<const u16x8*>(qrow + f0));
+        const u16x8 qv = *reinterpret_cast<const u16x8*>(qrow + f0);
         const f32x4 z0 = *reinterpret_cast<const f32x4*>(zl + f0), z1 = *reinterpret_cast<const f32x4*>(zl + f0 + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc = fmaf(bf16_bits_to_f32(qv[e]), z0[e], acc);
-            acc = fmaf(bf16_bits_to_f32(qv[4 + e]), z1[e], acc);
+            acc = fmaf(phi_of<M>(bf16_bits_to_f32(qv[e])), z0[e], acc);
+            acc = fmaf(phi_of<M>(bf16_bits_to_f32(qv[4 + e])), z1[e], acc);
         }
     }
     return half_pair_sum(acc);
@@ -108,14 +108,27 @@ __device__ __forceinline__ void stage_z(float* zl, const float* zg, int tid)
 
 // z += sum over the block's first Br staged key rows (pitch PK bf16, row
 // major) of phi(k): thread f < D owns feature f.
-template <int D, int PK = D + 8>
+template <int D, int PK = D + 8, int M = 0>
 __device__ __forceinline__ void commit_z(float* zg, const uint16_t* sk, int Br, int tid)
 {
     if (tid < D) {
         float acc = 0.f;
-        for (int j = 0; j < Br; ++j) acc += relu(bf16_bits_to_f32(sk[j * PK + tid]));
+        for (int j = 0; j < Br; ++j) acc += phi_of<M>(bf16_bits_to_f32(sk[j * PK + tid]));
         zg[tid] += acc;
     }
+}
+
+// One k-step of the linear part, S^T (hi + lo bf16) times phi(Q)^T: two
+// matrix-core passes for ReLU (exact in bf16), three for ELU + 1 (phi(Q) as
+// hi + lo as well; the lo x lo product, ~2^-18 of the term, is dropped).
+template <int M>
+__device__ __forceinline__ f32x16 linear_mfma(f32x16 acc, bf16x8 shi, bf16x8 slo, u16x8 qv)
+{
+    const PhiOp<M> pq = phi_op<M>(qv);
+    acc = mfma32(shi, pq.hi, acc);
+    acc = mfma32(slo, pq.hi, acc);
+    if constexpr (!PhiOp<M>::kExact) acc = mfma32(shi, pq.lo, acc);
+    return acc;
 }
 
 // Softmax part of one 32-query tile whose rows start at qtile in LDS:
@@ -239,7 +252,7 @@ __device__ __forceinline__ void store_tile_global(uint16_t* orow, const f32x16& 
 // Workgroups per XCD group: the NKT query tiles of 8 consecutive units.
 __host__ __device__ inline int step_grid(int units, int nkt) { return (units + 7) / 8 * 8 * nkt; }
 
-template <int D, int NKT, bool kNorm>
+template <int D, int NKT, bool kNorm, int M = 0>
 __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 {
     constexpr int NC = D / 32;              // value-column tiles = waves
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 
     // ---- softmax part (overlaps the S stream)
     float qz = 0.f, beta = 1.f;
-    if constexpr (kNorm) qz = query_dot_z<D>(sq + l32 * P, sz, hh);
+    if constexpr (kNorm) qz = query_dot_z<D, M>(sq + l32 * P, sz, hh);
     f32x16 o = softmax_tile<D, NKT, kNorm, PK, PV>(sq, sk, sv, Br, sl2, ct, lane, qz, &beta);
     f32x16 olin = {};                                   // normalised variant: the linear part apart
     // ---- linear part: O^T += S^T phi(Q)^T, S as hi + lo bf16.  Every wave is
@@ -358,14 +371,8 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
             bf16x8 shi, slo;
             split_hi_lo(sv8, shi, slo);
             const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + l32 * P + 16 * s + 8 * hh);
-            const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-            if constexpr (kNorm) {
-                olin = mfma32(shi, pq, olin);
-                olin = mfma32(slo, pq, olin);
-            } else {
-                o = mfma32(shi, pq, o);
-                o = mfma32(slo, pq, o);
-            }
+            if constexpr (kNorm) olin = linear_mfma<M>(olin, shi, slo, qv);
+            else o = linear_mfma<M>(o, shi, slo, qv);
         }
     }
     if constexpr (kNorm) {
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_bf16_mfma(StepArgs a)
 // gets phi(K)^T V of the block's first Br keys added by the matrix cores.  A is
 // V^T and B is ReLU(K), both through the transposing LDS read of the staged
 // rows (pitches PK and PV); keys past Br are zeroed in the V^T operand.
-template <int D, int NKT, int PK = D + 8, int PV = D + 8>
+template <int D, int NKT, int PK = D + 8, int PV = D + 8, int M = 0>
 __device__ __forceinline__ f32x16 commit_tile(f32x16 acc, const uint16_t* sk, const uint16_t* sv, int Br, int ct,
                                               int ft, int lane)
 {
@@ -417,7 +424,9 @@ __device__ __forceinline__ f32x16 commit_tile(f32x16 acc, const uint16_t* sk, co
                 kop[e] = static_cast<uint16_t>(k0[e]);
                 kop[4 + e] = static_cast<uint16_t>(k1[e]);
             }
-            acc = mfma32(as_bf16x8(vop), as_bf16x8(relu_bf16x8(kop)), acc);
+            const PhiOp<M> kp = phi_op<M>(kop);
+            acc = mfma32(as_bf16x8(vop), kp.hi, acc);
+            if constexpr (!PhiOp<M>::kExact) acc = mfma32(as_bf16x8(vop), kp.lo, acc);
         }
     }
     return acc;
@@ -442,7 +451,7 @@ __device__ __forceinline__ f32x16 commit_tile(f32x16 acc, const uint16_t* sk, co
 // barrier and written once after it, by one wave; a unit's state is touched
 // by one workgroup, so requests only need distinct slots.
 // ---------------------------------------------------------------------------
-template <int D, int NKT, bool kCommit, bool kNorm>
+template <int D, int NKT, bool kCommit, bool kNorm, int M = 0>
 __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(StepArgs a)
 {
     constexpr int KS = D / 16;
@@ -534,7 +543,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 
     // ---- the step, from the old state
     float qz = 0.f, beta = 1.f;
-    if constexpr (kNorm) qz = query_dot_z<D>(sq + (qt * 32 + l32) * P, sz, hh);
+    if constexpr (kNorm) qz = query_dot_z<D, M>(sq + (qt * 32 + l32) * P, sz, hh);
     f32x16 o = softmax_tile<D, NKT, kNorm, PK, PV>(sq + qt * 32 * P, sk, sv, Br, sl2, ct, lane, qz, &beta);
     f32x16 olin = {};                                   // normalised variant: the linear part apart
     __builtin_amdgcn_sched_barrier(0);
@@ -552,14 +561,8 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
         bf16x8 shi, slo;
         split_hi_lo(sv8, shi, slo);
         const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
-        const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-        if constexpr (kNorm) {
-            olin = mfma32(shi, pq, olin);
-            olin = mfma32(slo, pq, olin);
-        } else {
-            o = mfma32(shi, pq, o);
-            o = mfma32(slo, pq, o);
-        }
+        if constexpr (kNorm) olin = linear_mfma<M>(olin, shi, slo, qv);
+        else o = linear_mfma<M>(o, shi, slo, qv);
     }
     if constexpr (kNorm) {
 #pragma unroll
@@ -593,13 +596,13 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) acc[rr] = tile[(int64_t)rr * D];
         }
-        acc = commit_tile<D, NKT, PK, PV>(acc, sk, sv, Br, ct, ft, lane);
+        acc = commit_tile<D, NKT, PK, PV, M>(acc, sk, sv, Br, ct, ft, lane);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) tile[(int64_t)rr * D] = acc[rr];
     }
     // normalised variant: z += sum phi(k) over the block (z was staged before
     // the first barrier, so the step above used the old value)
-    if constexpr (kNorm) commit_z<D, PK>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
+    if constexpr (kNorm) commit_z<D, PK, M>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(NKT * D / 32 * kWave) void step_commit_bf16_mfma(St
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int D, bool kCommit, bool kNorm>
+template <int D, bool kCommit, bool kNorm, int M = 0>
 __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepArgs a)
 {
 #pragma clang fp contract(off)
@@ -788,9 +791,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         for (int s = 0; s < KS; ++s) {
             const u16x8 h8 = *reinterpret_cast<const u16x8*>(shi + cA * P + 16 * s + 8 * hh);
             const u16x8 l8 = *reinterpret_cast<const u16x8*>(slo + cA * P + 16 * s + 8 * hh);
-            const bf16x8 pq = as_bf16x8(relu_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)));
-            o = mfma32(as_bf16x8(h8), pq, o);
-            o = mfma32(as_bf16x8(l8), pq, o);
+            o = linear_mfma<M>(o, as_bf16x8(h8), as_bf16x8(l8), *reinterpret_cast<const u16x8*>(qrow + 16 * s));
         }
     };
     if (has_l) {
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         }
         if constexpr (kNorm) {
             if (jt == 0) {                                // one wave per query tile publishes phi(q).z
-                const float qz = query_dot_z<D>(qrow - 8 * hh, sz, hh);
+                const float qz = query_dot_z<D, M>(qrow - 8 * hh, sz, hh);
                 if (hh == 0) sqz[qt][l32] = qz;
             }
         }
@@ -921,13 +922,13 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
         for (int f = 0; f < NFT; ++f) {
             const int ft = qt + 2 * f;
             float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
-            const f32x16 acc = commit_tile<D, 2, PK, PV>(old[f], sk, sv, Br, ct, ft, lane);
+            const f32x16 acc = commit_tile<D, 2, PK, PV, M>(old[f], sk, sv, Br, ct, ft, lane);
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) __builtin_nontemporal_store(acc[rr], tile + (int64_t)rr * D);   // not read again here
         }
         // normalised variant: z += sum phi(k) over the block (the step used the
         // copy staged before the first barrier)
-        if constexpr (kNorm) commit_z<D, PK>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
+        if constexpr (kNorm) commit_z<D, PK, M>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
     }
 }
 
@@ -949,7 +950,7 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
 // buffer in the accumulator layout, phi(K)^T V is added after the outputs
 // are stored, and the rows that only this wave read are written back.
 // ---------------------------------------------------------------------------
-template <bool kCommit, bool kNorm>
+template <bool kCommit, bool kNorm, int M = 0>
 __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
 {
 #pragma clang fp contract(off)
@@ -1065,7 +1066,7 @@ __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
         }
         if constexpr (kNorm) {
             if (jt == 0) {
-                const float qz = query_dot_z<D>(qrow - 8 * hh, sz, hh);
+                const float qz = query_dot_z<D, M>(qrow - 8 * hh, sz, hh);
                 if (hh == 0) sqz[qt][l32] = qz;
             }
         }
@@ -1151,9 +1152,7 @@ __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
                 const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
-                const bf16x8 pq = as_bf16x8(relu_bf16x8(qv));
-                o[qt] = mfma32(shi, pq, o[qt]);
-                o[qt] = mfma32(slo, pq, o[qt]);
+                o[qt] = linear_mfma<M>(o[qt], shi, slo, qv);
             }
         }
     }
@@ -1177,12 +1176,12 @@ __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
         // ---- the commit of the wave's rows: S^T[c][f] += sum_j V[j][c] ReLU(K[j][f])
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft) {
-            const f32x16 acc = commit_tile<D, 2, PK, PV>(old[ft], sk, sv, Br, ct, ft, lane);
+            const f32x16 acc = commit_tile<D, 2, PK, PV, M>(old[ft], sk, sv, Br, ct, ft, lane);
             float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) __builtin_nontemporal_store(acc[rr], tile + (int64_t)rr * D);
         }
-        if constexpr (kNorm) commit_z<D, PK>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
+        if constexpr (kNorm) commit_z<D, PK, M>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
     }
 }
 
@@ -1411,7 +1410,7 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
                 // normalised variant: one denominator, both sides divided by e^c,
                 // c = max(m, ln(phi(q).z)) (kept above -69, where e^-c stays finite)
                 float qz = 0.f;
-                for (int f = 0; f < D; ++f) qz = fmaf(relu(Elem<T>::load(q, i * rs + f)), zg[f], qz);
+                for (int f = 0; f < D; ++f) qz = fmaf(phi_rt(a.phi, Elem<T>::load(q, i * rs + f)), zg[f], qz);
                 float c = m;
                 if (qz > 0.f) c = fmaxf(c, logf(qz));
                 c = fmaxf(c, -69.f);
@@ -1430,10 +1429,12 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
             for (int j = 0; j < Br; ++j) acc = fmaf(P[ii * Br + j], Elem<T>::load(v, j * rs + c), acc);
             if (zg) {
                 float lin = 0.f;
-                for (int f = 0; f < D; ++f) lin = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], lin);
+                for (int f = 0; f < D; ++f)
+                    lin = fmaf(phi_rt(a.phi, Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], lin);
                 acc = fmaf(wlin[ii], lin, acc);
             } else {
-                for (int f = 0; f < D; ++f) acc = fmaf(relu(Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], acc);
+                for (int f = 0; f < D; ++f)
+                    acc = fmaf(phi_rt(a.phi, Elem<T>::load(q, i * rs + f)), st[(int64_t)c * D + f], acc);
             }
             Elem<T>::store(out, i * rs + c, acc);
         }
@@ -1441,36 +1442,82 @@ __global__ __launch_bounds__(256) void step_generic(StepArgs a)
 }
 
 // ---------------------------------------------------------------------------
-template <int D>
-static void launch_step_d(const StepArgs& a, int units, hipStream_t stream)
+// The step on the matrix cores for map M; returns false for the shapes that
+// take the fp32 kernel (and, for ELU + 1, blocks of more than 64 rows).
+template <int D, int M>
+static bool launch_step_d(const StepArgs& a, int units, hipStream_t stream)
 {
-    if (a.blk <= 32) step_bf16_mfma<D, 1, false><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
-    else if (a.blk <= 64) {
-        if constexpr (D >= 64) step_pair_bf16_mfma<D, false, false><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
-        else step_bf16_mfma<D, 2, false><<<step_grid(units, 2), D / 32 * kWave, 0, stream>>>(a);
-    }
-    else step_long_bf16<D, false><<<step_grid(units, (a.blk + 31) / 32), D / 32 * kWave, 0, stream>>>(a);
-}
-
-// Normalised variant on the matrix cores: blocks of up to 32 rows (d >= 32),
-// 33..64 rows (d = 64, 128) and 65..256 rows; returns false for the shapes
-// that take the fp32 kernel.
-template <int D>
-static bool launch_step_norm_d(const StepArgs& a, int units, hipStream_t stream)
-{
+    constexpr int NT = D / 32 * kWave;
+    const bool norm = a.z != nullptr;
     if (a.blk <= 32) {
-        step_bf16_mfma<D, 1, true><<<step_grid(units, 1), D / 32 * kWave, 0, stream>>>(a);
+        if (norm) step_bf16_mfma<D, 1, true, M><<<step_grid(units, 1), NT, 0, stream>>>(a);
+        else step_bf16_mfma<D, 1, false, M><<<step_grid(units, 1), NT, 0, stream>>>(a);
         return true;
     }
-    if (a.blk > 64) {
-        step_long_bf16<D, true><<<step_grid(units, (a.blk + 31) / 32), D / 32 * kWave, 0, stream>>>(a);
-        return true;
+    if (a.blk <= 64) {
+        if constexpr (D >= 64) {
+            if (norm) step_pair_bf16_mfma<D, false, true, M><<<units, 2 * NT, 0, stream>>>(a);
+            else step_pair_bf16_mfma<D, false, false, M><<<units, 2 * NT, 0, stream>>>(a);
+            return true;
+        } else {
+            if (norm) return false;
+            step_bf16_mfma<D, 2, false, M><<<step_grid(units, 2), NT, 0, stream>>>(a);
+            return true;
+        }
     }
-    if constexpr (D >= 64) {
-        step_pair_bf16_mfma<D, false, true><<<units, 2 * D / 32 * kWave, 0, stream>>>(a);
+    if constexpr (M == 0) {
+        const int grid = step_grid(units, (a.blk + 31) / 32);
+        if (norm) step_long_bf16<D, true><<<grid, NT, 0, stream>>>(a);
+        else step_long_bf16<D, false><<<grid, NT, 0, stream>>>(a);
         return true;
     }
     return false;
+}
+
+// The fused step + commit on the matrix cores for map M (blocks of up to 64
+// rows); returns false for the shapes that run the step and then the commit.
+template <int D, int M>
+static bool launch_step_commit_d(const StepArgs& a, int units, hipStream_t stream)
+{
+    constexpr int NT = D / 32 * kWave;
+    const bool norm = a.z != nullptr;
+    if (a.blk > 64) return false;
+    if (a.blk <= 32) {
+        if (norm) step_commit_bf16_mfma<D, 1, true, true, M><<<units, NT, 0, stream>>>(a);
+        else step_commit_bf16_mfma<D, 1, true, false, M><<<units, NT, 0, stream>>>(a);
+        return true;
+    }
+    if constexpr (D == 32) {
+        if (norm) return false;
+        step_commit_bf16_mfma<D, 2, true, false, M><<<units, 2 * NT, 0, stream>>>(a);
+    } else if constexpr (D == 64) {
+        if (norm) step_pair_bf16_mfma<D, true, true, M><<<units, 2 * NT, 0, stream>>>(a);
+        else step_pair_bf16_mfma<D, true, false, M><<<units, 2 * NT, 0, stream>>>(a);
+    } else {
+        if (norm) step_unit_bf16<true, true, M><<<units, 4 * kWave, 0, stream>>>(a);
+        else step_unit_bf16<true, false, M><<<units, 4 * kWave, 0, stream>>>(a);
+    }
+    return true;
+}
+
+template <int M>
+static bool launch_step_m(const StepArgs& a, int units, hipStream_t stream)
+{
+    switch (a.d) {
+    case 32: return launch_step_d<32, M>(a, units, stream);
+    case 64: return launch_step_d<64, M>(a, units, stream);
+    default: return launch_step_d<128, M>(a, units, stream);
+    }
+}
+
+template <int M>
+static bool launch_step_commit_m(const StepArgs& a, int units, hipStream_t stream)
+{
+    switch (a.d) {
+    case 32: return launch_step_commit_d<32, M>(a, units, stream);
+    case 64: return launch_step_commit_d<64, M>(a, units, stream);
+    default: return launch_step_commit_d<128, M>(a, units, stream);
+    }
 }
 
 // z += sum over the block's first B_r rows of phi(k), one workgroup per
@@ -1489,7 +1536,7 @@ __global__ __launch_bounds__(128) void znorm_commit(StepArgs a)
     const int64_t rs = (int64_t)a.heads * D;
     const T* kb = static_cast<const T*>(a.k) + ((int64_t)r * a.blk * a.heads + h) * D + f;
     float acc = 0.f;
-    for (int j = 0; j < Br; ++j) acc += relu(Elem<T>::load(kb, j * rs));
+    for (int j = 0; j < Br; ++j) acc += phi_rt(a.phi, Elem<T>::load(kb, j * rs));
     a.z[((int64_t)slot * a.heads + h) * D + f] += acc;
 }
 
@@ -1504,36 +1551,10 @@ hipError_t launch_znorm_commit(const StepArgs& a, hipStream_t stream)
 hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
 {
     const int units = a.n_req * a.heads;
-    const bool norm = a.z != nullptr;
-    if (a.dtype_bf16 && a.d >= 32 && a.blk <= 64 && !(norm && a.d == 32 && a.blk > 32)) {
-        const bool two = a.blk > 32;
-        const dim3 block((two ? 2 : 1) * a.d / 32 * kWave);
-        switch (a.d) {
-        case 32:
-            if (norm) step_commit_bf16_mfma<32, 1, true, true><<<units, block, 0, stream>>>(a);
-            else if (two) step_commit_bf16_mfma<32, 2, true, false><<<units, block, 0, stream>>>(a);
-            else step_commit_bf16_mfma<32, 1, true, false><<<units, block, 0, stream>>>(a);
-            break;
-        case 64:
-            if (two) {
-                if (norm) step_pair_bf16_mfma<64, true, true><<<units, block, 0, stream>>>(a);
-                else step_pair_bf16_mfma<64, true, false><<<units, block, 0, stream>>>(a);
-            } else {
-                if (norm) step_commit_bf16_mfma<64, 1, true, true><<<units, block, 0, stream>>>(a);
-                else step_commit_bf16_mfma<64, 1, true, false><<<units, block, 0, stream>>>(a);
-            }
-            break;
-        default:
-            if (two) {
-                if (norm) step_unit_bf16<true, true><<<units, 4 * kWave, 0, stream>>>(a);
-                else step_unit_bf16<true, false><<<units, 4 * kWave, 0, stream>>>(a);
-            } else {
-                if (norm) step_commit_bf16_mfma<128, 1, true, true><<<units, block, 0, stream>>>(a);
-                else step_commit_bf16_mfma<128, 1, true, false><<<units, block, 0, stream>>>(a);
-            }
-            break;
-        }
-        return hipGetLastError();
+    if (a.dtype_bf16 && a.d >= 32) {
+        const bool done = a.phi == 1 ? launch_step_commit_m<1>(a, units, stream)
+                                     : launch_step_commit_m<0>(a, units, stream);
+        if (done) return hipGetLastError();
     }
     // other shapes: the step, then the commit (and the normaliser's), on the
     // same stream
@@ -1551,8 +1572,9 @@ hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream)
     c.blk = a.blk;
     c.d = a.d;
     c.dtype_bf16 = a.dtype_bf16;
+    c.phi = a.phi;
     e = launch_commit(c, stream);
-    if (e != hipSuccess || !norm) return e;
+    if (e != hipSuccess || !a.z) return e;
     return launch_znorm_commit(a, stream);
 }
 
@@ -1560,22 +1582,8 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream)
 {
     const int units = a.n_req * a.heads;
     bool done = false;
-    if (a.dtype_bf16 && a.d >= 32) {
-        done = true;
-        if (a.z) {
-            switch (a.d) {
-            case 32: done = launch_step_norm_d<32>(a, units, stream); break;
-            case 64: done = launch_step_norm_d<64>(a, units, stream); break;
-            default: done = launch_step_norm_d<128>(a, units, stream); break;
-            }
-        } else {
-            switch (a.d) {
-            case 32: launch_step_d<32>(a, units, stream); break;
-            case 64: launch_step_d<64>(a, units, stream); break;
-            default: launch_step_d<128>(a, units, stream); break;
-            }
-        }
-    }
+    if (a.dtype_bf16 && a.d >= 32)
+        done = a.phi == 1 ? launch_step_m<1>(a, units, stream) : launch_step_m<0>(a, units, stream);
     if (!done) {
         const int rows = a.blk < kGenericRows ? a.blk : kGenericRows;
         const size_t lds = sizeof(float) * ((size_t)rows * a.blk + rows);

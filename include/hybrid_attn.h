@@ -286,6 +286,60 @@ ha_status hybrid_state_prefill_norm(const void* k, const void* v,
                                     void* stream);
 
 /*
+ * The feature map as an explicit argument.  The pages' worked example uses
+ * phi = ReLU (every call above); the summary page names phi only as a
+ * kernel-function map ("core formula") of linear attention ("technical
+ * approach").  HA_PHI_ELU1 is ELU + 1, phi(x) = x + 1 for x > 0 and e^x
+ * otherwise: positive everywhere, so the normalised variant's denominator
+ * never vanishes.  The state S, z and every rule of the calls above are
+ * unchanged; a state must be built and read with one map.
+ *
+ * The calls below are the calls above with the map as an argument, and z
+ * optional: z == NULL gives the plain sum (hybrid_attn_step and its kin),
+ * z != NULL the normalised variant (the *_norm calls).  With HA_PHI_RELU
+ * they run the same kernels as those calls.  ELU + 1 is not exact in bf16:
+ * on the matrix cores phi of a bf16 input is formed in fp32 and split into
+ * hi + lo bf16 (one more pass per product); it runs on the matrix cores for
+ * blocks of up to 64 rows with d >= 32, and in plain fp32 kernels otherwise.
+ *   HA_ERR_UNSUPPORTED  unknown feature map.
+ */
+typedef enum { HA_PHI_RELU = 0, HA_PHI_ELU1 = 1 } ha_feature_map;
+
+ha_status hybrid_attn_step_phi(const void* q, const void* k, const void* v,
+                               const float* state, const float* z,
+                               const int32_t* slots, void* out,
+                               const int32_t* blk_lens, int32_t n_req,
+                               int32_t n_slots, int32_t heads, int32_t blk,
+                               int32_t d, float scale, ha_feature_map phi,
+                               ha_dtype dtype, void* stream);
+
+ha_status hybrid_attn_step_commit_phi(const void* q, const void* k,
+                                      const void* v, float* state, float* z,
+                                      const int32_t* slots, void* out,
+                                      const int32_t* blk_lens, int32_t n_req,
+                                      int32_t n_slots, int32_t heads,
+                                      int32_t blk, int32_t d, float scale,
+                                      ha_feature_map phi, ha_dtype dtype,
+                                      void* stream);
+
+ha_status hybrid_state_commit_phi(const void* k, const void* v, float* state,
+                                  float* z, const int32_t* slots,
+                                  const int32_t* blk_lens, int32_t n_req,
+                                  int32_t n_slots, int32_t heads, int32_t blk,
+                                  int32_t d, ha_feature_map phi,
+                                  ha_dtype dtype, void* stream);
+
+ha_status hybrid_state_prefill_phi(const void* k, const void* v,
+                                   const int64_t* cu_seqlens,
+                                   int64_t total_tokens, int64_t max_len,
+                                   float* state, float* z,
+                                   const int32_t* slots, int32_t n_req,
+                                   int32_t n_slots, int32_t heads, int32_t d,
+                                   int32_t chunk, void* workspace,
+                                   size_t workspace_bytes, ha_feature_map phi,
+                                   ha_dtype dtype, void* stream);
+
+/*
  * The exact step that block-hybrid attention replaces (paper abstract: without
  * linearisation every denoising step attends to all previous blocks through
  * the KV cache), for comparison at the same shapes:

@@ -33,8 +33,9 @@ def test_header_declares_the_calls():
     for n in ("hybrid_attn_step", "hybrid_attn_step_commit", "hybrid_state_commit", "hybrid_state_prefill",
               "hybrid_state_prefill_workspace_bytes", "hybrid_exact_step", "hybrid_exact_step_workspace_bytes",
               "hybrid_attn_step_norm", "hybrid_attn_step_commit_norm", "hybrid_state_commit_norm",
-              "hybrid_state_prefill_norm", "hybrid_state_prefill_noalloc", "hybrid_last_error",
-              "hybrid_abi_version"):
+              "hybrid_state_prefill_norm", "hybrid_state_prefill_noalloc", "hybrid_attn_step_phi",
+              "hybrid_attn_step_commit_phi", "hybrid_state_commit_phi", "hybrid_state_prefill_phi",
+              "hybrid_last_error", "hybrid_abi_version"):
         assert n in names
 
 
@@ -265,6 +266,25 @@ def test_noalloc_prefill_validates_before_touching_the_gpu(lib):
     assert fn(1, 1, 1, 100, 0, 1, 1, 2, 2, 4, 48, 256, binding.HA_BF16, None) == binding.HA_ERR_UNSUPPORTED
     assert fn(1, 1, 1, 100, 0, 1, 1, 2, 2, 4, 64, 0, binding.HA_BF16, None) == binding.HA_ERR_INVALID_ARG
     assert fn(1, 1, 1, 100, 0, 1, 1, -1, 2, 4, 64, 256, binding.HA_BF16, None) == binding.HA_ERR_INVALID_ARG
+
+
+def test_feature_map_calls_validate(lib):
+    """The *_phi calls reject an unknown map (unsupported) and keep the plain
+    calls' checks; an empty batch is a no-op."""
+    bf = binding.HA_BF16
+    assert lib.hybrid_attn_step_phi(1, 1, 1, 1, None, 1, 1, None, 2, 2, 4, 32, 64, 0.1, 5, bf, None) \
+        == binding.HA_ERR_UNSUPPORTED
+    assert "feature map" in last(lib)
+    assert lib.hybrid_attn_step_commit_phi(1, 1, 1, 1, None, 1, 1, None, 2, 2, 4, 32, 64, 0.1, -1, bf, None) \
+        == binding.HA_ERR_UNSUPPORTED
+    assert lib.hybrid_state_commit_phi(1, 1, 1, None, 1, None, 2, 2, 4, 32, 64, 2, bf, None) \
+        == binding.HA_ERR_UNSUPPORTED
+    assert lib.hybrid_state_prefill_phi(1, 1, 1, 100, 0, 1, None, 1, 2, 2, 4, 64, 256, 1, 1 << 40, 9, bf, None) \
+        == binding.HA_ERR_UNSUPPORTED
+    assert lib.hybrid_attn_step_phi(1, 1, 1, 1, None, 1, 1, None, 2, 2, 4, 300, 64, 0.1, 1, bf, None) \
+        == binding.HA_ERR_INVALID_ARG
+    assert lib.hybrid_attn_step_phi(None, None, None, None, None, None, None, None, 0, 2, 4, 32, 64, 0.1, 1, bf,
+                                    None) == binding.HA_OK
 
 
 def test_prefill_workspace_size(lib):

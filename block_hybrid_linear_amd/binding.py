@@ -269,8 +269,8 @@ def hybrid_state_prefill(k, v, cu_seqlens, state, slots, max_len=None, chunk=256
     k, v packed [total, H, d]; cu_seqlens int64 [n_req + 1] on the GPU.
     ``max_len`` (host int) is an optional upper bound of the prompt lengths.
     ``workspace`` is a GPU uint8 tensor of at least
-    ``hybrid_state_prefill_workspace_bytes`` bytes; if omitted one is
-    allocated through torch."""
+    ``hybrid_state_prefill_workspace_bytes`` bytes (contents on entry do not
+    matter); if omitted one is allocated through torch."""
     args, _ws = _prefill_args(k, v, cu_seqlens, state, slots, max_len, chunk, workspace, stream)
     _check("hybrid_state_prefill", load_library().hybrid_state_prefill(*args, _stream(stream)))
     return state

@@ -52,6 +52,7 @@ bool known_dtype(ha_dtype t) { return t == HA_F32 || t == HA_BF16; }
 // bytes), then one fp32 partial per (slice, unit) slot.
 size_t plan_bytes(int32_t n_req) { return ((size_t)(n_req + 2) * sizeof(int64_t) + 255) / 256 * 256; }
 
+
 // Checks shared by step and commit.  Returns HA_OK or the failure status.
 ha_status check_block_call(const char* fn, int32_t n_req, int32_t n_slots, int32_t heads,
                            int32_t blk, int32_t d, ha_dtype dtype, int32_t max_blk = HYBRID_ATTN_MAX_BLK)

@@ -36,7 +36,7 @@ struct PhiKVArgs {
     const int32_t* slots;
     const int32_t* blk_lens;    // commit (may be NULL)
     const int64_t* cu;          // prefill: [n_req + 1]
-    int64_t* plan;              // prefill workspace: [n_req + 2]
+    int64_t* plan;              // prefill workspace: [n_req + 2], written by the slice kernel for the reduce
     float* partial;             // prefill workspace: [slices + n_req * heads][d][d]
     float* z;                   // normalised variant: z = sum phi(k) [n_slots][heads][d] (prefill: overwritten);
                                 // NULL: plain
@@ -117,6 +117,7 @@ hipError_t launch_step_commit(const StepArgs& a, hipStream_t stream);
 hipError_t launch_znorm_commit(const StepArgs& a, hipStream_t stream);
 hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream);
+
 hipError_t launch_exact(const ExactArgs& a, hipStream_t stream);
 
 }  // namespace ha

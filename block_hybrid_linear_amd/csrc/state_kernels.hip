@@ -87,23 +87,39 @@ struct PhiKVTile {
     }
 };
 
-// Adds ReLU(K)^T V over rows [0, nrows) of (kb, vb) (rows rs elements apart)
-// into acc.  nrows >= 1.  Every thread of the workgroup must call it.
-template <int D, int PF, int M = 0>
+// The tiles wave w4 of the waves on one head owns, t = w4 TPW + u, share
+// their operands: tile u is value-row tile ct0 + u / NFT and feature tile
+// ft0 + u % NFT, so each k-step reads NCT V^T and NFT K^T operands once
+// (and applies phi once per K^T operand) for its TPW products.  Written out
+// rather than left to the compiler to merge the repeated reads, which it
+// does or not depending on the code around.
+template <int NT, int TPW> struct TileOperands {
+    static constexpr int NFT = TPW < NT ? TPW : NT;      // distinct feature tiles
+    static constexpr int NCT = TPW / NFT;                // distinct value-row tiles
+    static_assert(NCT * NFT == TPW, "tiles form a ct x ft block");
+    __device__ __forceinline__ static int ct0(int w4) { return (w4 * TPW) / NT; }
+    __device__ __forceinline__ static int ft0(int w4) { return (w4 * TPW) % NT; }
+};
+
+// Adds phi(K)^T V over rows [0, nrows) of (kb, vb) (rows rs elements apart)
+// into acc, in stages of tile P.  nrows >= 1.  Every thread of the workgroup
+// must call it.  The first P::NLT threads (whole waves) stage K and V; with
+// 32-token stages that is fewer than the workgroup, and the other waves only
+// multiply.
+template <class P, int PF, int M = 0>
 __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint16_t* vb, int64_t rs,
-                                                 int64_t nrows, typename PhiKVTile<D>::Lds& lds,
-                                                 f32x16 (&acc)[PhiKVTile<D>::TPW])
+                                                 int64_t nrows, typename P::Lds& lds, f32x16 (&acc)[P::TPW])
 {
-    using P = PhiKVTile<D>;
     constexpr int T = P::T, NT = P::NT, TPW = P::TPW, CG = P::CG;
-    static_assert(P::NLT == P::NW * kWave, "every thread stages one block");
+    static_assert(P::NLT <= P::NW * kWave, "at most one staging block per thread");
     const int tid = threadIdx.x;
     const int lane = tid % kWave, w = tid / kWave;
     const int l32 = lane % 32, hh = lane / 32;
+    const bool loader = tid < P::NLT;                    // wave-uniform
 
     // this thread's 8x8 staging block: tensor (K or V), token group, column group
     const int blocks_per_tensor = (T / 8) * CG;
-    const int tensor = tid / blocks_per_tensor;          // 0 = K, 1 = V
+    const int tensor = loader ? tid / blocks_per_tensor : 0;   // 0 = K, 1 = V
     const int bidx = tid % blocks_per_tensor;
     const int tg = P::kColsFast ? bidx / CG : bidx % (T / 8);
     const int cg = P::kColsFast ? bidx % CG : bidx / (T / 8);
@@ -137,36 +153,45 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
             *reinterpret_cast<u32x4*>(dst + P::slot(cg * 8 + c, tg)) = y;
         }
     };
+    using O = TileOperands<NT, TPW>;
+    const int ct0 = O::ct0(w), ft0 = O::ft0(w);
     auto mma_stage = [&](int buf) {
         const uint16_t* kt = lds[buf][0];
         const uint16_t* vt = lds[buf][1];
 #pragma unroll
         for (int s = 0; s < T / 16; ++s) {
             const int g = 2 * s + hh;                       // token group of this lane's 8 tokens
+            u16x8 av[O::NCT];
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                const int t = w * TPW + u, ct = t / NT, ft = t % NT;
-                const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(ct * 32 + l32, g));
-                const u16x8 bk = *reinterpret_cast<const u16x8*>(kt + P::slot(ft * 32 + l32, g));
-                const PhiOp<M> kp = phi_op<M>(bk);           // ELU + 1: hi + lo, two passes
-                acc[u] = mfma32(as_bf16x8(av), kp.hi, acc[u]);
-                if constexpr (!PhiOp<M>::kExact) acc[u] = mfma32(as_bf16x8(av), kp.lo, acc[u]);
+            for (int c = 0; c < O::NCT; ++c)
+                av[c] = *reinterpret_cast<const u16x8*>(vt + P::slot((ct0 + c) * 32 + l32, g));
+#pragma unroll
+            for (int f = 0; f < O::NFT; ++f) {
+                const PhiOp<M> kp = phi_op<M>(*reinterpret_cast<const u16x8*>(kt + P::slot((ft0 + f) * 32 + l32, g)));
+#pragma unroll
+                for (int c = 0; c < O::NCT; ++c) {                // tile u = c NFT + f
+                    f32x16& d = acc[c * O::NFT + f];
+                    d = mfma32(as_bf16x8(av[c]), kp.hi, d);
+                    if constexpr (!PhiOp<M>::kExact) d = mfma32(as_bf16x8(av[c]), kp.lo, d);   // ELU + 1
+                }
             }
         }
     };
 
     const int nstages = (int)((nrows + T - 1) / T);
     u32x4 x0[8], x1[8], x2[8];
-    load_stage(0, x0);
-    if (PF > 1) load_stage((int64_t)T, x1);
-    if (PF > 2) load_stage((int64_t)2 * T, x2);
+    if (loader) {
+        load_stage(0, x0);
+        if (PF > 1) load_stage((int64_t)T, x1);
+        if (PF > 2) load_stage((int64_t)2 * T, x2);
+    }
     auto run_stage = [&](int sg, u32x4 (&x)[8], bool more) {
         const int buf = sg & 1;
         // The barrier also guarantees every wave finished reading this buffer
         // two stages ago, before it is overwritten.
-        store_stage(buf, (int64_t)sg * T, x);
+        if (loader) store_stage(buf, (int64_t)sg * T, x);
         __syncthreads();
-        if (more) load_stage((int64_t)(sg + PF) * T, x);
+        if (loader && more) load_stage((int64_t)(sg + PF) * T, x);
         mma_stage(buf);
     };
     if (PF == 1) {
@@ -185,22 +210,65 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
 // that wave w of the WPH waves working on it holds.  The writes are
 // non-temporal (the kernel never reads them back; for the prefill's partial
 // states that measured 2.9 % faster, with the reduce's non-temporal reads).
+//
+// Addressing: register r of tile (ct, ft) is row c = 32 ct + 8 (r/4) + 4 hh +
+// r%4, column 32 ft + l32.  The wave-uniform part (tile and r/4) goes into a
+// scalar base pointer, the lane's part is one offset (4 hh) D + l32, and r%4
+// is an immediate.  The offset is made opaque to the optimiser, which would
+// otherwise precompute and hold one 64-bit address per register (128 of them
+// for eight tiles).
+template <int D>
+__device__ __forceinline__ uint32_t tile_lane_offset()
+{
+    const int lane = threadIdx.x % kWave;
+    uint32_t lo = (uint32_t)((4 * (lane / 32)) * D + lane % 32);
+    asm volatile("" : "+v"(lo));
+    return lo;
+}
+
 template <int D, int WPH = PhiKVShape<D>::NW>
 __device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (D / 32) / WPH], bool store, int w)
 {
     constexpr int NT = D / 32, TPW = NT * NT / WPH;
-    const int lane = threadIdx.x % kWave;
-    const int l32 = lane % 32, hh = lane / 32;
+    const uint32_t lo = tile_lane_offset<D>();
+    w = __builtin_amdgcn_readfirstlane(w);
+    asm volatile("" : "+s"(base), "+s"(w));  // the tile bases, computed here, not hoisted and held
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int t = w * TPW + u, ct = t / NT, ft = t % NT;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int c = ct * 32 + 8 * (rr / 4) + 4 * hh + rr % 4;
-            float* p = base + (int64_t)c * D + ft * 32 + l32;
-            if (store) __builtin_nontemporal_store(acc[u][rr], p);
-            else acc[u][rr] = *p;
+        for (int q = 0; q < 4; ++q) {
+            float* b = base + (int64_t)(ct * 32 + 8 * q) * D + ft * 32;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float* p = b + lo + e * D;
+                if (store) __builtin_nontemporal_store(acc[u][4 * q + e], p);
+                else acc[u][4 * q + e] = *p;
+            }
         }
+    }
+}
+
+// Adds to acc the tiles that tiles_io would read for wave w, with
+// non-temporal loads (each partial state is read once).
+template <int D, int WPH = PhiKVShape<D>::NW>
+__device__ __forceinline__ void tiles_add(const float* base, f32x16 (&acc)[(D / 32) * (D / 32) / WPH], int w)
+{
+    constexpr int NT = D / 32, TPW = NT * NT / WPH;
+    const uint32_t lo = tile_lane_offset<D>();
+    w = __builtin_amdgcn_readfirstlane(w);
+    asm volatile("" : "+s"(base), "+s"(w));
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int t = w * TPW + u, ct = t / NT, ft = t % NT;
+        f32x16 p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float* b = base + (int64_t)(ct * 32 + 8 * q) * D + ft * 32;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[4 * q + e] = __builtin_nontemporal_load(b + lo + e * D);
+        }
+        acc[u] += p;
     }
 }
 
@@ -208,10 +276,13 @@ __device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (
 // Commit: one workgroup per (request, head); the accumulators start from the
 // old state tiles, so the matrix cores add ReLU(K)^T V onto S in fp32.
 // ---------------------------------------------------------------------------
-template <int D, int M = 0>
+// Blocks of at most 32 rows take 32-token stages (T32): a 64- or 128-token
+// stage would multiply that many padding rows as well.  The 32-token tile
+// has fewer staging blocks than threads, so only the first waves load.
+template <int D, int M = 0, bool T32 = false>
 __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(PhiKVArgs a)
 {
-    using P = PhiKVTile<D>;
+    using P = PhiKVTile<D, 1, PhiKVShape<D>::NW, T32 ? 32 : PhiKVShape<D>::T>;
     __shared__ __attribute__((aligned(16))) typename P::Lds lds;
     const int r = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
     int Br = a.blk_lens ? a.blk_lens[r] : a.blk;
@@ -223,74 +294,138 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(Ph
     float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
     f32x16 acc[P::TPW];
     tiles_io<D>(st, acc, false, threadIdx.x / kWave);
-    phikv_accumulate<D, 1, M>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
+    phikv_accumulate<P, 1, M>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
                               Br, lds, acc);
     tiles_io<D>(st, acc, true, threadIdx.x / kWave);
 }
 
 // ---------------------------------------------------------------------------
-// Prefill, step 1 (one workgroup): the plan.  A unit is a group of hp
-// adjacent heads (hp = 1 or 2, upr = heads / hp units per request).  Prompt r
-// is cut into nch_r = ceil(L_r / chunk) chunks.  The work list is laid out
-// unit by unit, and within a unit prompt by prompt: unit u's part is the
-// N = sum_r nch_r chunks of all prompts in order, the same for every unit.
-// plan[r] = sum over r' < r of nch_r' (exclusive prefix), plan[n_req] = N and
-// plan[n_req + 1] = chunks per slice ceil(N / spu) (spu slices per unit).
-// Malformed offsets (outside [0, total_tokens] or decreasing) count as empty
-// prompts.
+// Prefill: two launches, the slice workgroups and the reduce.  A unit is a
+// group of hp adjacent heads (hp = 1 or 2, upr = heads / hp units per
+// request).  Prompt r is cut into nch_r = ceil(L_r / chunk) chunks.  The work
+// list is laid out unit by unit, and within a unit prompt by prompt: unit u's
+// part is the N = sum_r nch_r chunks of all prompts in order, the same for
+// every unit.  Malformed offsets (outside [0, total_tokens] or decreasing)
+// count as empty prompts.  Slice w = u spu + i owns chunks [i S, (i+1) S) of
+// unit u's part, S = ceil(N / spu) -- the same number of chunks for every
+// workgroup, whatever the prompt lengths, and cut at the same token positions
+// for every unit, so the workgroups of the units of one prompt stream the
+// same token rows (the same DRAM pages) at the same time.
+//
+// Each workgroup works out N, S and the prompt holding its first chunk from
+// cu_seqlens itself: thread t sums the chunk counts of a run of
+// ceil(n_req / 256) prompts, one scan over the 256 run sums gives N and every
+// run's first chunk, and the thread whose run holds chunk i S walks its run
+// to the prompt.  Workgroup 0 also records the plan for the reduce:
+// plan[r] = chunks of the prompts before r (exclusive prefix), plan[n_req] =
+// N and plan[n_req + 1] = S.
+//
+// The (unit, prompt) pieces of a slice each end in one fp32 state per head.
+// A piece whose prompt lies inside this slice is written to the state
+// directly; a piece of a prompt that spans slices i_first .. i_last becomes a
+// partial state in workspace slot w + u n_req + r (hp states per slot;
+// unique, because slices and pieces are both consecutive intervals of the
+// one list), which the reduce adds up.  (Summing them in the slice kernel,
+// by whichever workgroup finishes a prompt last, measured slower: the
+// cross-workgroup hand-off needs an agent-scope release, a write-back of the
+// whole L2, per arrival, and the sums bunch up at the kernel's end in a few
+// waves, where the reduce spreads them over the whole GPU.)
 // ---------------------------------------------------------------------------
+// A value that is the same in every lane, as such (kept in scalar registers).
+__device__ __forceinline__ int64_t first_lane64(int64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// floor(n / d) for 0 <= n < 2^53 and 1 <= d < 2^53: the correctly rounded
+// fp64 quotient truncates to the true quotient or to one more or less, which
+// one integer comparison corrects.  A handful of instructions where a 64-bit
+// integer division expands to a long sequence (and these are inlined into
+// every copy of the cursor code).
+__device__ __forceinline__ int64_t div_floor(int64_t n, int64_t d)
+{
+    int64_t q = (int64_t)((double)n / (double)d);
+    if (q * d > n) --q;
+    else if ((q + 1) * d <= n) ++q;
+    return q;
+}
+
 __device__ __forceinline__ int64_t chunks_of(const PhiKVArgs& a, int r)
 {
     const int64_t s0 = a.cu[r], s1 = a.cu[r + 1];
     if (s0 < 0 || s1 > a.total_tokens || s1 < s0) return 0;
-    return (s1 - s0 + a.chunk - 1) / a.chunk;
+    return div_floor(s1 - s0 + a.chunk - 1, a.chunk);
 }
 
-__global__ __launch_bounds__(256) void prefill_plan(PhiKVArgs a)
+// The same where r is the same in every lane (the cursor's prompt).
+__device__ __forceinline__ int64_t chunks_of_uniform(const PhiKVArgs& a, int r)
 {
-    __shared__ int64_t part[257];
-    const int n = a.n_req, tid = threadIdx.x;
-    const int per = (n + 255) / 256;
-    const int r0 = tid * per < n ? tid * per : n;
-    const int r1 = (r0 + per < n) ? r0 + per : n;
-    int64_t s = 0;
-    for (int r = r0; r < r1; ++r) s += chunks_of(a, r);
-    part[tid + 1] = s;
-    scan256(part, tid);
-    int64_t run = part[tid];
-    for (int r = r0; r < r1; ++r) {
-        a.plan[r] = run;
-        run += chunks_of(a, r);
-    }
-    if (tid == 0) {
-        const int64_t N = part[256];
-        a.plan[n] = N;
-        const int64_t S = (N + a.spu - 1) / a.spu;
-        a.plan[n + 1] = S > 0 ? S : 1;
-    }
+    const int64_t s0 = uniform_load(a.cu, r), s1 = uniform_load(a.cu, r + 1);
+    if (s0 < 0 || s1 > a.total_tokens || s1 < s0) return 0;
+    return first_lane64(div_floor(s1 - s0 + a.chunk - 1, a.chunk));
 }
 
-// ---------------------------------------------------------------------------
-// Prefill, step 2: slice workgroups.  Slice w = u spu + i owns chunks
-// [i S, (i+1) S) of unit u's part of the list -- the same number of chunks for
-// every workgroup, whatever the prompt lengths, and cut at the same token
-// positions for every unit, so the workgroups of the units of one prompt
-// stream the same token rows (the same DRAM pages) at the same time.  It
-// writes one fp32 partial state per head of each (unit, prompt) it touches,
-// into slot w + u n_req + r (hp states per slot).  (The slot is unique:
-// slices and (unit, prompt) pieces are both consecutive intervals of the one
-// list, so a later slice never overlaps an earlier piece.)
-// ---------------------------------------------------------------------------
 struct SliceCursor {
     int r;              // request
     int u;              // unit (head group) of the slice
     int w;              // slice index in list order, u spu + i
     int64_t c0, c1;     // remaining chunk range of this slice within the unit's part
+    int64_t pr;         // chunks of the prompts before r in the unit's part
+    int64_t lo, hi;     // the slice's whole chunk range
 };
 
-__device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur)
+// Plans the workgroup's slice (see above); workgroup 0 also writes the plan
+// for the reduce.  part: 259 int64 of LDS, free again on return.  Every
+// thread of the workgroup calls it; returns false when the slice has no
+// chunks.
+__device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur, int64_t* part)
 {
-    const int64_t N = uniform_load(a.plan, a.n_req), S = uniform_load(a.plan, a.n_req + 1);
+    // 256 runs whatever the workgroup size (64, 256 or 512 threads): thread
+    // tid handles runs tid, tid + blockDim.x, ...
+    constexpr int kRuns = 256, kMaxRunsPerThread = 4;
+    const int tid = threadIdx.x, nt = blockDim.x, n = a.n_req;
+    const int per = (n + kRuns - 1) / kRuns;
+    auto run_first = [&](int v) { return v * per < n ? v * per : n; };
+    auto run_end = [&](int v) { return run_first(v) + per < n ? run_first(v) + per : n; };
+    for (int v = tid; v < kRuns; v += nt) {
+        int64_t s = 0;
+        for (int r = run_first(v); r < run_end(v); ++r) s += chunks_of(a, r);
+        part[v + 1] = s;
+    }
+    if (tid == 0) part[0] = 0;
+    for (int off = 1; off < kRuns; off <<= 1) {          // inclusive scan of part[1..256]
+        __syncthreads();
+        int64_t add[kMaxRunsPerThread];
+#pragma unroll
+        for (int j = 0; j < kMaxRunsPerThread; ++j) {
+            const int v = tid + j * nt;
+            add[j] = (v < kRuns && v >= off) ? part[v + 1 - off] : 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kMaxRunsPerThread; ++j) {
+            const int v = tid + j * nt;
+            if (v < kRuns) part[v + 1] += add[j];
+        }
+    }
+    __syncthreads();
+    const int64_t N = first_lane64(part[256]);
+    const int64_t S = N > 0 ? first_lane64(div_floor(N + a.spu - 1, a.spu)) : 1;
+    if (blockIdx.x == 0) {
+        for (int v = tid; v < kRuns; v += nt) {
+            int64_t pr = part[v];
+            for (int r = run_first(v); r < run_end(v); ++r) {
+                a.plan[r] = pr;
+                pr += chunks_of(a, r);
+            }
+        }
+        if (tid == 0) {
+            a.plan[n] = N;
+            a.plan[n + 1] = S;
+        }
+    }
     // workgroups are numbered unit-fast (consecutive workgroups, which the
     // dispatcher deals to different XCDs, take different units of the same
     // token range)
@@ -300,25 +435,42 @@ __device__ __forceinline__ bool slice_begin(const PhiKVArgs& a, SliceCursor& cur
     cur.w = cur.u * a.spu + i;
     cur.c0 = (int64_t)i * S;
     cur.c1 = cur.c0 + S < N ? cur.c0 + S : N;
-    if (cur.c0 >= cur.c1) return false;
-    int lo = 0, hi = a.n_req;                 // last r with plan[r] <= c0
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) / 2;
-        if (uniform_load(a.plan, mid) <= cur.c0) lo = mid;
-        else hi = mid;
+    cur.lo = cur.c0;
+    cur.hi = cur.c1;
+    for (int v = tid; v < kRuns; v += nt) {              // the one run holding chunk c0
+        if (cur.c0 < cur.c1 && part[v] <= cur.c0 && cur.c0 < part[v + 1]) {
+            int64_t pr = part[v];
+            int r = run_first(v);
+            for (int64_t ch = chunks_of(a, r); pr + ch <= cur.c0; ch = chunks_of(a, r)) {
+                pr += ch;
+                ++r;
+            }
+            part[257] = r;
+            part[258] = pr;
+        }
     }
-    cur.r = lo;
-    return true;
+    __syncthreads();
+    cur.r = cur.c0 < cur.c1 ? (int)first_lane64(part[257]) : 0;
+    cur.pr = cur.c0 < cur.c1 ? first_lane64(part[258]) : 0;
+    __syncthreads();                                     // part is free again
+    return cur.c0 < cur.c1;
 }
 
 // Next piece of the slice: unit h = cur.u of prompt r (heads hp h ..
 // hp h + hp - 1), token rows [t0, t1) of prompt r, whose first row starts at
-// element p0 of k and v.
+// element p0 of k and v; [pr, pe) is the prompt's chunk range in the unit's
+// part.
 __device__ __forceinline__ void slice_piece(const PhiKVArgs& a, SliceCursor& cur, int& h, int64_t& t0, int64_t& t1,
-                                            int64_t& p0)
+                                            int64_t& p0, int64_t& pr, int64_t& pe)
 {
-    while (uniform_load(a.plan, cur.r + 1) <= cur.c0) ++cur.r;   // skip finished and empty prompts
-    const int64_t pr = uniform_load(a.plan, cur.r), pe = uniform_load(a.plan, cur.r + 1);
+    int64_t ch = chunks_of_uniform(a, cur.r);
+    while (cur.pr + ch <= cur.c0) {                      // skip finished and empty prompts
+        cur.pr += ch;
+        ++cur.r;
+        ch = chunks_of_uniform(a, cur.r);
+    }
+    pr = cur.pr;
+    pe = pr + ch;
     const int64_t k0 = cur.c0 - pr;
     const int64_t k1 = (cur.c1 < pe ? cur.c1 : pe) - pr;
     const int64_t s0 = uniform_load(a.cu, cur.r);
@@ -337,6 +489,7 @@ struct StageCursor {
     int r, h;           // unit of the current piece
     int64_t t, t1;      // current stage's first row and the piece's end (rows of prompt r)
     int64_t p0;         // element offset of the piece's prompt row 0, head h
+    int64_t pr, pe;     // the prompt's chunk range in the unit's part
     bool live;
 };
 
@@ -344,7 +497,7 @@ __device__ __forceinline__ void stage_next_piece(const PhiKVArgs& a, StageCursor
 {
     s.live = s.sl.c0 < s.sl.c1;
     if (!s.live) return;
-    slice_piece(a, s.sl, s.h, s.t, s.t1, s.p0);
+    slice_piece(a, s.sl, s.h, s.t, s.t1, s.p0, s.pr, s.pe);
     s.r = s.sl.r;
 }
 
@@ -390,8 +543,9 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
     constexpr int WPH = P::NW / HP;            // compute waves per head
     static_assert(NLD == 0 ? P::NLT == P::NW * kWave : P::NLT == NLD * kWave, "one staging block per loader thread");
     __shared__ __attribute__((aligned(16))) typename P::Lds lds;
+    static_assert(sizeof(lds) >= 259 * sizeof(int64_t), "the plan scan borrows the stage buffers");
     StageCursor cp, ld;                        // compute and load cursors
-    if (!slice_begin(a, cp.sl)) return;
+    if (!slice_begin(a, cp.sl, reinterpret_cast<int64_t*>(&lds))) return;
     stage_next_piece(a, cp);
     ld = cp;
 
@@ -416,7 +570,10 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
     // last row; a finished cursor re-reads the last row it had).  Non-temporal:
     // every key/value byte is read once, and the stream measured 6 % faster
     // with the non-temporal hint than with ordinary loads.
-    auto load_stage = [&](u32x4 (&x)[8]) {
+    // `valid` records the stage's rows in its piece (0 past the slice's end),
+    // for the store three stages later.
+    auto load_stage = [&](u32x4 (&x)[8], int64_t& valid) {
+        valid = ld.live ? ld.t1 - ld.t : 0;
         const uint16_t* src = tbase + ld.p0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -461,37 +618,48 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
     float zacc[kNorm ? NZ : 1];
 #pragma unroll
     for (int u = 0; u < (kNorm ? NZ : 1); ++u) zacc[u] = 0.f;
+    using O = TileOperands<NT, TPW>;
+    static_assert(O::NFT == NZ, "the z sums cover the distinct feature tiles");
+    const int ct0 = O::ct0(w4), ft0 = O::ft0(w4);
     auto mma_stage = [&](int buf) {
         const uint16_t* kt = lds[buf][0];
         const uint16_t* vt = lds[buf][1];
 #pragma unroll
         for (int s = 0; s < T / 16; ++s) {
             const int g = 2 * s + hh;
+            u16x8 av[O::NCT];
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                const int t = w4 * TPW + u, ct = t / NT, ft = t % NT;
-                const u16x8 av = *reinterpret_cast<const u16x8*>(vt + P::slot(hw * D + ct * 32 + l32, g));
-                const PhiOp<M> kp = phi_op<M>(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g)));
-                acc[u] = mfma32(as_bf16x8(av), kp.hi, acc[u]);
-                if constexpr (!PhiOp<M>::kExact) acc[u] = mfma32(as_bf16x8(av), kp.lo, acc[u]);   // ELU + 1
+            for (int c = 0; c < O::NCT; ++c)
+                av[c] = *reinterpret_cast<const u16x8*>(vt + P::slot(hw * D + (ct0 + c) * 32 + l32, g));
+#pragma unroll
+            for (int f = 0; f < O::NFT; ++f) {
+                const PhiOp<M> kp = phi_op<M>(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + (ft0 + f) * 32 + l32, g)));
+#pragma unroll
+                for (int c = 0; c < O::NCT; ++c) {                // tile u = c NFT + f
+                    f32x16& d = acc[c * O::NFT + f];
+                    d = mfma32(as_bf16x8(av[c]), kp.hi, d);
+                    if constexpr (!PhiOp<M>::kExact) d = mfma32(as_bf16x8(av[c]), kp.lo, d);   // ELU + 1
+                }
                 if constexpr (kNorm && HP == 2) {
                     // head pairs: the z sums from the operand in hand (a second
                     // read as below does not fit in the registers); every wave
                     // sums, only the writer waves' sums are stored
-                    if (u < NZ) {
-                        float s8 = 0.f;
-                        if constexpr (M == 0) {
-                            const u32x4 w = __builtin_bit_cast(u32x4, kp.hi);
+                    float s8 = 0.f;
+                    if constexpr (M == 0) {
+                        const u32x4 b = __builtin_bit_cast(u32x4, kp.hi);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
-                        } else {
+                        for (int e = 0; e < 4; ++e)
+                            s8 += __uint_as_float(b[e] << 16) + __uint_as_float(b[e] & 0xffff0000u);
+                    } else {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) s8 += kp.f[2 * e] + kp.f[2 * e + 1];
-                        }
-                        zacc[u] += s8;
+                        for (int e = 0; e < 4; ++e) s8 += kp.f[2 * e] + kp.f[2 * e + 1];
                     }
+                    zacc[f] += s8;
                 }
+                // ELU + 1: keep the scheduler from computing several operands'
+                // exponentials at once (their fp32 temporaries exhaust the
+                // registers of the one-head d = 128 shape)
+                if constexpr (M != 0) __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -521,59 +689,97 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
         }
     };
 
-    // One stage: the loading waves store the compute cursor's stage and issue
-    // the loads three stages ahead; the computing waves multiply and flush the
-    // unit's partial state when its piece ends.  Staging and loads run on
-    // every path (past the end they repeat the last rows), so every path
-    // around a loading wave's loop issues the three register sets' loads in
-    // the same order and each stage waits only for its own set; only the
-    // arithmetic is skipped past the end.  With split roles, loader and
-    // compute waves run separate copies of the loop with the same barriers
-    // (the cursors are workgroup-uniform), so the compute copy has no loads
-    // for the wait counters to track.
+    // End of a piece in a computing wave: the wave's tiles of the (unit,
+    // prompt) go to the state directly when the prompt lies inside this
+    // slice, else to the piece's partial slot for the reduce (see above).
+    // z: lanes hh = 0 of the writer waves hold feature 32 ft + l32 of NZ
+    // tiles.
+    auto finish_piece = [&]() {
+        const int64_t piece = (int64_t)cp.h * a.n_req + cp.r;       // (unit, prompt)
+        const bool inside = cp.pr >= cp.sl.lo && cp.pe <= cp.sl.hi;    // the whole prompt is in this slice
+        const int slot = uniform_load(a.slots, cp.r);
+        if (inside && (slot < 0 || slot >= a.n_slots)) {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+            if constexpr (kNorm) {
+#pragma unroll
+                for (int u = 0; u < NZ; ++u) zacc[u] = 0.f;
+            }
+            return;
+        }
+        const int64_t dst = inside ? (int64_t)slot * a.heads + (int64_t)cp.h * HP + hw
+                                   : ((int64_t)cp.sl.w + piece) * HP + hw;
+        tiles_io<D, WPH>((inside ? a.state : a.partial) + dst * D * D, acc, true, w4);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+        if constexpr (kNorm) {
+            float* zd = (inside ? a.z : a.zpartial) + dst * D;
+#pragma unroll
+            for (int u = 0; u < NZ; ++u) {
+                const float zs = half_pair_sum(zacc[u]);
+                if (zwriter && hh == 0) zd[((w4 * TPW + u) % NT) * 32 + l32] = zs;
+                zacc[u] = 0.f;
+            }
+        }
+    };
+
+    // One stage: the loading waves store the stage and issue the loads three
+    // stages ahead; the computing waves multiply and finish the piece when it
+    // ends.  Staging and loads run on every path (past the end they repeat
+    // the last rows), so every path around a loading wave's loop issues the
+    // three register sets' loads in the same order and each stage waits only
+    // for its own set; only the arithmetic is skipped past the end.  With
+    // split roles, loader and compute waves run separate loops with the same
+    // barriers (the cursors are workgroup-uniform), so the compute loop has
+    // no loads for the wait counters to track.
     int sg = 0;
     auto run_all = [&](auto load_tag, auto mma_tag) {
         constexpr bool kLoad = decltype(load_tag)::value, kMma = decltype(mma_tag)::value;
         u32x4 x0[8], x1[8], x2[8];
+        int64_t v0 = 0, v1 = 0, v2 = 0;                // rows of the stage each register set holds
         if constexpr (kLoad) {
-            load_stage(x0);
-            load_stage(x1);
-            load_stage(x2);
+            load_stage(x0, v0);
+            load_stage(x1, v1);
+            load_stage(x2, v2);
         }
-        auto run_stage = [&](u32x4 (&x)[8]) {
+        // One stage; returns whether it was live.  The loading waves of a
+        // split workgroup keep no compute cursor: the stage they store is
+        // the one their register set was loaded with three stages earlier.
+        auto run_stage = [&](u32x4 (&x)[8], int64_t& valid) {
             const int buf = sg & 1;
-            if constexpr (kLoad) store_stage(buf, cp.t1 - cp.t, x);
+            if constexpr (kLoad) store_stage(buf, kMma ? cp.t1 - cp.t : valid, x);
             __syncthreads();
-            if constexpr (kLoad) load_stage(x);
-            if (!cp.live) return;              // uniform
+            if constexpr (kLoad) load_stage(x, valid);
             if constexpr (kMma) {
+                if (!cp.live) return;          // uniform
                 mma_stage(buf);
                 if constexpr (kNorm && HP == 1) {
                     if (zwriter) z_stage(buf);
                 }
-                if (cp.t + T >= cp.t1) {
-                    const int64_t piece = (int64_t)cp.h * a.n_req + cp.r;    // (unit, prompt) of the piece
-                    tiles_io<D, WPH>(a.partial + (((int64_t)cp.sl.w + piece) * HP + hw) * D * D, acc, true, w4);
-#pragma unroll
-                    for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
-                    if constexpr (kNorm) {
-                        float* zp = a.zpartial + (((int64_t)cp.sl.w + piece) * HP + hw) * D;
-#pragma unroll
-                        for (int u = 0; u < NZ; ++u) {
-                            const float zs = half_pair_sum(zacc[u]);
-                            if (zwriter && hh == 0) zp[((w4 * TPW + u) % NT) * 32 + l32] = zs;
-                            zacc[u] = 0.f;
-                        }
-                    }
-                }
+                if (cp.t + T >= cp.t1) finish_piece();
+                stage_advance(a, cp, T);
             }
             ++sg;
-            stage_advance(a, cp, T);
         };
-        while (cp.live) {
-            run_stage(x0);
-            run_stage(x1);
-            run_stage(x2);
+        if constexpr (kMma && kLoad) {
+            while (cp.live) {
+                run_stage(x0, v0);
+                run_stage(x1, v1);
+                run_stage(x2, v2);
+            }
+        } else if constexpr (kLoad) {
+            while (v0 > 0) {                   // the stage about to be stored is live
+                run_stage(x0, v0);
+                run_stage(x1, v1);
+                run_stage(x2, v2);
+            }
+        } else {
+            // computing waves of a split workgroup: no register sets to
+            // rotate, so one stage per turn, then the loaders' barrier count
+            // (the stages rounded up to a multiple of three)
+            int n = 0;
+            for (; cp.live; ++n) run_stage(x0, v0);
+            for (; n % 3 != 0; ++n) __syncthreads();
         }
     };
     if constexpr (NLD == 0) run_all(std::true_type{}, std::true_type{});
@@ -587,39 +793,45 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
 template <typename T>
 __global__ __launch_bounds__(256) void prefill_slices_generic(PhiKVArgs a)
 {
+    __shared__ int64_t part[259];
     SliceCursor cur;
-    if (!slice_begin(a, cur)) return;
+    if (!slice_begin(a, cur, part)) return;
     const int D = a.d;
-    const int64_t rs = (int64_t)a.heads * D;
+    const int64_t rs = (int64_t)a.heads * D, dd = (int64_t)D * D;
     while (cur.c0 < cur.c1) {
         int h;
-        int64_t t0, t1, p0;
-        slice_piece(a, cur, h, t0, t1, p0);
+        int64_t t0, t1, p0, pr, pe;
+        slice_piece(a, cur, h, t0, t1, p0, pr, pe);
         const T* kb = static_cast<const T*>(a.k) + p0 + t0 * rs;
         const T* vb = static_cast<const T*>(a.v) + p0 + t0 * rs;
-        const int64_t piece = (int64_t)cur.w + (int64_t)h * a.n_req + cur.r;
-        float* dst = a.partial + piece * D * D;
+        const bool inside = pr >= cur.lo && pe <= cur.hi;           // the whole prompt is in this slice
+        const int slot = a.slots[cur.r];
+        if (inside && (slot < 0 || slot >= a.n_slots)) continue;
+        const int64_t dst = inside ? (int64_t)slot * a.heads + h : (int64_t)cur.w + (int64_t)h * a.n_req + cur.r;
+        float* sd = (inside ? a.state : a.partial) + dst * dd;
         for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
             const int c = e / D, f = e % D;
             float acc = 0.f;
             for (int64_t t = 0; t < t1 - t0; ++t)
                 acc = fmaf(Elem<T>::load(vb, t * rs + c), phi_rt(a.phi, Elem<T>::load(kb, t * rs + f)), acc);
-            dst[e] = acc;
+            sd[e] = acc;
         }
         if (a.z) {                                       // normalised variant: sum phi(k) of the piece
+            float* zd = (inside ? a.z : a.zpartial) + dst * D;
             for (int f = threadIdx.x; f < D; f += blockDim.x) {
                 float acc = 0.f;
                 for (int64_t t = 0; t < t1 - t0; ++t) acc += phi_rt(a.phi, Elem<T>::load(kb, t * rs + f));
-                a.zpartial[piece * D + f] = acc;
+                zd[f] = acc;
             }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Prefill, step 3: S[slot] = sum of the head's partials in ascending slice
-// order (deterministic), 0 for an empty prompt.  Each thread owns four
-// consecutive floats of one (request, head) state.
+// Prefill, the reduce: S[slot] = sum of the head's partials in ascending
+// slice order (deterministic), 0 for an empty prompt; a prompt that lay in
+// one slice was written by it.  Each thread owns four consecutive floats of
+// one (request, head) state.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
 {
@@ -634,8 +846,9 @@ __global__ __launch_bounds__(256) void prefill_reduce(PhiKVArgs a)
     const int64_t cfirst = a.plan[r], cend = a.plan[r + 1];
     const int64_t piece = (int64_t)hu * a.n_req + r, w0 = (int64_t)hu * a.spu;
     // slices w0 + cfirst / S .. w0 + (cend - 1) / S hold the head's partials
-    const int64_t wfirst = w0 + (cend > cfirst ? cfirst / S : 0);
-    const int64_t nw = cend > cfirst ? (cend - 1) / S - cfirst / S + 1 : 0;
+    const int64_t wfirst = w0 + (cend > cfirst ? div_floor(cfirst, S) : 0);
+    const int64_t nw = cend > cfirst ? div_floor(cend - 1, S) - div_floor(cfirst, S) + 1 : 0;
+    if (nw == 1) return;                                 // written by its slice
     // sum of the n partials at base + (wfirst + i + piece) hp stride, i < n, in
     // ascending order; loaded four at a time (indices clamped to the last one,
     // so every load is valid) so that their latencies overlap, non-temporal
@@ -692,17 +905,22 @@ hipError_t launch_commit(const PhiKVArgs& a, hipStream_t stream)
     const dim3 grid(a.n_req * a.heads);
     if (a.dtype_bf16 && a.d >= 32) {
         const bool elu = a.phi == 1;
+        const bool t32 = a.blk <= 32;          // one 32-token stage holds the block
         switch (a.d) {
         case 32:
             if (elu) commit_bf16_mfma<32, 1><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a);
             else commit_bf16_mfma<32, 0><<<grid, PhiKVShape<32>::NW * kWave, 0, stream>>>(a);
             break;
         case 64:
-            if (elu) commit_bf16_mfma<64, 1><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a);
+            if (elu && t32) commit_bf16_mfma<64, 1, true><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a);
+            else if (elu) commit_bf16_mfma<64, 1><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a);
+            else if (t32) commit_bf16_mfma<64, 0, true><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a);
             else commit_bf16_mfma<64, 0><<<grid, PhiKVShape<64>::NW * kWave, 0, stream>>>(a);
             break;
         default:
-            if (elu) commit_bf16_mfma<128, 1><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+            if (elu && t32) commit_bf16_mfma<128, 1, true><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+            else if (elu) commit_bf16_mfma<128, 1><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
+            else if (t32) commit_bf16_mfma<128, 0, true><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
             else commit_bf16_mfma<128, 0><<<grid, PhiKVShape<128>::NW * kWave, 0, stream>>>(a);
             break;
         }
@@ -732,27 +950,22 @@ static void launch_prefill_slices(const PhiKVArgs& a, dim3 grid, hipStream_t str
 
 hipError_t launch_prefill(const PhiKVArgs& a, hipStream_t stream)
 {
-    prefill_plan<<<1, 256, 0, stream>>>(a);
+    const dim3 grid(a.slices);
+    if (a.dtype_bf16 && a.d >= 32) {
+        if (a.phi == 1) {
+            if (a.z) launch_prefill_slices<true, 1>(a, grid, stream);
+            else launch_prefill_slices<false, 1>(a, grid, stream);
+        } else {
+            if (a.z) launch_prefill_slices<true, 0>(a, grid, stream);
+            else launch_prefill_slices<false, 0>(a, grid, stream);
+        }
+    } else if (a.dtype_bf16) {
+        prefill_slices_generic<uint16_t><<<grid, 256, 0, stream>>>(a);
+    } else {
+        prefill_slices_generic<float><<<grid, 256, 0, stream>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.total_tokens > 0) {
-        const dim3 grid(a.slices);
-        if (a.dtype_bf16 && a.d >= 32) {
-            if (a.phi == 1) {
-                if (a.z) launch_prefill_slices<true, 1>(a, grid, stream);
-                else launch_prefill_slices<false, 1>(a, grid, stream);
-            } else {
-                if (a.z) launch_prefill_slices<true, 0>(a, grid, stream);
-                else launch_prefill_slices<false, 0>(a, grid, stream);
-            }
-        } else if (a.dtype_bf16) {
-            prefill_slices_generic<uint16_t><<<grid, 256, 0, stream>>>(a);
-        } else {
-            prefill_slices_generic<float><<<grid, 256, 0, stream>>>(a);
-        }
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     const int64_t n4 = (int64_t)a.d * a.d / 4;
     prefill_reduce<<<dim3((unsigned)((n4 + 255) / 256), a.heads, a.n_req), 256, 0, stream>>>(a);
     return hipGetLastError();

@@ -165,11 +165,13 @@ ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v,
  *   pair of adjacent heads) the chunks of all prompts form one list, which is
  *   split into the same number of equal ranges, one per workgroup, so the
  *   work is balanced whatever the prompt lengths and all heads are cut at
- *   the same token positions.  Each workgroup writes one fp32 partial state
- *   per (request, head) its range touches into `workspace`; a second kernel
- *   sums the partials of each (request, head) in a fixed order
- *   (deterministic: the same inputs give bit-identical states).  The result
- *   does not depend on chunk beyond fp32 rounding.
+ *   the same token positions.  Two kernel launches: the workgroups (each
+ *   working out its range from cu_seqlens) write a (request, head) whose
+ *   chunks lie in one range straight into the state, and one fp32 partial
+ *   state per range into `workspace` for one that spans several; a second
+ *   kernel sums those partials in ascending range order (deterministic: the
+ *   same inputs give bit-identical states).  The result does not depend on
+ *   chunk beyond fp32 rounding.
  * workspace: device scratch of at least
  *   hybrid_state_prefill_workspace_bytes(...) bytes (non-NULL when
  *   n_req > 0); its contents on entry do not matter.  Calls sharing one

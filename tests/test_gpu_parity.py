@@ -170,9 +170,9 @@ def test_step_deterministic():
 # Commit
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (128, 100), (128, 128), (128, 1), (128, 200), (128, 256),
-                                   (64, 32), (64, 77), (64, 256), (32, 32), (32, 5), (32, 200), (16, 4), (16, 64),
-                                   (16, 256)])
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 20), (128, 33), (128, 64), (128, 100), (128, 128), (128, 1),
+                                   (128, 200), (128, 256), (64, 32), (64, 9), (64, 77), (64, 256), (32, 32), (32, 5),
+                                   (32, 200), (16, 4), (16, 64), (16, 256)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_commit_parity(d, blk, dtype):
     n_req, H, n_slots = 3, 4, 5
@@ -465,6 +465,37 @@ def test_prefill_deterministic():
     a, _, _, _ = prefill_case(lengths, 4, 128, torch.bfloat16, 14000)
     b, _, _, _ = prefill_case(lengths, 4, 128, torch.bfloat16, 14000)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [128, 64, 16])
+def test_prefill_workspace_reused_with_stale_contents(d):
+    """One workspace, filled with 0xFF bytes, serves calls of different shapes
+    in a row (its contents on entry do not matter): prompts inside one slice
+    and prompts spanning several, empty prompts, and requests whose slot is
+    out of range (skipped: no slot is written for them)."""
+    H = 4
+    cases = [([9000, 0, 4100, 33], [0, 1, 2, 3]),
+             ([20000, 50, 7000], [2, -1, 0]),
+             ([15000, 300, 0], [-1, 1, 3])]
+    n_slots = 4
+    big = max(bh.hybrid_state_prefill_workspace_bytes(len(l), H, d, sum(l), 0, 256) for l, _ in cases)
+    ws = torch.full((big,), 255, dtype=torch.uint8, device=DEV)
+    for i, (lengths, slots) in enumerate(cases):
+        cu = synth.cu_from_lengths(lengths)
+        k, v = (synth.normal((int(cu[-1]), H, d), 15000 + 10 * i + t) for t in range(2))
+        state = torch.full((n_slots, H, d, d), 9.0, device=DEV)
+        before = to64(state)
+        bh.hybrid_state_prefill(k.to(DEV), v.to(DEV), cu.to(DEV), state,
+                                torch.tensor(slots, dtype=torch.int32, device=DEV), workspace=ws)
+        torch.cuda.synchronize()
+        got = state_to_oracle(state)
+        valid = [s for s in slots if s >= 0]
+        untouched = [s for s in range(n_slots) if s not in valid]
+        assert np.array_equal(got[untouched], state_to_oracle(torch.from_numpy(before))[untouched]), \
+            f"call {i}: a slot not named (or named by an out-of-range request) was written"
+        keep = [r for r, s in enumerate(slots) if s >= 0]
+        ref = oracle.prefill(k, v, cu, slots=list(range(len(lengths))))
+        assert_parity(got[[slots[r] for r in keep]], ref[keep], torch.bfloat16, f"call {i}")
 
 
 def test_prepared_calls_match_and_rerun():

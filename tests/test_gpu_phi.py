@@ -91,7 +91,8 @@ def test_step_elu1_correctly_rounded(d, blk, fused):
 
 
 @pytest.mark.parametrize("norm", [False, True])
-@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (64, 32), (64, 64), (32, 48), (16, 20), (128, 200)])
+@pytest.mark.parametrize("d,blk", [(128, 32), (128, 64), (64, 32), (64, 64), (32, 48), (16, 20), (128, 200),
+                                   (128, 21), (64, 9)])
 def test_commit_and_fused_elu1(d, blk, norm):
     """Commit, and the fused step + commit (output bit-identical to the step's
     on the matrix-core shapes), against the oracle's commit with ELU + 1."""

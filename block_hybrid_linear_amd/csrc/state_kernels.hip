@@ -1,7 +1,8 @@
-// Prefix-state kernels: block commit S += ReLU(K)^T V and prompt prefill
-// S = sum_t ReLU(k_t)^T v_t ("Retrofitting Linear Attention into Diffusion
+// Prefix-state kernels: block commit S += phi(K)^T V and prompt prefill
+// S = sum_t phi(k_t)^T v_t ("Retrofitting Linear Attention into Diffusion
 // Language Models", paper-daily summary page, section "technical details in
-// action": S_1 = phi(K_1)^T V_1, S_{1,2} = phi(K_1)^T V_1 + phi(K_2)^T V_2).
+// action": S_1 = phi(K_1)^T V_1, S_{1,2} = phi(K_1)^T V_1 + phi(K_2)^T V_2,
+// with phi = ReLU; ELU + 1 as the second fixed map, template argument M).
 // The state is stored transposed: state[c][f] = S[f][c].
 #include <type_traits>
 
@@ -11,9 +12,9 @@
 namespace ha {
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core reduction of ReLU(K)^T V over a range of token rows.
+// bf16 matrix-core reduction of phi(K)^T V over a range of token rows.
 //
-//   dS^T[c][f] = sum_j V[j][c] * ReLU(K[j][f])      (A = V^T, B = ReLU(K), k = token)
+//   dS^T[c][f] = sum_j V[j][c] * phi(K[j][f])      (A = V^T, B = phi(K), k = token)
 //
 // The reduction runs over tokens, which are the strided dimension of the
 // token-major inputs, so K and V go through LDS transposed: each thread loads
@@ -32,12 +33,11 @@ namespace ha {
 // k-step, so they fold into instruction offsets.  (d = 64, 32: the token
 // group varies fastest, which is conflict-free without a permutation.)
 //
-// Stages of T tokens are double-buffered in LDS; PF stages of global loads
-// are in flight while a stage is multiplied (prefill: 3, commit: 1), one
-// barrier per stage.  In the prefill loop every stage issues its loads
-// unconditionally (a stage past the end re-reads the last valid rows, which
-// hit in L2, and is zeroed when stored), so the number of loads in flight is
-// the same on every path.
+// Stages of T tokens are double-buffered in LDS, one barrier per stage.  In
+// the commit the next stage's loads are in flight while a stage is
+// multiplied; the prefill's own loop keeps three stages of loads in flight,
+// issued unconditionally on every path (a stage past the end re-reads the
+// last valid rows, which hit in L2, and is padded when stored).
 //
 // Output tiles are 32 x 32; wave w owns value-row tile ct = (w*TPW)/NT and
 // TPW feature tiles.  Accumulator register r of lane l holds
@@ -106,7 +106,7 @@ template <int NT, int TPW> struct TileOperands {
 // must call it.  The first P::NLT threads (whole waves) stage K and V; with
 // 32-token stages that is fewer than the workgroup, and the other waves only
 // multiply.
-template <class P, int PF, int M = 0>
+template <class P, int M = 0>
 __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint16_t* vb, int64_t rs,
                                                  int64_t nrows, typename P::Lds& lds, f32x16 (&acc)[P::TPW])
 {
@@ -179,29 +179,16 @@ __device__ __forceinline__ void phikv_accumulate(const uint16_t* kb, const uint1
     };
 
     const int nstages = (int)((nrows + T - 1) / T);
-    u32x4 x0[8], x1[8], x2[8];
-    if (loader) {
-        load_stage(0, x0);
-        if (PF > 1) load_stage((int64_t)T, x1);
-        if (PF > 2) load_stage((int64_t)2 * T, x2);
-    }
-    auto run_stage = [&](int sg, u32x4 (&x)[8], bool more) {
+    u32x4 x[8];
+    if (loader) load_stage(0, x);
+    for (int sg = 0; sg < nstages; ++sg) {
         const int buf = sg & 1;
         // The barrier also guarantees every wave finished reading this buffer
         // two stages ago, before it is overwritten.
         if (loader) store_stage(buf, (int64_t)sg * T, x);
         __syncthreads();
-        if (loader && more) load_stage((int64_t)(sg + PF) * T, x);
+        if (loader && sg + 1 < nstages) load_stage((int64_t)(sg + 1) * T, x);
         mma_stage(buf);
-    };
-    if (PF == 1) {
-        for (int sg = 0; sg < nstages; ++sg) run_stage(sg, x0, sg + 1 < nstages);
-    } else {
-        for (int sg = 0; sg < nstages; sg += 3) {
-            run_stage(sg, x0, true);
-            run_stage(sg + 1, x1, true);
-            run_stage(sg + 2, x2, true);
-        }
     }
     __syncthreads();   // LDS is reused by the caller's next range
 }
@@ -274,7 +261,7 @@ __device__ __forceinline__ void tiles_add(const float* base, f32x16 (&acc)[(D / 
 
 // ---------------------------------------------------------------------------
 // Commit: one workgroup per (request, head); the accumulators start from the
-// old state tiles, so the matrix cores add ReLU(K)^T V onto S in fp32.
+// old state tiles, so the matrix cores add phi(K)^T V onto S in fp32.
 // ---------------------------------------------------------------------------
 // Blocks of at most 32 rows take 32-token stages (T32): a 64- or 128-token
 // stage would multiply that many padding rows as well.  The 32-token tile
@@ -294,7 +281,7 @@ __global__ __launch_bounds__(PhiKVShape<D>::NW * kWave) void commit_bf16_mfma(Ph
     float* st = a.state + ((int64_t)slot * a.heads + h) * D * D;
     f32x16 acc[P::TPW];
     tiles_io<D>(st, acc, false, threadIdx.x / kWave);
-    phikv_accumulate<P, 1, M>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
+    phikv_accumulate<P, M>(static_cast<const uint16_t*>(a.k) + off, static_cast<const uint16_t*>(a.v) + off, rs,
                               Br, lds, acc);
     tiles_io<D>(st, acc, true, threadIdx.x / kWave);
 }
@@ -608,7 +595,7 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
     f32x16 acc[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
-    // normalised variant: z = sum phi(k) per feature, from the ReLU(K) operands
+    // normalised variant: z = sum phi(k) per feature, from the phi(K) operands
     // the wave already reads.  The wave's first NZ tiles share one value-row
     // tile and cover NZ distinct feature tiles; in the waves whose first tile
     // is in value row 0 (the ones that write z), lane (l32, hh) sums in fp32

@@ -407,15 +407,20 @@ def test_state_layout_row_is_value_dim():
     assert_parity(out, oracle.step(q, k, np.zeros(v.shape), Sd, scale=d ** -0.5), torch.bfloat16, "oracle")
 
 
-def test_prefill_many_ragged_requests():
-    """Hundreds of prompts, many shorter than a chunk, some empty: the
-    balanced split crosses request and head boundaries inside workgroups."""
+@pytest.mark.parametrize("d,H", [(64, 2), (32, 2), (16, 2), (128, 2), (128, 3)])
+def test_prefill_many_ragged_requests(d, H):
+    """Hundreds of prompts (more than the 256 runs each slice workgroup's
+    planning scan covers, so every run holds two), many shorter than a chunk,
+    some empty: the balanced split crosses request and head boundaries inside
+    workgroups, prompts lie inside one slice or span several.  Every
+    workgroup size of the slice kernels: 64 threads (d = 32), 256 (d = 16, 64,
+    one head of d = 128), 512 (head pairs)."""
     rng = np.random.default_rng(77)
     lengths = [int(x) for x in rng.integers(0, 700, size=300)]
     lengths[5] = 0
     lengths[6] = 1
     lengths[7] = 5000
-    state, ref, _, _ = prefill_case(lengths, 2, 64, torch.bfloat16, 13000, chunk=64)
+    state, ref, _, _ = prefill_case(lengths, H, d, torch.bfloat16, 13000 + d + H, chunk=64)
     assert_parity(state_to_oracle(state), ref, torch.bfloat16, "many prompts")
 
 

@@ -1197,7 +1197,7 @@ __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
 // key stage (32 contiguous bytes of row cA per lane and k-step) and added to
 // the normalised softmax output.
 // ---------------------------------------------------------------------------
-template <int D, bool kNorm>
+template <int D, bool kNorm, int M = 0>
 __global__ __launch_bounds__(D / 32 * kWave) void step_long_bf16(StepArgs a)
 {
 #pragma clang fp contract(off)
@@ -1333,7 +1333,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_long_bf16(StepArgs a)
         sr[s][1] = srow[4 * s + 1];
     }
     float alpha, beta = 1.f;
-    if constexpr (kNorm) norm_weights(m, l, query_dot_z<D>(sq + l32 * P, sz, hh), alpha, beta);
+    if constexpr (kNorm) norm_weights(m, l, query_dot_z<D, M>(sq + l32 * P, sz, hh), alpha, beta);
     else alpha = __builtin_amdgcn_rcpf(l);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) o[rr] *= alpha;
@@ -1344,9 +1344,7 @@ __global__ __launch_bounds__(D / 32 * kWave) void step_long_bf16(StepArgs a)
                               sr[s][1][0], sr[s][1][1], sr[s][1][2], sr[s][1][3]};
         bf16x8 shi, slo;
         split_hi_lo(sv8, shi, slo);
-        const bf16x8 pq = as_bf16x8(relu_bf16x8(*reinterpret_cast<const u16x8*>(qrow + 16 * s)));
-        acc = mfma32(shi, pq, acc);
-        acc = mfma32(slo, pq, acc);
+        acc = linear_mfma<M>(acc, shi, slo, *reinterpret_cast<const u16x8*>(qrow + 16 * s));
     }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) o[rr] = kNorm ? fmaf(beta, acc[rr], o[rr]) : o[rr] + acc[rr];
@@ -1465,13 +1463,10 @@ static bool launch_step_d(const StepArgs& a, int units, hipStream_t stream)
             return true;
         }
     }
-    if constexpr (M == 0) {
-        const int grid = step_grid(units, (a.blk + 31) / 32);
-        if (norm) step_long_bf16<D, true><<<grid, NT, 0, stream>>>(a);
-        else step_long_bf16<D, false><<<grid, NT, 0, stream>>>(a);
-        return true;
-    }
-    return false;
+    const int grid = step_grid(units, (a.blk + 31) / 32);
+    if (norm) step_long_bf16<D, true, M><<<grid, NT, 0, stream>>>(a);
+    else step_long_bf16<D, false, M><<<grid, NT, 0, stream>>>(a);
+    return true;
 }
 
 // The fused step + commit on the matrix cores for map M (blocks of up to 64

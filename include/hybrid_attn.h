@@ -302,7 +302,8 @@ ha_status hybrid_state_prefill_norm(const void* k, const void* v,
  * they run the same kernels as those calls.  ELU + 1 is not exact in bf16:
  * on the matrix cores phi of a bf16 input is formed in fp32 and split into
  * hi + lo bf16 (one more pass per product); it runs on the matrix cores for
- * blocks of up to 64 rows with d >= 32, and in plain fp32 kernels otherwise.
+ * every bf16 shape with d >= 32 (blocks of up to 256 rows), and in plain fp32
+ * kernels otherwise.
  *   HA_ERR_UNSUPPORTED  unknown feature map.
  */
 typedef enum { HA_PHI_RELU = 0, HA_PHI_ELU1 = 1 } ha_feature_map;

@@ -18,8 +18,9 @@ from parity import assert_parity, rows_mask, state_from_oracle, state_to_oracle,
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 SENTINEL = -1024.0
-MAT_CASES = [(128, 32), (128, 64), (64, 32), (64, 64), (128, 17), (64, 50)]
-FALLBACK_CASES = [(32, 40), (128, 100), (16, 32)]
+MAT_CASES = [(128, 32), (128, 64), (64, 32), (64, 64), (128, 17), (64, 50), (128, 100), (64, 200), (128, 256),
+             (32, 130)]
+FALLBACK_CASES = [(32, 40), (16, 32)]
 
 
 def gen(shape, seed, dtype=torch.bfloat16, std=1.0):
@@ -70,7 +71,7 @@ def _bf16_ulp(x):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("d,blk", [(128, 64), (128, 32), (64, 64), (64, 32)])
+@pytest.mark.parametrize("d,blk", [(128, 64), (128, 32), (64, 64), (64, 32), (128, 200)])
 def test_step_elu1_correctly_rounded(d, blk, fused):
     """phi(Q) as hi + lo bf16 on the matrix cores: every bf16 output within one
     ulp of the exact value (plus fp32 accumulation error)."""

@@ -643,10 +643,11 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
                     }
                     zacc[f] += s8;
                 }
-                // ELU + 1: keep the scheduler from computing several operands'
-                // exponentials at once (their fp32 temporaries exhaust the
-                // registers of the one-head d = 128 shape)
-                if constexpr (M != 0) __builtin_amdgcn_sched_barrier(0);
+                // ELU + 1, and the normalised one-head shapes: keep the
+                // scheduler from preparing several K^T operands at once (their
+                // temporaries exhausted the registers of the one-head d = 128
+                // kernels, which also hold three stages of loads)
+                if constexpr (M != 0 || (kNorm && HP == 1)) __builtin_amdgcn_sched_barrier(0);
             }
         }
     };

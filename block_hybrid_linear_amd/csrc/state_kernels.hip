@@ -596,15 +596,33 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
 #pragma unroll
     for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
     // normalised variant: z = sum phi(k) per feature, from the phi(K) operands
-    // the wave already reads.  The wave's first NZ tiles share one value-row
-    // tile and cover NZ distinct feature tiles; in the waves whose first tile
-    // is in value row 0 (the ones that write z), lane (l32, hh) sums in fp32
-    // its half of each k-step's tokens of feature 32 ft + l32.
+    // the wave holds for its products; lane (l32, hh) sums in fp32 its half of
+    // each k-step's tokens of feature 32 ft + l32.  Head pairs: every compute
+    // wave sums its NZ distinct feature tiles and the waves whose first tile
+    // is in value row 0 write them.  One head per workgroup: feature tile ft
+    // is summed and written by wave ft alone, so the work is spread over the
+    // waves (one writer summing every tile made it the straggler at each
+    // stage's barrier).
     constexpr int NZ = TPW < NT ? TPW : NT;
-    const bool zwriter = (w4 * TPW) / NT == 0;           // wave-uniform
-    float zacc[kNorm ? NZ : 1];
+    constexpr int NZA = HP == 2 ? NZ : 1;                // z accumulators per lane
+    static_assert(HP == 2 || (NT <= WPH && (TPW == 1 || TPW >= NT)),
+                  "one head per workgroup: wave ft < NT holds feature tile ft among its operands");
+    const bool zwriter = HP == 2 ? (w4 * TPW) / NT == 0 : w4 < NT;   // wave-uniform
+    float zacc[kNorm ? NZA : 1];
 #pragma unroll
-    for (int u = 0; u < (kNorm ? NZ : 1); ++u) zacc[u] = 0.f;
+    for (int u = 0; u < (kNorm ? NZA : 1); ++u) zacc[u] = 0.f;
+    auto zsum8 = [&](const PhiOp<M>& kp) {               // phi of the operand's 8 tokens, summed
+        float s8 = 0.f;
+        if constexpr (M == 0) {
+            const u32x4 b = __builtin_bit_cast(u32x4, kp.hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s8 += __uint_as_float(b[e] << 16) + __uint_as_float(b[e] & 0xffff0000u);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s8 += kp.f[2 * e] + kp.f[2 * e + 1];
+        }
+        return s8;
+    };
     using O = TileOperands<NT, TPW>;
     static_assert(O::NFT == NZ, "the z sums cover the distinct feature tiles");
     const int ct0 = O::ct0(w4), ft0 = O::ft0(w4);
@@ -627,21 +645,9 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
                     d = mfma32(as_bf16x8(av[c]), kp.hi, d);
                     if constexpr (!PhiOp<M>::kExact) d = mfma32(as_bf16x8(av[c]), kp.lo, d);   // ELU + 1
                 }
-                if constexpr (kNorm && HP == 2) {
-                    // head pairs: the z sums from the operand in hand (a second
-                    // read as below does not fit in the registers); every wave
-                    // sums, only the writer waves' sums are stored
-                    float s8 = 0.f;
-                    if constexpr (M == 0) {
-                        const u32x4 b = __builtin_bit_cast(u32x4, kp.hi);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            s8 += __uint_as_float(b[e] << 16) + __uint_as_float(b[e] & 0xffff0000u);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) s8 += kp.f[2 * e] + kp.f[2 * e + 1];
-                    }
-                    zacc[f] += s8;
+                if constexpr (kNorm && HP == 2) zacc[f] += zsum8(kp);
+                if constexpr (kNorm && HP == 1) {
+                    if (ft0 + f == w4) zacc[0] += zsum8(kp);         // wave-uniform: wave ft owns tile ft
                 }
                 // ELU + 1, and the normalised one-head shapes: keep the
                 // scheduler from preparing several K^T operands at once (their
@@ -651,36 +657,10 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
             }
         }
     };
-    // normalised variant, writer waves: the stage's sums of phi(k), re-reading
-    // the K^T operands of the first NZ tiles after the multiplications
-    auto z_stage = [&](int buf) {
-        const uint16_t* kt = lds[buf][0];
-#pragma unroll
-        for (int s = 0; s < T / 16; ++s) {
-            const int g = 2 * s + hh;
-#pragma unroll
-            for (int u = 0; u < NZ; ++u) {
-                const int ft = (w4 * TPW + u) % NT;
-                const u16x8 kr = *reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g));
-                float s8 = 0.f;
-                if constexpr (M == 0) {
-                    const u32x4 w = __builtin_bit_cast(u32x4, relu_bf16x8(kr));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) s8 += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xffff0000u);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        s8 += phi_of<M>(bf16_bits_to_f32(kr[2 * e])) + phi_of<M>(bf16_bits_to_f32(kr[2 * e + 1]));
-                }
-                zacc[u] += s8;
-            }
-        }
-    };
-
     // End of a piece in a computing wave: the wave's tiles of the (unit,
     // prompt) go to the state directly when the prompt lies inside this
     // slice, else to the piece's partial slot for the reduce (see above).
-    // z: lanes hh = 0 of the writer waves hold feature 32 ft + l32 of NZ
+    // z: lanes hh = 0 of the writer waves hold feature 32 ft + l32 of their
     // tiles.
     auto finish_piece = [&]() {
         const int64_t piece = (int64_t)cp.h * a.n_req + cp.r;       // (unit, prompt)
@@ -691,7 +671,7 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
             for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
             if constexpr (kNorm) {
 #pragma unroll
-                for (int u = 0; u < NZ; ++u) zacc[u] = 0.f;
+                for (int u = 0; u < NZA; ++u) zacc[u] = 0.f;
             }
             return;
         }
@@ -703,9 +683,10 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
         if constexpr (kNorm) {
             float* zd = (inside ? a.z : a.zpartial) + dst * D;
 #pragma unroll
-            for (int u = 0; u < NZ; ++u) {
+            for (int u = 0; u < NZA; ++u) {
                 const float zs = half_pair_sum(zacc[u]);
-                if (zwriter && hh == 0) zd[((w4 * TPW + u) % NT) * 32 + l32] = zs;
+                const int ft = HP == 2 ? (w4 * TPW + u) % NT : w4;
+                if (zwriter && hh == 0) zd[ft * 32 + l32] = zs;
                 zacc[u] = 0.f;
             }
         }
@@ -741,9 +722,6 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
             if constexpr (kMma) {
                 if (!cp.live) return;          // uniform
                 mma_stage(buf);
-                if constexpr (kNorm && HP == 1) {
-                    if (zwriter) z_stage(buf);
-                }
                 if (cp.t + T >= cp.t1) finish_piece();
                 stage_advance(a, cp, T);
             }

@@ -947,8 +947,9 @@ __global__ __launch_bounds__(2 * D / 32 * kWave) void step_pair_bf16_mfma(StepAr
 // once for both query tiles.
 // With the commit, the wave owns state rows [32 ct, 32 ct + 32) (every
 // feature tile): the old tile of feature tile qq is taken from the quarter
-// buffer in the accumulator layout, phi(K)^T V is added after the outputs
-// are stored, and the rows that only this wave read are written back.
+// buffer in the accumulator layout, phi(K)^T V is added to it and the tile
+// is written back as soon as the quarter's linear products are issued, so
+// the state's writes overlap the later quarters' reads.
 // ---------------------------------------------------------------------------
 template <bool kCommit, bool kNorm, int M = 0>
 __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
@@ -1126,20 +1127,24 @@ __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
     // as it arrives: the raw rows go to the wave's buffer and come back as A
     // operands (row cA - 32 ct, features 16 s + 8 hh .. + 7); LDS accesses of
     // one wave complete in order, so no barrier is needed
+    // With the commit, each quarter's state tile is updated and written back
+    // as soon as its products are issued (only this wave reads or writes these
+    // rows, and the old values are on chip), so the state's writes overlap the
+    // later quarters' reads instead of following the outputs in one burst.
     const int arow = 16 * ((l32 / 4) % 2) + 4 * (l32 / 8) + l32 % 4;
     float* qb = sbuf[ct];
     f32x16 o[2] = {{}, {}};                          // the linear part first, as the head-pair kernel
-    f32x16 old[kCommit ? 4 : 1];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             *reinterpret_cast<f32x4*>(qb + (8 * i + lane / 8) * SQP + 4 * (lane % 8)) = sraw[qq][i];
+        f32x16 old;
         if constexpr (kCommit) {
             // the old tile of feature tile qq in the accumulator layout (rows
             // 32 ct + 16 hh + rr, features 32 qq + l32)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) old[qq][rr] = qb[(16 * hh + rr) * SQP + l32];
+            for (int rr = 0; rr < 16; ++rr) old[rr] = qb[(16 * hh + rr) * SQP + l32];
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -1154,6 +1159,13 @@ __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
                 const u16x8 qv = *reinterpret_cast<const u16x8*>(sq + (qt * 32 + l32) * P + 16 * s + 8 * hh);
                 o[qt] = linear_mfma<M>(o[qt], shi, slo, qv);
             }
+        }
+        if constexpr (kCommit) {
+            // the commit of tile qq: S^T[c][f] += sum_j V[j][c] phi(K[j][f])
+            const f32x16 acc = commit_tile<D, 2, PK, PV, M>(old, sk, sv, Br, ct, qq, lane);
+            float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * qq + l32;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) __builtin_nontemporal_store(acc[rr], tile + (int64_t)rr * D);
         }
     }
     // the sum of the two parts in the head-pair kernel's order, so the fused
@@ -1172,17 +1184,7 @@ __global__ __launch_bounds__(4 * kWave) void step_unit_bf16(StepArgs a)
     for (int qt = 0; qt < 2; ++qt)
         if (qt * 32 + l32 < Br) store_tile_global<D>(out + (int64_t)(qt * 32 + l32) * rs, o[qt], hh, ct);
 
-    if constexpr (kCommit) {
-        // ---- the commit of the wave's rows: S^T[c][f] += sum_j V[j][c] ReLU(K[j][f])
-#pragma unroll
-        for (int ft = 0; ft < 4; ++ft) {
-            const f32x16 acc = commit_tile<D, 2, PK, PV, M>(old[ft], sk, sv, Br, ct, ft, lane);
-            float* tile = a.state_rw + soff + (int64_t)(32 * ct + 16 * hh) * D + 32 * ft + l32;
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) __builtin_nontemporal_store(acc[rr], tile + (int64_t)rr * D);
-        }
-        if constexpr (kNorm) commit_z<D, PK, M>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
-    }
+    if constexpr (kCommit && kNorm) commit_z<D, PK, M>(a.z + ((int64_t)slot * a.heads + h) * D, sk, Br, tid);
 }
 
 // ---------------------------------------------------------------------------

@@ -3,9 +3,9 @@ against the fp64 oracle's softmax over [prefix; active block], through the C
 ABI.
 
 Prefixes span several key chunks with ragged tails, one request has an empty
-prefix, blocks are ragged; every head dim and both dtypes are covered, plus
-the chunk size, malformed offsets, requests with no valid rows, large logits
-and determinism.
+prefix, blocks are ragged; every head dim and both dtypes are covered, and
+even head counts at d = 128, plus the chunk size, malformed offsets,
+requests with no valid rows, large logits and determinism.
 """
 import numpy as np
 import pytest
@@ -69,6 +69,22 @@ def test_exact_step_parity(d, blk, dtype):
     blk_lens = torch.tensor([blk, max(1, (blk * 2) // 3), 1, blk], dtype=torch.int32, device=DEV)
     e = check_exact(q, k, v, kc, vc, cu, blk_lens, d ** -0.5, f"exact d={d} blk={blk} {dtype}")
     print(f"d={d} blk={blk} {dtype}: err {e:.2e}", flush=True)
+
+
+EVEN_HEAD_CASES = [(2, 32), (4, 64), (6, 1), (4, 17), (2, 50), (8, 33)]   # (heads, blk) at d = 128
+
+
+@pytest.mark.parametrize("H,blk", EVEN_HEAD_CASES)
+def test_exact_step_even_heads(H, blk):
+    """bf16 at d = 128 with even head counts (adjacent heads of one token row
+    in neighbouring units of the work list): 4 requests with prefixes 0, 37,
+    700 and 1500 keys, ragged blocks."""
+    prefix = [0, 37, 700, 1500]
+    seed = 9300 + 10 * H + blk
+    q, k, v, kc, vc, cu = make_case(prefix, blk, H, 128, torch.bfloat16, seed)
+    blk_lens = torch.tensor([blk, max(1, (blk * 2) // 3), 1, blk], dtype=torch.int32, device=DEV)
+    e = check_exact(q, k, v, kc, vc, cu, blk_lens, 128 ** -0.5, f"even heads H={H} blk={blk}")
+    print(f"H={H} blk={blk}: err {e:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("chunk", [1, 7, 32, 100, 256, 5000])

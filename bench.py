@@ -227,6 +227,25 @@ def graph_call_us(job: Job, reps: int = 3) -> dict:
     return res
 
 
+def device_copy_GBps(n_bytes: int = 1 << 30, reps: int = 5) -> float:
+    """Measured device copy bandwidth, the second denominator next to the 8
+    TB/s spec: read + written bytes per second of a plain device-to-device
+    copy of `n_bytes`, best of `reps` timed copies after one warm-up."""
+    x = torch.ones(n_bytes // 4, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        y.copy_(x)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del x, y
+    return 2 * n_bytes / (best * 1e-3) / 1e9
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload's units
 # ---------------------------------------------------------------------------
@@ -916,6 +935,11 @@ def main():
                    "token_steps_per_s": round(tok / (dec_us * 1e-6), 1),
                    "denoising_steps_per_s": round(calls / (dec_us * 1e-6), 1),
                    "from": "graph_us of the step and step_commit calls (state as the bench step leaves it)"}
+    copy_gbs = device_copy_GBps()
+    for kd in kernels.values():
+        kd["of_copy"] = round(kd["GBps"] / copy_gbs, 4)
+        if "graph_GBps" in kd:
+            kd["graph_of_copy"] = round(kd["graph_GBps"] / copy_gbs, 4)
     dom = max(kernels, key=lambda k: kernels[k]["share_of_step"])
     kd = kernels[dom]
     traffic = measured_traffic(dom, wl.name)
@@ -940,6 +964,10 @@ def main():
                                    "kind's calls of one step replayed back to back in a HIP graph"},
         "kernels": kernels,
         "denoise": denoise,
+        "device_copy": {"GBps": round(copy_gbs, 1), "bytes_per_copy": 2 << 30,
+                        "what": "read + written bytes per second of a 1 GiB device-to-device copy (best of 5); "
+                                "the kernels' of_copy fractions use it as the denominator (streams that only "
+                                "read can exceed it)"},
     }
     if not args.no_context:
         log("[bench] context: hybrid step vs exact full-prefix step at the serving shapes")

@@ -213,8 +213,12 @@ __device__ __forceinline__ uint32_t tile_lane_offset()
     return lo;
 }
 
+// rot (wave-uniform): accumulator u holds feature tile (t + rot) mod NT of
+// its value-row tile instead of t mod NT (a wave whose TPW tiles cover every
+// feature tile of one value-row tile may take them in a rotated order).
 template <int D, int WPH = PhiKVShape<D>::NW>
-__device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (D / 32) / WPH], bool store, int w)
+__device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (D / 32) / WPH], bool store, int w,
+                                         int rot = 0)
 {
     constexpr int NT = D / 32, TPW = NT * NT / WPH;
     const uint32_t lo = tile_lane_offset<D>();
@@ -222,7 +226,7 @@ __device__ __forceinline__ void tiles_io(float* base, f32x16 (&acc)[(D / 32) * (
     asm volatile("" : "+s"(base), "+s"(w));  // the tile bases, computed here, not hoisted and held
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int t = w * TPW + u, ct = t / NT, ft = t % NT;
+        const int t = w * TPW + u, ct = t / NT, ft = (t + rot) % NT;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float* b = base + (int64_t)(ct * 32 + 8 * q) * D + ft * 32;
@@ -602,13 +606,18 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
     // is in value row 0 write them.  One head per workgroup: feature tile ft
     // is summed and written by wave ft alone, so the work is spread over the
     // waves (one writer summing every tile made it the straggler at each
-    // stage's barrier).
+    // stage's barrier).  Where a wave's tiles are every feature tile of one
+    // value row (d = 128), wave w4 takes them in the order w4, w4 + 1, .. (mod
+    // NT), so its own tile is always the first and the sum needs no branch.
     constexpr int NZ = TPW < NT ? TPW : NT;
     constexpr int NZA = HP == 2 ? NZ : 1;                // z accumulators per lane
     static_assert(HP == 2 || (NT <= WPH && (TPW == 1 || TPW >= NT)),
                   "one head per workgroup: wave ft < NT holds feature tile ft among its operands");
     const bool zwriter = HP == 2 ? (w4 * TPW) / NT == 0 : w4 < NT;   // wave-uniform
     float zacc[kNorm ? NZA : 1];
+    using O0 = TileOperands<NT, TPW>;
+    constexpr bool kRot = kNorm && HP == 1 && O0::NFT == NT && O0::NCT == 1;
+    const int rot = kRot ? w4 : 0;                       // wave-uniform
 #pragma unroll
     for (int u = 0; u < (kNorm ? NZA : 1); ++u) zacc[u] = 0.f;
     auto zsum8 = [&](const PhiOp<M>& kp) {               // phi of the operand's 8 tokens, summed
@@ -638,7 +647,8 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
                 av[c] = *reinterpret_cast<const u16x8*>(vt + P::slot(hw * D + (ct0 + c) * 32 + l32, g));
 #pragma unroll
             for (int f = 0; f < O::NFT; ++f) {
-                const PhiOp<M> kp = phi_op<M>(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + (ft0 + f) * 32 + l32, g)));
+                const int ft = kRot ? (f + rot) % NT : ft0 + f;
+                const PhiOp<M> kp = phi_op<M>(*reinterpret_cast<const u16x8*>(kt + P::slot(hw * D + ft * 32 + l32, g)));
 #pragma unroll
                 for (int c = 0; c < O::NCT; ++c) {                // tile u = c NFT + f
                     f32x16& d = acc[c * O::NFT + f];
@@ -647,7 +657,11 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
                 }
                 if constexpr (kNorm && HP == 2) zacc[f] += zsum8(kp);
                 if constexpr (kNorm && HP == 1) {
-                    if (ft0 + f == w4) zacc[0] += zsum8(kp);         // wave-uniform: wave ft owns tile ft
+                    if constexpr (kRot) {
+                        if (f == 0) zacc[0] += zsum8(kp);            // the wave's own tile, rot = w4
+                    } else if (ft0 + f == w4) {
+                        zacc[0] += zsum8(kp);                         // wave-uniform: wave ft owns tile ft
+                    }
                 }
                 // ELU + 1, and the normalised one-head shapes: keep the
                 // scheduler from preparing several K^T operands at once (their
@@ -677,7 +691,7 @@ __global__ __launch_bounds__((prefill_threads<D, HP>()), 2 / HP) void prefill_sl
         }
         const int64_t dst = inside ? (int64_t)slot * a.heads + (int64_t)cp.h * HP + hw
                                    : ((int64_t)cp.sl.w + piece) * HP + hw;
-        tiles_io<D, WPH>((inside ? a.state : a.partial) + dst * D * D, acc, true, w4);
+        tiles_io<D, WPH>((inside ? a.state : a.partial) + dst * D * D, acc, true, w4, rot);
 #pragma unroll
         for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
         if constexpr (kNorm) {

@@ -135,7 +135,9 @@ ha_status hybrid_state_commit(const void* k, const void* v, float* state,
  *
  * with the same arguments, rules and results as hybrid_attn_step followed by
  * hybrid_state_commit on the same k, v (up to fp32 rounding of the state),
- * but one pass over the inputs: the state is read once and written once.
+ * but in one launch that reads q, k and v once and writes the state once.
+ * At d = 128 with 33..64 rows it also reads the state once; shorter blocks
+ * read the old tiles a second time for the commit, mostly from the caches.
  * Requests of one call must use distinct slots (as for hybrid_state_commit).
  */
 ha_status hybrid_attn_step_commit(const void* q, const void* k, const void* v,
